@@ -1,0 +1,98 @@
+"""The oracle's pins catch plausible mistakes.
+
+Each case plants one mistake in a private copy of ``oracle/oracle.c`` (on the
+CPU, in a temporary directory), builds it, and checks that at least one pin
+comparison now fails.  The unmodified oracle passes the same battery.
+"""
+import math
+import subprocess
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from decode_attention_kv_06_amd.workloads import IfaSpec, SfaSpec, make_ifa, make_sfa
+from test_oracle_pins import _sfa_gather_ref, _sfa_small, dense_kv_bnsd, sdpa_ref, to64
+
+MUTANTS = {
+    "gqa_mapping_modulo": ("j = h / g;", "j = h % Nkv;"),
+    "scale_dropped": ("x[cnt] = scale * dot;\n            ko[cnt] = off;", "x[cnt] = dot;\n            ko[cnt] = off;"),
+    "mask_polarity": ("if (mask[mi]) continue;", "if (!mask[mi]) continue;"),
+    "bnsd_read_as_bsh": ("off = ((b * Nkv + j) * S + s) * D;", "off = (b * S + s) * Nkv * D + j * D;"),
+    "padding_not_clamped": ("int64_t p = pad[b] < 0 ? 0 : pad[b];", "int64_t p = pad[b];"),
+    "zero_rule_as_clamp": ("if (lo < 0 || hi < 0) {", "if (lo < 0) lo = 0;\n            if (hi < 0) {"),
+    "paged_cache_dims_swapped": ("off = ((blk * Nkv + j) * block_size + s % block_size) * D;",
+                                 "off = ((j * num_blocks + blk) * block_size + s % block_size) * D;"),
+    "value_dequant_affine_other_way": ("v = (v + of) * sc;", "v = v * sc + of;"),
+    "query_head_uses_kv_head": ("dot += elem(q, q_dtype, (b * N + h) * D + d) * kv;",
+                                "dot += elem(q, q_dtype, (b * N + j) * D + d) * kv;"),
+    "sfa_rope_dropped": ("dot += elem(q_rope, dtype, (b * QN + h) * DR + d) * elem(key_rope, dtype, row * DR + d);",
+                         "(void)0;"),
+    "sfa_block_table_skipped": ("int64_t row = blk * block_size + t % block_size;", "int64_t row = t;"),
+    "sfa_length_bound_inclusive": ("if (t < 0 || t >= lkv[b]) continue;", "if (t < 0 || t > lkv[b]) continue;"),
+}
+
+
+def _battery(lib):
+    """(name, passed) for each pin comparison, evaluated with ``lib``."""
+    res = []
+
+    def close(a, b):
+        return bool(np.allclose(a, b, rtol=0, atol=1e-10))
+
+    for layout in ("BNSD", "BSH"):
+        inp = make_ifa(IfaSpec("m", 931, "bf16", "bf16", B=3, N=6, Nkv=2, D=16, layout=layout, S=37,
+                               len_range=(1, 37), mask="u8", mask_p=0.3))
+        res.append(("sdpa_" + layout, close(oracle.ifa(inp, use=lib), sdpa_ref(inp))))
+    inp = make_ifa(IfaSpec("m", 932, "f16", "f16", B=4, N=2, Nkv=1, D=8, S=40, lengths=[10, 30, 35, 20],
+                           pads=[5, -3, 10, 25]))
+    try:
+        res.append(("left_pad", close(oracle.ifa(inp, use=lib), sdpa_ref(inp))))
+    except ValueError:
+        res.append(("left_pad", False))
+    inp = make_ifa(IfaSpec("m", 933, "bf16", "bf16", B=3, N=4, Nkv=2, D=16, S=96, len_range=(1, 96), paged=True,
+                           block_size=16, max_blocks=6, num_blocks=20))
+    bt = inp["block_table"].long()
+    kd = to64(inp["k"])[bt].permute(0, 2, 1, 3, 4).reshape(3, 2, 96, 16)
+    vd = to64(inp["v"])[bt].permute(0, 2, 1, 3, 4).reshape(3, 2, 96, 16)
+    try:
+        res.append(("paged", close(oracle.ifa(inp, use=lib), sdpa_ref(inp, kd, vd))))
+    except ValueError:
+        res.append(("paged", False))
+    inp = make_ifa(IfaSpec("m", 934, "f16", "i8", B=2, N=4, Nkv=2, D=16, S=30, len_range=(5, 30),
+                           antiquant="per_channel"))
+    k64, v64 = dense_kv_bnsd(inp)
+    sc, of = to64(inp["aq_scale"]), to64(inp["aq_offset"])
+    kdq = (k64 + of[0].view(1, 2, 1, 16)) * sc[0].view(1, 2, 1, 16)
+    vdq = (v64 + of[1].view(1, 2, 1, 16)) * sc[1].view(1, 2, 1, 16)
+    res.append(("antiquant", close(oracle.ifa(inp, use=lib), sdpa_ref(inp, kdq, vdq))))
+    inp = make_sfa(_sfa_small())
+    res.append(("sfa", close(oracle.sfa(inp, use=lib), _sfa_gather_ref(inp))))
+    inp = make_sfa(_sfa_small(n_valid=[40, 50]))
+    idx = inp["sparse_indices"].clone()
+    idx[0, 0, 0, 40:] = 200                      # == lkv[0]: must be ignored
+    inp["sparse_indices"] = idx
+    res.append(("sfa_bound", close(oracle.sfa(inp, use=lib), _sfa_gather_ref(inp))))
+    return res
+
+
+def _build(src, path):
+    subprocess.check_call(["gcc", "-O1", "-fopenmp", "-shared", "-fPIC", "-std=c11", src, "-o", path, "-lm"])
+    return oracle.bind(path)
+
+
+def test_unmodified_oracle_passes_battery():
+    assert all(ok for _, ok in _battery(oracle.lib()))
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, tmp_path):
+    src = open(oracle._SRC).read()
+    old, new = MUTANTS[name]
+    assert src.count(old) == 1, name
+    mpath = tmp_path / "mutant.c"
+    mpath.write_text(src.replace(old, new))
+    lib = _build(str(mpath), str(tmp_path / "libmutant.so"))
+    results = _battery(lib)
+    assert not all(ok for _, ok in results), "mistake %s passed every pin: %s" % (name, results)
