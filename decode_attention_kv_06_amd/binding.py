@@ -1,0 +1,264 @@
+"""ctypes binding of libifadecode (include/ifa_decode.h).
+
+Argument marshalling only: shapes and dtypes are read off torch tensors, the
+argument structs are filled, and the C entry points are called on the current
+HIP stream.  Every computation happens in the library's HIP kernels; there is
+no fallback path, and a missing library is an error.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libifadecode.so")
+
+IFA_OK = 0
+IFA_ERR_PARAM_NULLPTR = 161001
+IFA_ERR_PARAM_INVALID = 161002
+IFA_ERR_RUNTIME = 361001
+
+DT_F16, DT_BF16, DT_I8, DT_U8, DT_BOOL = 1, 2, 3, 4, 5
+_DT = {torch.float16: DT_F16, torch.bfloat16: DT_BF16, torch.int8: DT_I8, torch.uint8: DT_U8, torch.bool: DT_BOOL}
+
+P = ctypes.c_void_p
+I32, I64, U32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32
+
+
+class IfaDecodeArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", U32), ("query", P), ("key", P), ("value", P), ("attention_out", P),
+        ("dtype_q", I32), ("dtype_kv", I32), ("dtype_out", I32), ("input_layout", ctypes.c_char_p),
+        ("batch", I64), ("num_heads", I64), ("num_key_value_heads", I64), ("head_dim", I64), ("kv_seq_len", I64),
+        ("scale_value", ctypes.c_double), ("actual_seq_lengths", P), ("kv_padding_size", P),
+        ("kv_padding_size_count", I64), ("atten_mask", P), ("dtype_mask", I32), ("mask_batch", I64),
+        ("mask_heads", I64), ("mask_seq", I64), ("pse_shift", P), ("antiquant_scale", P), ("antiquant_offset", P),
+        ("antiquant_mode", I32), ("split_tokens", I64), ("profile_event_begin", P), ("profile_event_end", P)]
+
+
+class IfaPagedArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", U32), ("query", P), ("key_cache", P), ("value_cache", P), ("attention_out", P),
+        ("dtype_q", I32), ("dtype_kv", I32), ("dtype_out", I32), ("input_layout", ctypes.c_char_p),
+        ("batch", I64), ("num_heads", I64), ("num_key_value_heads", I64), ("head_dim", I64),
+        ("scale_value", ctypes.c_double), ("actual_seq_lengths", P), ("atten_mask", P), ("dtype_mask", I32),
+        ("mask_batch", I64), ("mask_heads", I64), ("mask_seq", I64), ("pse_shift", P), ("antiquant_scale", P),
+        ("antiquant_offset", P), ("antiquant_mode", I32), ("block_table", P), ("max_blocks_per_seq", I64),
+        ("block_size", I64), ("num_blocks", I64), ("kv_cache_layout", I32), ("split_tokens", I64),
+        ("profile_event_begin", P), ("profile_event_end", P)]
+
+
+class SfaMlaArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", U32), ("query", P), ("query_rope", P), ("key", P), ("key_rope", P), ("value", P),
+        ("sparse_indices", P), ("block_table", P), ("actual_seq_lengths_query", P), ("actual_seq_lengths_kv", P),
+        ("attention_out", P), ("dtype", I32), ("batch", I64), ("q_seq", I64), ("q_heads", I64), ("kv_heads", I64),
+        ("head_dim", I64), ("rope_dim", I64), ("sparse_size", I64), ("block_size", I64), ("num_blocks", I64),
+        ("max_blocks", I64), ("scale_value", ctypes.c_float), ("sparse_block_size", I64), ("sparse_mode", I64),
+        ("attention_mode", I64), ("layout_query", ctypes.c_char_p), ("layout_kv", ctypes.c_char_p),
+        ("split_hint", I64), ("profile_event_begin", P), ("profile_event_end", P)]
+
+
+class IfaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__("%s returned %d (%s)" % (what, status, status_string(status)))
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the in-tree library, building it first if it is not there."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            from . import build as _build
+            _build.build()
+        L = ctypes.CDLL(LIB_PATH)
+        size_t_p = ctypes.POINTER(ctypes.c_size_t)
+        for name, st in (("ifa_decode", IfaDecodeArgs), ("ifa_decode_paged", IfaPagedArgs),
+                         ("sfa_decode_mla", SfaMlaArgs)):
+            ws = getattr(L, name + "_workspace_size")
+            ws.argtypes = [ctypes.POINTER(st), size_t_p]
+            ws.restype = ctypes.c_int
+            run = getattr(L, name)
+            run.argtypes = [ctypes.POINTER(st), P, ctypes.c_size_t, P]
+            run.restype = ctypes.c_int
+        L.ifa_status_string.argtypes = [ctypes.c_int]
+        L.ifa_status_string.restype = ctypes.c_char_p
+        L.ifa_abi_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().ifa_status_string(status).decode()
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _host_i64(a) -> Optional[np.ndarray]:
+    if a is None:
+        return None
+    if isinstance(a, torch.Tensor):
+        a = a.cpu().numpy()
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int64).reshape(-1))
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _run(name: str, args, workspace: Optional[torch.Tensor], stream, device) -> int:
+    L = lib()
+    nbytes = ctypes.c_size_t(0)
+    rc = getattr(L, name + "_workspace_size")(ctypes.byref(args), ctypes.byref(nbytes))
+    if rc != IFA_OK:
+        raise IfaError(rc, name + "_workspace_size")
+    if workspace is None or workspace.numel() < nbytes.value:
+        workspace = torch.empty(max(int(nbytes.value), 1), dtype=torch.uint8, device=device)
+    rc = getattr(L, name)(ctypes.byref(args), ctypes.c_void_p(workspace.data_ptr()),
+                          ctypes.c_size_t(workspace.numel()), _stream(stream))
+    if rc != IFA_OK:
+        raise IfaError(rc, name)
+    return int(nbytes.value)
+
+
+def _mask_fields(mask):
+    if mask is None:
+        return None, 0, 0, 0, 0
+    if mask.dim() != 4 or mask.shape[2] != 1:
+        raise ValueError("atten_mask must be (B|1, N|1, 1, S)")
+    return mask, _DT[mask.dtype], mask.shape[0], mask.shape[1], mask.shape[3]
+
+
+def ifa_decode_args(q, k, v, out, *, num_heads, num_key_value_heads=0, input_layout="BSH", scale_value=None,
+                    actual_seq_lengths=None, kv_padding_size=None, atten_mask=None, antiquant_scale=None,
+                    antiquant_offset=None, antiquant_mode=0, split_tokens=0, keep=None):
+    """Fill an IfaDecodeArgs from tensors; `keep` collects host arrays that must outlive the call."""
+    N = int(num_heads)
+    if input_layout == "BSH":
+        B, H, S = q.shape[0], q.shape[2], k.shape[1]
+        D = H // N
+    elif input_layout == "BNSD":
+        B, D, S = q.shape[0], q.shape[3], k.shape[2]
+    elif input_layout == "BSND":
+        B, D, S = q.shape[0], q.shape[3], k.shape[1]
+    else:
+        B, D, S = q.shape[0], 0, 0
+    lens = _host_i64(actual_seq_lengths)
+    pads = _host_i64(kv_padding_size)
+    mask, dmask, mB, mN, mS = _mask_fields(atten_mask)
+    if keep is not None:
+        keep.extend([lens, pads, input_layout.encode()])
+    a = IfaDecodeArgs()
+    a.struct_size = ctypes.sizeof(IfaDecodeArgs)
+    a.query, a.key, a.value, a.attention_out = _ptr(q), _ptr(k), _ptr(v), _ptr(out)
+    a.dtype_q, a.dtype_kv, a.dtype_out = _DT[q.dtype], _DT[k.dtype], _DT[out.dtype]
+    a.input_layout = input_layout.encode()
+    a.batch, a.num_heads, a.num_key_value_heads, a.head_dim, a.kv_seq_len = B, N, int(num_key_value_heads), D, S
+    a.scale_value = float(scale_value if scale_value is not None else 1.0 / float(D) ** 0.5)
+    a.actual_seq_lengths = None if lens is None else lens.ctypes.data
+    a.kv_padding_size = None if pads is None else pads.ctypes.data
+    a.kv_padding_size_count = 0 if pads is None else len(pads)
+    a.atten_mask, a.dtype_mask, a.mask_batch, a.mask_heads, a.mask_seq = _ptr(mask), dmask, mB, mN, mS
+    a.pse_shift = None
+    a.antiquant_scale, a.antiquant_offset = _ptr(antiquant_scale), _ptr(antiquant_offset)
+    a.antiquant_mode = int(antiquant_mode)
+    a.split_tokens = int(split_tokens)
+    return a
+
+
+def ifa_decode(q, k, v, out, *, workspace=None, stream=None, **kw) -> int:
+    """IncreFlashAttention over a dense padded cache; writes `out`, returns workspace bytes used."""
+    keep: list = []
+    a = ifa_decode_args(q, k, v, out, keep=keep, **kw)
+    return _run("ifa_decode", a, workspace, stream, q.device)
+
+
+def ifa_paged_args(q, key_cache, value_cache, out, block_table, *, num_heads, num_key_value_heads=0,
+                   input_layout="BNSD", scale_value=None, actual_seq_lengths=None, atten_mask=None,
+                   antiquant_scale=None, antiquant_offset=None, antiquant_mode=0, kv_cache_layout=0,
+                   split_tokens=0, keep=None):
+    N = int(num_heads)
+    nkv = int(num_key_value_heads) or N
+    if kv_cache_layout == 0:
+        nblk, bs, D = key_cache.shape[0], key_cache.shape[2], key_cache.shape[3]
+    else:
+        nblk, bs = key_cache.shape[0], key_cache.shape[1]
+        D = key_cache.shape[2] // nkv
+    lens = _host_i64(actual_seq_lengths)
+    mask, dmask, mB, mN, mS = _mask_fields(atten_mask)
+    if keep is not None:
+        keep.extend([lens, input_layout.encode()])
+    a = IfaPagedArgs()
+    a.struct_size = ctypes.sizeof(IfaPagedArgs)
+    a.query, a.key_cache, a.value_cache, a.attention_out = _ptr(q), _ptr(key_cache), _ptr(value_cache), _ptr(out)
+    a.dtype_q, a.dtype_kv, a.dtype_out = _DT[q.dtype], _DT[key_cache.dtype], _DT[out.dtype]
+    a.input_layout = input_layout.encode()
+    a.batch, a.num_heads, a.num_key_value_heads, a.head_dim = q.shape[0], N, int(num_key_value_heads), D
+    a.scale_value = float(scale_value if scale_value is not None else 1.0 / float(D) ** 0.5)
+    a.actual_seq_lengths = None if lens is None else lens.ctypes.data
+    a.atten_mask, a.dtype_mask, a.mask_batch, a.mask_heads, a.mask_seq = _ptr(mask), dmask, mB, mN, mS
+    a.pse_shift = None
+    a.antiquant_scale, a.antiquant_offset = _ptr(antiquant_scale), _ptr(antiquant_offset)
+    a.antiquant_mode = int(antiquant_mode)
+    a.block_table = _ptr(block_table)
+    a.max_blocks_per_seq = block_table.shape[1]
+    a.block_size, a.num_blocks, a.kv_cache_layout = bs, nblk, int(kv_cache_layout)
+    a.split_tokens = int(split_tokens)
+    return a
+
+
+def ifa_decode_paged(q, key_cache, value_cache, out, block_table, *, workspace=None, stream=None, **kw) -> int:
+    """IncreFlashAttention over a paged cache; writes `out`, returns workspace bytes used."""
+    keep: list = []
+    a = ifa_paged_args(q, key_cache, value_cache, out, block_table, keep=keep, **kw)
+    return _run("ifa_decode_paged", a, workspace, stream, q.device)
+
+
+def sfa_args(query, query_rope, key, key_rope, value, sparse_indices, block_table, actual_seq_lengths_kv, out, *,
+             scale_value=None, actual_seq_lengths_query=None, sparse_mode=0, sparse_block_size=1,
+             attention_mode=2, layout_query="BSND", layout_kv="PA_BSND", split_hint=0, keep=None):
+    B, QS, QN, D = query.shape
+    DR = query_rope.shape[-1]
+    nblk, bs = key.shape[0], key.shape[1]
+    a = SfaMlaArgs()
+    a.struct_size = ctypes.sizeof(SfaMlaArgs)
+    a.query, a.query_rope, a.key, a.key_rope, a.value = (_ptr(query), _ptr(query_rope), _ptr(key),
+                                                         _ptr(key_rope), _ptr(value))
+    a.sparse_indices, a.block_table = _ptr(sparse_indices), _ptr(block_table)
+    a.actual_seq_lengths_query = _ptr(actual_seq_lengths_query)
+    a.actual_seq_lengths_kv = _ptr(actual_seq_lengths_kv)
+    a.attention_out = _ptr(out)
+    a.dtype = _DT[query.dtype]
+    a.batch, a.q_seq, a.q_heads, a.kv_heads = B, QS, QN, key.shape[2]
+    a.head_dim, a.rope_dim = D, DR
+    a.sparse_size = sparse_indices.shape[-1]
+    a.block_size, a.num_blocks, a.max_blocks = bs, nblk, block_table.shape[1]
+    a.scale_value = float(scale_value if scale_value is not None else 1.0 / float(D + DR) ** 0.5)
+    a.sparse_block_size, a.sparse_mode, a.attention_mode = sparse_block_size, sparse_mode, attention_mode
+    lq, lk = layout_query.encode(), layout_kv.encode()
+    if keep is not None:
+        keep.extend([lq, lk])
+    a.layout_query, a.layout_kv = lq, lk
+    a.split_hint = int(split_hint)
+    return a
+
+
+def sfa_decode_mla(query, query_rope, key, key_rope, value, sparse_indices, block_table, actual_seq_lengths_kv,
+                   out, *, workspace=None, stream=None, **kw) -> int:
+    """SparseFlashAttention (MLA-absorb, PA_BSND); writes `out`, returns workspace bytes used."""
+    keep: list = []
+    a = sfa_args(query, query_rope, key, key_rope, value, sparse_indices, block_table, actual_seq_lengths_kv, out,
+                 keep=keep, **kw)
+    return _run("sfa_decode_mla", a, workspace, stream, query.device)

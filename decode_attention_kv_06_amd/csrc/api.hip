@@ -1,0 +1,522 @@
+// Host side of libifadecode: argument validation, the split planner and the
+// launches behind the C ABI declared in include/ifa_decode.h.
+//
+// Validation follows the parameter tables and constraint lists of the
+// IncreFlashAttention README, the aclnnIncreFlashAttentionV2 page and the
+// SparseFlashAttention README; it makes no HIP call, so an invalid call
+// returns before touching the device.
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+#include <functional>
+#include <mutex>
+#include <queue>
+#include <vector>
+
+#include "ifa_decode.h"
+#include "internal.h"
+#include "sfa.h"
+
+namespace {
+
+using namespace ifa;
+
+constexpr int kAbiVersion = 1;
+
+bool is_float_dt(int dt) { return dt == IFA_DT_F16 || dt == IFA_DT_BF16; }
+
+int parse_layout(const char *s, int *out) {
+    if (!s || !strcmp(s, "BSH")) { *out = 0; return IFA_OK; }
+    if (!strcmp(s, "BNSD")) { *out = 1; return IFA_OK; }
+    if (!strcmp(s, "BSND")) { *out = 2; return IFA_OK; }
+    return IFA_ERR_PARAM_INVALID;
+}
+
+// ----------------------------------------------------------------- planning
+
+struct Window { int32_t lo, hi; };
+
+struct IfaPlan {
+    int kv = 0, D = 0, G = 0, n_hg = 0, g = 0, N = 0, Nkv = 0, B = 0;
+    bool paged = false;
+    int chunk = 0;
+    std::vector<Window> win;             // per batch
+    std::vector<int32_t> nch;            // chunks per batch
+    int64_t total_chunks = 0;
+    size_t workspace = 0;
+};
+
+// Device facts used by the planner, cached per device.
+struct DeviceInfo { int cus = 0; };
+
+std::mutex g_mu;
+DeviceInfo g_dev[64];
+int g_resident[64][3][4][4][2];   // [dev][kv][log2 D/64][log2 G][paged] resident waves, 0 = unknown
+
+int current_device(int *dev) { return hipGetDevice(dev) == hipSuccess ? IFA_OK : IFA_ERR_RUNTIME; }
+
+int resident_waves(int kv, int D, int G, bool paged) {
+    int dev = 0;
+    if (current_device(&dev) != IFA_OK || dev < 0 || dev >= 64) return 0;
+    const int di = D == 64 ? 0 : D == 128 ? 1 : D == 256 ? 2 : 3;
+    const int gi = G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3;
+    std::lock_guard<std::mutex> lk(g_mu);
+    int &slot = g_resident[dev][kv][di][gi][paged ? 1 : 0];
+    if (!slot) slot = split_resident_waves(kv, D, G, paged);
+    return slot;
+}
+
+// Greedy list-scheduling estimate of the split kernel's makespan, in units of
+// KV positions, for a chunk size: workgroups (four consecutive work items)
+// are handed to the earliest free slot in grid order, as the dispatcher does.
+double simulate(const std::vector<Window> &win, int chunk, int heads_per_chunk, int slots, double item_cost) {
+    std::priority_queue<double, std::vector<double>, std::greater<double>> q;
+    for (int i = 0; i < slots; i++) q.push(0.0);
+    int pending = 0;
+    double wg_cost = 0.0;
+    double finish = 0.0;
+    auto emit = [&]() {
+        double t = q.top();
+        q.pop();
+        t += wg_cost + item_cost;
+        finish = std::max(finish, t);
+        q.push(t);
+        pending = 0;
+        wg_cost = 0.0;
+    };
+    for (const Window &w : win) {
+        const int len = w.hi - w.lo;
+        for (int c0 = 0; c0 < len; c0 += chunk) {
+            const double n = std::min(chunk, len - c0);
+            for (int h = 0; h < heads_per_chunk; h++) {
+                wg_cost = std::max(wg_cost, n);
+                if (++pending == kWavesPerBlock) emit();
+            }
+        }
+    }
+    if (pending) emit();
+    return finish;
+}
+
+int choose_chunk(const std::vector<Window> &win, int tt, int heads_per_chunk, int waves, double partial_cost) {
+    const int cands[] = {64, 96, 128, 192, 256, 384, 512, 768, 1024, 1536, 2048, 3072, 4096};
+    int64_t total = 0;
+    int maxlen = 0;
+    for (const Window &w : win) {
+        total += w.hi - w.lo;
+        maxlen = std::max(maxlen, w.hi - w.lo);
+    }
+    if (total == 0) return std::max(tt, 64);
+    const int slots = std::max(1, waves / kWavesPerBlock);
+    int best = 0;
+    double best_cost = 0.0;
+    for (int c : cands) {
+        if (c % tt) continue;
+        if (best && c > maxlen + tt) break;    // larger chunks no longer change the plan
+        // Fixed cost per work item (first-load latency, q load, state merge)
+        // plus the partial write and read-back, in position equivalents.
+        const double cost = simulate(win, c, heads_per_chunk, slots, 24.0 + partial_cost);
+        if (!best || cost < best_cost * 0.98) {
+            best = c;
+            best_cost = cost;
+        }
+    }
+    return best ? best : std::max(tt, 64);
+}
+
+int chunk_count(int len, int chunk) { return len > 0 ? (len + chunk - 1) / chunk : 0; }
+
+int finish_plan(IfaPlan &p, int64_t split_tokens, int eb) {
+    p.G = 1;
+    while (p.G < p.g && p.G < 8) p.G <<= 1;
+    p.n_hg = (p.g + p.G - 1) / p.G;
+    const int tt = split_tile_tokens(p.kv, p.D, p.G);
+    if (split_tokens > 0) {
+        p.chunk = (int)split_tokens;
+    } else {
+        const int waves = resident_waves(p.kv, p.D, p.G, p.paged);
+        if (waves <= 0) return IFA_ERR_RUNTIME;
+        const double per_pos_bytes = 2.0 * p.D * eb;
+        const double partial = 2.0 * p.G * (p.D + 2) * 4.0 / per_pos_bytes;
+        p.chunk = choose_chunk(p.win, tt, p.Nkv * p.n_hg, waves, partial);
+    }
+    p.nch.resize(p.B);
+    p.total_chunks = 0;
+    for (int b = 0; b < p.B; b++) {
+        p.nch[b] = chunk_count(p.win[b].hi - p.win[b].lo, p.chunk);
+        p.total_chunks += p.nch[b];
+    }
+    const size_t acc = (size_t)p.total_chunks * p.N * p.D * sizeof(float);
+    const size_t ml = (size_t)p.total_chunks * p.N * 2 * sizeof(float);
+    p.workspace = (acc + 255) / 256 * 256 + (ml + 255) / 256 * 256;
+    return IFA_OK;
+}
+
+// ----------------------------------------------------------------- IFA validation
+
+struct IfaCommon {
+    int layout = 0;
+    int64_t Nkv = 0;
+};
+
+int check_common(const void *q, const void *out, int dq, int dkv, int dout, const char *layout, int64_t B, int64_t N,
+                 int64_t Nkv_in, int64_t D, double scale, const void *mask, int dmask, int64_t mB, int64_t mN,
+                 const void *pse, const void *aqs, const void *aqo, int aq_mode, int64_t split_tokens,
+                 IfaCommon *c) {
+    if (!q || !out) return IFA_ERR_PARAM_NULLPTR;
+    if (!is_float_dt(dq) || dout != dq) return IFA_ERR_PARAM_INVALID;
+    if (dkv != dq && dkv != IFA_DT_I8) return IFA_ERR_PARAM_INVALID;
+    if (parse_layout(layout, &c->layout) != IFA_OK) return IFA_ERR_PARAM_INVALID;
+    if (B < 1 || B > 65536 || N < 1 || N > 256) return IFA_ERR_PARAM_INVALID;
+    if (Nkv_in < 0 || Nkv_in > N) return IFA_ERR_PARAM_INVALID;
+    c->Nkv = Nkv_in == 0 ? N : Nkv_in;
+    if (N % c->Nkv) return IFA_ERR_PARAM_INVALID;
+    if (D != 64 && D != 128 && D != 256 && D != 512) return IFA_ERR_PARAM_INVALID;
+    if (!std::isfinite(scale)) return IFA_ERR_PARAM_INVALID;
+    if (mask) {
+        if (dmask != IFA_DT_BOOL && dmask != IFA_DT_I8 && dmask != IFA_DT_U8) return IFA_ERR_PARAM_INVALID;
+        if ((mB != 1 && mB != B) || (mN != 1 && mN != N)) return IFA_ERR_PARAM_INVALID;
+    }
+    if (pse) return IFA_ERR_PARAM_INVALID;
+    if (dkv == IFA_DT_I8) {
+        if (aq_mode != IFA_ANTIQUANT_PER_TENSOR && aq_mode != IFA_ANTIQUANT_PER_CHANNEL) return IFA_ERR_PARAM_INVALID;
+        if (!aqs || !aqo) return IFA_ERR_PARAM_NULLPTR;
+    } else if (aq_mode != IFA_ANTIQUANT_NONE || aqs || aqo) {
+        return IFA_ERR_PARAM_INVALID;
+    }
+    if (split_tokens < 0 || split_tokens % 16 || split_tokens > (1 << 24)) return IFA_ERR_PARAM_INVALID;
+    return IFA_OK;
+}
+
+int kv_kind(int dkv) { return dkv == IFA_DT_F16 ? KV_F16 : dkv == IFA_DT_BF16 ? KV_BF16 : KV_I8; }
+
+int plan_dense(const ifa_decode_args *a, IfaPlan &p, IfaCommon &c) {
+    if (!a) return IFA_ERR_PARAM_NULLPTR;
+    if (a->struct_size < sizeof(ifa_decode_args)) return IFA_ERR_PARAM_INVALID;
+    int rc = check_common(a->query, a->attention_out, a->dtype_q, a->dtype_kv, a->dtype_out, a->input_layout,
+                          a->batch, a->num_heads, a->num_key_value_heads, a->head_dim, a->scale_value, a->atten_mask,
+                          a->dtype_mask, a->mask_batch, a->mask_heads, a->pse_shift, a->antiquant_scale,
+                          a->antiquant_offset, a->antiquant_mode, a->split_tokens, &c);
+    if (rc) return rc;
+    if (!a->key || !a->value) return IFA_ERR_PARAM_NULLPTR;
+    const int64_t S = a->kv_seq_len;
+    if (S < 1 || S > (int64_t)1 << 30) return IFA_ERR_PARAM_INVALID;
+    if (a->kv_padding_size && a->kv_padding_size_count != 1 && a->kv_padding_size_count != a->batch)
+        return IFA_ERR_PARAM_INVALID;
+    p.B = (int)a->batch;
+    p.N = (int)a->num_heads;
+    p.Nkv = (int)c.Nkv;
+    p.g = p.N / p.Nkv;
+    p.D = (int)a->head_dim;
+    p.kv = kv_kind(a->dtype_kv);
+    p.paged = false;
+    p.win.resize(p.B);
+    int64_t max_hi = 0;
+    for (int b = 0; b < p.B; b++) {
+        int64_t L = S, lo = 0, hi = S;
+        if (a->actual_seq_lengths) {
+            L = a->actual_seq_lengths[b];
+            if (L < 0 || L > S) return IFA_ERR_PARAM_INVALID;
+            lo = 0;
+            hi = L;
+            if (a->kv_padding_size) {
+                int64_t pad = a->kv_padding_size[a->kv_padding_size_count == 1 ? 0 : b];
+                if (pad < 0) pad = 0;                       // README: pad < 0 is set to 0
+                lo = S - pad - L;
+                hi = S - pad;
+                if (lo < 0 || hi < 0) lo = hi = 0;         // README: start or end < 0 -> zeros
+            }
+        }
+        p.win[b] = {(int32_t)lo, (int32_t)hi};
+        max_hi = std::max(max_hi, hi);
+    }
+    if (a->atten_mask && a->mask_seq < max_hi) return IFA_ERR_PARAM_INVALID;
+    return IFA_OK;
+}
+
+int plan_paged(const ifa_paged_args *a, IfaPlan &p, IfaCommon &c) {
+    if (!a) return IFA_ERR_PARAM_NULLPTR;
+    if (a->struct_size < sizeof(ifa_paged_args)) return IFA_ERR_PARAM_INVALID;
+    int rc = check_common(a->query, a->attention_out, a->dtype_q, a->dtype_kv, a->dtype_out, a->input_layout,
+                          a->batch, a->num_heads, a->num_key_value_heads, a->head_dim, a->scale_value, a->atten_mask,
+                          a->dtype_mask, a->mask_batch, a->mask_heads, a->pse_shift, a->antiquant_scale,
+                          a->antiquant_offset, a->antiquant_mode, a->split_tokens, &c);
+    if (rc) return rc;
+    if (!a->key_cache || !a->value_cache || !a->block_table || !a->actual_seq_lengths) return IFA_ERR_PARAM_NULLPTR;
+    const int64_t bs = a->block_size;
+    const int align = a->dtype_kv == IFA_DT_I8 ? 32 : 16;
+    if (bs < 16 || bs > 512 || bs % align) return IFA_ERR_PARAM_INVALID;
+    if (a->max_blocks_per_seq < 1 || a->num_blocks < 1 || a->num_blocks > INT32_MAX) return IFA_ERR_PARAM_INVALID;
+    if (a->kv_cache_layout != 0 && a->kv_cache_layout != 1) return IFA_ERR_PARAM_INVALID;
+    // README: BSH / BSND queries only pair with the (blocknum, blocksize, H) cache.
+    if (a->kv_cache_layout == 0 && c.layout != 1) return IFA_ERR_PARAM_INVALID;
+    const int64_t reach = a->max_blocks_per_seq * bs;
+    if (reach > (int64_t)1 << 30) return IFA_ERR_PARAM_INVALID;
+    p.B = (int)a->batch;
+    p.N = (int)a->num_heads;
+    p.Nkv = (int)c.Nkv;
+    p.g = p.N / p.Nkv;
+    p.D = (int)a->head_dim;
+    p.kv = kv_kind(a->dtype_kv);
+    p.paged = true;
+    p.win.resize(p.B);
+    int64_t max_hi = 0, blocks_needed = 0;
+    for (int b = 0; b < p.B; b++) {
+        const int64_t L = a->actual_seq_lengths[b];
+        if (L < 0 || L > reach) return IFA_ERR_PARAM_INVALID;
+        p.win[b] = {0, (int32_t)L};
+        max_hi = std::max(max_hi, L);
+        blocks_needed += (L + bs - 1) / bs;
+    }
+    // README: blocknum may not be smaller than the blocks the lengths need.
+    if (blocks_needed > a->num_blocks) return IFA_ERR_PARAM_INVALID;
+    if (a->atten_mask && a->mask_seq < max_hi) return IFA_ERR_PARAM_INVALID;
+    return IFA_OK;
+}
+
+// ----------------------------------------------------------------- launching
+
+uint32_t bs_magic(uint32_t d, int *shift) {
+    int l = 0;
+    while (((uint64_t)1 << l) < d) l++;
+    *shift = l;
+    return (uint32_t)((((uint64_t)1 << 32) * (((uint64_t)1 << l) - d)) / d + 1);
+}
+
+struct Launch {
+    const void *q, *k, *v;
+    void *out;
+    const uint8_t *mask;
+    int64_t mask_sB, mask_sH;
+    int mask_mode;
+    const int32_t *block_table;
+    int64_t sB, sN, sS, blk_stride, head_stride, row_stride;
+    int max_blocks, block_size, num_blocks;
+    const void *aqs, *aqo;
+    int aq_mode;
+    bool q_bf16;
+    double scale;
+    hipEvent_t ev_begin, ev_end;
+};
+
+int run(const IfaPlan &p, const Launch &L, void *ws, size_t ws_bytes, hipStream_t stream) {
+    if (p.workspace && (!ws || ws_bytes < p.workspace)) return p.workspace && !ws ? IFA_ERR_PARAM_NULLPTR
+                                                                                  : IFA_ERR_PARAM_INVALID;
+    float *part_acc = reinterpret_cast<float *>(ws);
+    const size_t acc_bytes = ((size_t)p.total_chunks * p.N * p.D * sizeof(float) + 255) / 256 * 256;
+    float *part_ml = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + acc_bytes);
+
+    SplitParams sp;
+    memset(&sp, 0, sizeof sp);
+    sp.q = L.q;
+    sp.k = L.k;
+    sp.v = L.v;
+    sp.mask = L.mask;
+    sp.block_table = L.block_table;
+    sp.k_scale = L.aqs;
+    sp.sB = L.sB;
+    sp.sN = L.sN;
+    sp.sS = L.sS;
+    sp.blk_stride = L.blk_stride;
+    sp.head_stride = L.head_stride;
+    sp.row_stride = L.row_stride;
+    sp.mask_sB = L.mask_sB;
+    sp.mask_sH = L.mask_sH;
+    sp.N = p.N;
+    sp.Nkv = p.Nkv;
+    sp.g = p.g;
+    sp.n_hg = p.n_hg;
+    sp.max_blocks = L.max_blocks;
+    sp.block_size = L.block_size;
+    sp.num_blocks = L.num_blocks;
+    if (p.paged) sp.bs_magic = bs_magic((uint32_t)L.block_size, &sp.bs_shift);
+    sp.mask_mode = L.mask_mode;
+    sp.aq_mode = L.aq_mode;
+    sp.q_bf16 = L.q_bf16;
+    sp.score_mul = (float)(L.scale * 1.4426950408889634);
+    sp.chunk = p.chunk;
+
+    CombineParams cp;
+    memset(&cp, 0, sizeof cp);
+    cp.out = L.out;
+    cp.v_scale = L.aqs;
+    cp.v_offset = L.aqo;
+    cp.N = p.N;
+    cp.Nkv = p.Nkv;
+    cp.g = p.g;
+    cp.D = p.D;
+    cp.out_bf16 = L.q_bf16;
+    cp.aq_mode = L.aq_mode;
+
+    int64_t chunk_base = 0;
+    const bool timed = L.ev_begin && L.ev_end;
+    if (timed && hipEventRecord(L.ev_begin, stream) != hipSuccess) return IFA_ERR_RUNTIME;
+    for (int b0 = 0; b0 < p.B; b0 += kSliceBatches) {
+        const int nb = std::min(kSliceBatches, p.B - b0);
+        sp.nb = cp.nb = nb;
+        sp.b0 = cp.b0 = b0;
+        int32_t cum = 0;
+        for (int i = 0; i < nb; i++) {
+            sp.lo[i] = p.win[b0 + i].lo;
+            sp.hi[i] = p.win[b0 + i].hi;
+            sp.cum[i] = cp.cum[i] = cum;
+            cum += p.nch[b0 + i];
+        }
+        sp.cum[nb] = cp.cum[nb] = cum;
+        sp.part_acc = part_acc + chunk_base * p.N * p.D;
+        sp.part_ml = part_ml + chunk_base * p.N * 2;
+        cp.part_acc = sp.part_acc;
+        cp.part_ml = sp.part_ml;
+        const int64_t items = (int64_t)cum * p.Nkv * p.n_hg;
+        if (items > INT32_MAX) return IFA_ERR_PARAM_INVALID;
+        sp.n_items = (int)items;
+        if (items > 0 && launch_split(sp, p.kv, p.D, p.G, p.paged, stream) != hipSuccess) return IFA_ERR_RUNTIME;
+        if (timed && b0 + kSliceBatches >= p.B && hipEventRecord(L.ev_end, stream) != hipSuccess)
+            return IFA_ERR_RUNTIME;
+        if (launch_combine(cp, stream) != hipSuccess) return IFA_ERR_RUNTIME;
+        chunk_base += cum;
+    }
+    return IFA_OK;
+}
+
+Launch dense_launch(const ifa_decode_args *a, const IfaPlan &p, const IfaCommon &c) {
+    Launch L;
+    memset(&L, 0, sizeof L);
+    L.q = a->query;
+    L.k = a->key;
+    L.v = a->value;
+    L.out = a->attention_out;
+    const int64_t S = a->kv_seq_len, D = p.D, Nkv = p.Nkv;
+    if (c.layout == 1) {         // BNSD: [B, Nkv, S, D]
+        L.sB = Nkv * S * D;
+        L.sN = S * D;
+        L.sS = D;
+    } else {                     // BSH / BSND: [B, S, Nkv, D]
+        L.sB = S * Nkv * D;
+        L.sN = D;
+        L.sS = Nkv * D;
+    }
+    if (a->atten_mask) {
+        L.mask = reinterpret_cast<const uint8_t *>(a->atten_mask);
+        L.mask_sB = a->mask_batch == 1 ? 0 : a->mask_heads * a->mask_seq;
+        L.mask_sH = a->mask_heads == 1 ? 0 : a->mask_seq;
+        L.mask_mode = a->mask_heads == 1 ? 1 : 2;
+    }
+    L.aqs = a->antiquant_scale;
+    L.aqo = a->antiquant_offset;
+    L.aq_mode = a->dtype_kv == IFA_DT_I8 ? a->antiquant_mode : 0;
+    L.q_bf16 = a->dtype_q == IFA_DT_BF16;
+    L.scale = a->scale_value;
+    L.ev_begin = reinterpret_cast<hipEvent_t>(a->profile_event_begin);
+    L.ev_end = reinterpret_cast<hipEvent_t>(a->profile_event_end);
+    return L;
+}
+
+Launch paged_launch(const ifa_paged_args *a, const IfaPlan &p) {
+    Launch L;
+    memset(&L, 0, sizeof L);
+    L.q = a->query;
+    L.k = a->key_cache;
+    L.v = a->value_cache;
+    L.out = a->attention_out;
+    const int64_t bs = a->block_size, D = p.D, Nkv = p.Nkv;
+    L.block_table = a->block_table;
+    L.max_blocks = (int)a->max_blocks_per_seq;
+    L.block_size = (int)bs;
+    L.num_blocks = (int)a->num_blocks;
+    L.blk_stride = Nkv * bs * D;
+    if (a->kv_cache_layout == 0) {   // (blocknum, KV_N, blocksize, D)
+        L.head_stride = bs * D;
+        L.row_stride = D;
+    } else {                         // (blocknum, blocksize, KV_N*D)
+        L.head_stride = D;
+        L.row_stride = Nkv * D;
+    }
+    if (a->atten_mask) {
+        L.mask = reinterpret_cast<const uint8_t *>(a->atten_mask);
+        L.mask_sB = a->mask_batch == 1 ? 0 : a->mask_heads * a->mask_seq;
+        L.mask_sH = a->mask_heads == 1 ? 0 : a->mask_seq;
+        L.mask_mode = a->mask_heads == 1 ? 1 : 2;
+    }
+    L.aqs = a->antiquant_scale;
+    L.aqo = a->antiquant_offset;
+    L.aq_mode = a->dtype_kv == IFA_DT_I8 ? a->antiquant_mode : 0;
+    L.q_bf16 = a->dtype_q == IFA_DT_BF16;
+    L.scale = a->scale_value;
+    L.ev_begin = reinterpret_cast<hipEvent_t>(a->profile_event_begin);
+    L.ev_end = reinterpret_cast<hipEvent_t>(a->profile_event_end);
+    return L;
+}
+
+int eb_of(int dkv) { return dkv == IFA_DT_I8 ? 1 : 2; }
+
+}  // namespace
+
+extern "C" {
+
+int ifa_abi_version(void) { return kAbiVersion; }
+
+const char *ifa_status_string(int status) {
+    switch (status) {
+    case IFA_OK: return "IFA_OK";
+    case IFA_ERR_PARAM_NULLPTR: return "IFA_ERR_PARAM_NULLPTR: a mandatory pointer is NULL";
+    case IFA_ERR_PARAM_INVALID: return "IFA_ERR_PARAM_INVALID: unsupported dtype, layout, shape or constraint";
+    case IFA_ERR_RUNTIME: return "IFA_ERR_RUNTIME: a HIP call or kernel launch failed";
+    }
+    return "unknown status";
+}
+
+int ifa_decode_workspace_size(const ifa_decode_args *a, size_t *bytes) {
+    if (!bytes) return IFA_ERR_PARAM_NULLPTR;
+    IfaPlan p;
+    IfaCommon c;
+    int rc = plan_dense(a, p, c);
+    if (rc) return rc;
+    rc = finish_plan(p, a->split_tokens, eb_of(a->dtype_kv));
+    if (rc) return rc;
+    *bytes = p.workspace;
+    return IFA_OK;
+}
+
+int ifa_decode(const ifa_decode_args *a, void *ws, size_t ws_bytes, ifa_stream_t stream) {
+    IfaPlan p;
+    IfaCommon c;
+    int rc = plan_dense(a, p, c);
+    if (rc) return rc;
+    rc = finish_plan(p, a->split_tokens, eb_of(a->dtype_kv));
+    if (rc) return rc;
+    return run(p, dense_launch(a, p, c), ws, ws_bytes, reinterpret_cast<hipStream_t>(stream));
+}
+
+int ifa_decode_paged_workspace_size(const ifa_paged_args *a, size_t *bytes) {
+    if (!bytes) return IFA_ERR_PARAM_NULLPTR;
+    IfaPlan p;
+    IfaCommon c;
+    int rc = plan_paged(a, p, c);
+    if (rc) return rc;
+    rc = finish_plan(p, a->split_tokens, eb_of(a->dtype_kv));
+    if (rc) return rc;
+    *bytes = p.workspace;
+    return IFA_OK;
+}
+
+int ifa_decode_paged(const ifa_paged_args *a, void *ws, size_t ws_bytes, ifa_stream_t stream) {
+    IfaPlan p;
+    IfaCommon c;
+    int rc = plan_paged(a, p, c);
+    if (rc) return rc;
+    rc = finish_plan(p, a->split_tokens, eb_of(a->dtype_kv));
+    if (rc) return rc;
+    return run(p, paged_launch(a, p), ws, ws_bytes, reinterpret_cast<hipStream_t>(stream));
+}
+
+int sfa_decode_mla_workspace_size(const sfa_mla_args *a, size_t *bytes) {
+    return ifa::sfa_workspace_size(a, bytes);
+}
+
+int sfa_decode_mla(const sfa_mla_args *a, void *ws, size_t ws_bytes, ifa_stream_t stream) {
+    return ifa::sfa_run(a, ws, ws_bytes, reinterpret_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

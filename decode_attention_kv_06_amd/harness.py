@@ -1,0 +1,41 @@
+"""Moves a generated workload to the GPU and calls the matching entry point.
+
+Marshalling only (device copies, output allocation, argument selection); the
+attention itself runs in the library's kernels.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import binding
+from .workloads import IfaSpec, SfaSpec
+
+
+def to_device(inp: dict, device: str = "cuda") -> dict:
+    out = {}
+    for key, val in inp.items():
+        out[key] = val.to(device) if isinstance(val, torch.Tensor) else val
+    return out
+
+
+def alloc_out(inp: dict) -> torch.Tensor:
+    return torch.empty_like(inp["q"])
+
+
+def call(dev: dict, out: torch.Tensor, split: int = 0, workspace=None, stream=None) -> int:
+    """Run the entry point that `dev["spec"]` describes; returns workspace bytes."""
+    s = dev["spec"]
+    if isinstance(s, SfaSpec):
+        return binding.sfa_decode_mla(dev["q"], dev["q_rope"], dev["key"], dev["key_rope"], dev["value"],
+                                      dev["sparse_indices"], dev["block_table"], dev["actual_seq_lengths_kv"], out,
+                                      scale_value=s.scale_value, sparse_mode=s.sparse_mode, split_hint=split,
+                                      workspace=workspace, stream=stream)
+    assert isinstance(s, IfaSpec)
+    common = dict(num_heads=s.N, num_key_value_heads=s.Nkv, input_layout=s.layout, scale_value=s.scale_value,
+                  actual_seq_lengths=dev["actual_seq_lengths"], atten_mask=dev["mask"],
+                  antiquant_scale=dev["aq_scale"], antiquant_offset=dev["aq_offset"], antiquant_mode=dev["aq_mode"],
+                  split_tokens=split, workspace=workspace, stream=stream)
+    if s.paged:
+        return binding.ifa_decode_paged(dev["q"], dev["k"], dev["v"], out, dev["block_table"],
+                                        kv_cache_layout=s.cache_layout, **common)
+    return binding.ifa_decode(dev["q"], dev["k"], dev["v"], out, kv_padding_size=dev["kv_padding_size"], **common)

@@ -1,0 +1,249 @@
+/*
+ * ifa_decode.h — C ABI of the MI355X (gfx950) decode-attention library.
+ *
+ * Three operations, each with the two-phase calling convention of the
+ * aclnnIncreFlashAttentionV2 page ("Function Prototype"): a workspace-size
+ * query that validates the arguments, then a run call that enqueues the work
+ * on a HIP stream.
+ *
+ *   ifa_decode        IncreFlashAttention over a dense padded KV cache
+ *   ifa_decode_paged  IncreFlashAttention over a paged KV cache (block table)
+ *   sfa_decode_mla    SparseFlashAttention, MLA-absorb mode, paged cache
+ *
+ * What is computed (IncreFlashAttention README "Formula"; V2 page "Formula"):
+ *     attentionOut = softmax(scaleValue * query . key^T  [masked]) . value
+ * with the query S axis fixed to 1, per batch over the KV positions the
+ * README's constraints define (actual lengths, left padding, page attention),
+ * and for SFA (SparseFlashAttention README "Formula") over the cache rows
+ * named by sparse_indices, with the rope parts added to the scores.
+ *
+ * Conventions where the pages leave a choice open:
+ *   - attenMask: a nonzero byte EXCLUDES the position (the V2 page's worked
+ *     example passes an all-zero mask in an ordinary call);
+ *   - GQA: query head h reads KV head h / (num_heads / num_key_value_heads);
+ *   - an empty attention set (length 0, every position masked, no valid
+ *     sparse index) gives an all-zero output row, like the left-padding rule;
+ *   - antiquant: dequantised = (x + offset) * scale; index 0 of the leading
+ *     axis of scale/offset is K, index 1 is V;
+ *   - output rounding: fp32 result rounded to nearest-even into fp16/bf16.
+ *
+ * Ownership.  Every tensor is caller-owned device memory (pointers from
+ * hipMalloc or a framework allocator).  The library allocates and frees
+ * nothing, and keeps no pointer after a call returns.  Host arrays
+ * (actual_seq_lengths, kv_padding_size) are read during the call only.  The
+ * workspace is caller-allocated with at least the size the matching
+ * *_workspace_size call returned for the same arguments; it must not be in
+ * use by another call that may run concurrently.  attention_out and the
+ * workspace must not alias any input; for SFA, value may alias key.
+ *
+ * Execution.  The run calls enqueue kernels on `stream` and return without
+ * waiting (the V2 page's example synchronises the stream after the call).
+ * No call synchronises the device or allocates, so a call can be captured
+ * into a HIP graph.  Results are deterministic: the same inputs on the same
+ * device give the same bytes (V2 page "Constraints > Deterministic computation").
+ *
+ * Errors (V2 page "Return Value"):
+ *   IFA_ERR_PARAM_NULLPTR (161001)  a mandatory pointer is NULL
+ *   IFA_ERR_PARAM_INVALID (161002)  a dtype, layout, shape, constraint or the
+ *                                   workspace size is not supported
+ *   IFA_ERR_RUNTIME       (361001)  a HIP call or kernel launch failed
+ * Every check runs before anything is enqueued; on an error nothing is
+ * launched and attention_out is untouched.
+ */
+#ifndef IFA_DECODE_H
+#define IFA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as HIP's hipStream_t; NULL is the default stream. */
+struct ihipStream_t;
+typedef struct ihipStream_t *ifa_stream_t;
+
+enum {
+    IFA_OK = 0,
+    IFA_ERR_PARAM_NULLPTR = 161001,
+    IFA_ERR_PARAM_INVALID = 161002,
+    IFA_ERR_RUNTIME = 361001
+};
+
+enum {
+    IFA_DT_F16 = 1,  /* IEEE binary16 */
+    IFA_DT_BF16 = 2, /* bfloat16 */
+    IFA_DT_I8 = 3,   /* int8 (KV cache with antiquant; or mask) */
+    IFA_DT_U8 = 4,   /* uint8 (mask) */
+    IFA_DT_BOOL = 5  /* one byte per element, 0 or 1 (mask) */
+};
+
+enum { IFA_ANTIQUANT_NONE = 0, IFA_ANTIQUANT_PER_TENSOR = 1, IFA_ANTIQUANT_PER_CHANNEL = 2 };
+
+/*
+ * Dense padded KV cache (IncreFlashAttention; V2 page parameter table).
+ *
+ * query / attention_out: (B,N,1,D) "BNSD", (B,1,N,D) "BSND" or (B,1,N*D)
+ *   "BSH"; contiguous; dtype_q.
+ * key / value: (B,N_kv,S,D) "BNSD", (B,S,N_kv,D) "BSND" or (B,S,N_kv*D)
+ *   "BSH", the same layout as the query; contiguous; identical shapes.
+ * actual_seq_lengths: host int64[batch], 0 <= L_b <= kv_seq_len, or NULL
+ *   (every batch uses kv_seq_len).  Positions [0, L_b) are attended (right
+ *   padding) unless kv_padding_size is given.
+ * kv_padding_size: host int64[batch] or int64[1] (broadcast), or NULL.  With
+ *   actual_seq_lengths present the window is [Smax - p - L_b, Smax - p),
+ *   p = max(pad_b, 0); a window with start or end < 0 gives a zero row
+ *   (README "Constraints > kv left padding").  Ignored without lengths.
+ * atten_mask: device bytes (mask_batch, mask_heads, 1, mask_seq) with
+ *   mask_batch in {1,B}, mask_heads in {1,N}, mask_seq >= every position
+ *   attended; indexed by the physical cache position.  NULL for none.
+ * antiquant_scale / antiquant_offset: device, dtype_q; per-tensor shape (2),
+ *   per-channel (2,N_kv,1,D) (equivalently (2,N_kv,D) or (2,H)).  Required
+ *   when dtype_kv is IFA_DT_I8, forbidden otherwise (README "Constraints >
+ *   antiquantScale and antiquantOffset").
+ * pse_shift must be NULL (positional bias is not implemented).
+ * Envelope: 1 <= B <= 65536, 1 <= N <= 256, N % N_kv == 0,
+ *   head_dim in {64, 128, 256, 512}, dtype_out == dtype_q, dtype_kv ==
+ *   dtype_q or IFA_DT_I8.
+ * split_tokens: 0 lets the planner choose how many KV positions one work
+ *   item covers; a positive multiple of 16 forces it (testing and tuning).
+ * profile_event_begin / _end: NULL, or two hipEvent_t the call records on
+ *   `stream` immediately before and after its split kernel, so a caller can
+ *   time that kernel alone.  With more than 128 batches the split kernel runs
+ *   once per 128-batch slice and the pair brackets all of them.
+ */
+typedef struct ifa_decode_args {
+    uint32_t struct_size; /* sizeof(ifa_decode_args) */
+    const void *query;
+    const void *key;
+    const void *value;
+    void *attention_out;
+    int32_t dtype_q, dtype_kv, dtype_out;
+    const char *input_layout; /* "BSH" | "BNSD" | "BSND"; NULL means "BSH" */
+    int64_t batch, num_heads, num_key_value_heads, head_dim, kv_seq_len;
+    double scale_value;
+    const int64_t *actual_seq_lengths;
+    const int64_t *kv_padding_size;
+    int64_t kv_padding_size_count; /* 1 or batch when kv_padding_size != NULL */
+    const void *atten_mask;
+    int32_t dtype_mask;
+    int64_t mask_batch, mask_heads, mask_seq;
+    const void *pse_shift;
+    const void *antiquant_scale;
+    const void *antiquant_offset;
+    int32_t antiquant_mode;
+    int64_t split_tokens;
+    void *profile_event_begin; /* optional hipEvent_t recorded right before the split kernel */
+    void *profile_event_end;   /* optional hipEvent_t recorded right after it (both or neither) */
+} ifa_decode_args;
+
+/*
+ * Paged KV cache (README "Constraints > page attention").
+ *
+ * key_cache / value_cache: kv_cache_layout 0 = (num_blocks, N_kv, block_size,
+ *   D) or 1 = (num_blocks, block_size, N_kv*D); identical shapes.  Layout 1
+ *   is the only one allowed for "BSH"/"BSND" queries.
+ * block_table: device int32 [batch, max_blocks_per_seq]; logical position s
+ *   of batch b is row s % block_size of block block_table[b][s / block_size].
+ *   Entries for positions < L_b must lie in [0, num_blocks); an entry outside
+ *   that range is never dereferenced and its positions are left out.
+ * actual_seq_lengths: host int64[batch], required, 0 <= L_b <=
+ *   max_blocks_per_seq * block_size.
+ * block_size: 16..512, a multiple of 16 (fp16/bf16) or of 32 (int8).
+ * atten_mask indexes the logical position; mask_seq >= max L_b.
+ * Left padding is not combined with paging (IFA_ERR_PARAM_INVALID).
+ */
+typedef struct ifa_paged_args {
+    uint32_t struct_size; /* sizeof(ifa_paged_args) */
+    const void *query;
+    const void *key_cache;
+    const void *value_cache;
+    void *attention_out;
+    int32_t dtype_q, dtype_kv, dtype_out;
+    const char *input_layout;
+    int64_t batch, num_heads, num_key_value_heads, head_dim;
+    double scale_value;
+    const int64_t *actual_seq_lengths;
+    const void *atten_mask;
+    int32_t dtype_mask;
+    int64_t mask_batch, mask_heads, mask_seq;
+    const void *pse_shift;
+    const void *antiquant_scale;
+    const void *antiquant_offset;
+    int32_t antiquant_mode;
+    const int32_t *block_table;
+    int64_t max_blocks_per_seq, block_size, num_blocks;
+    int32_t kv_cache_layout;
+    int64_t split_tokens;
+    void *profile_event_begin; /* as in ifa_decode_args */
+    void *profile_event_end;
+} ifa_paged_args;
+
+/*
+ * SparseFlashAttention, MLA-absorb mode (attention_mode 2), query layout
+ * "BSND", cache layout "PA_BSND" (SparseFlashAttention README parameter table
+ * and constraints).
+ *
+ * query [B,1,Q_N,512], query_rope [B,1,Q_N,64]; key and value
+ *   [num_blocks, block_size, 1, 512], key_rope [num_blocks, block_size, 1, 64];
+ *   one dtype (fp16 or bf16) for all of them; value may alias key.
+ * sparse_indices: device int32 [B,1,1,sparse_size]; entry t is valid when
+ *   0 <= t < actual_seq_lengths_kv[b] (valid entries first, invalid last, as
+ *   the README asks; every valid entry is used wherever it stands, and each
+ *   occurrence of a repeated index counts).
+ * block_table: device int32 [B, max_blocks]; the row of index t is
+ *   block_table[b][t / block_size], t % block_size.
+ * actual_seq_lengths_kv: device int32 [B], required.
+ * actual_seq_lengths_query: device int32 [B] or NULL; with q_seq == 1 the
+ *   only valid values are 0 (row output is zero) and 1.
+ * attention_out [B,1,Q_N,512], dtype as the inputs.
+ * Envelope: q_seq == 1, kv_heads == 1, head_dim == 512, rope_dim == 64,
+ *   1 <= q_heads <= 128, sparse_size >= 1, block_size a multiple of 16 and
+ *   <= 1024, sparse_block_size == 1, sparse_mode 0 or 3 (equal at q_seq 1),
+ *   attention_mode == 2.
+ * split_hint: 0 lets the planner choose the number of index chunks per
+ *   batch; a positive value forces it (testing and tuning).
+ */
+typedef struct sfa_mla_args {
+    uint32_t struct_size; /* sizeof(sfa_mla_args) */
+    const void *query, *query_rope;
+    const void *key, *key_rope, *value;
+    const int32_t *sparse_indices;
+    const int32_t *block_table;
+    const int32_t *actual_seq_lengths_query;
+    const int32_t *actual_seq_lengths_kv;
+    void *attention_out;
+    int32_t dtype;
+    int64_t batch, q_seq, q_heads, kv_heads, head_dim, rope_dim;
+    int64_t sparse_size, block_size, num_blocks, max_blocks;
+    float scale_value;
+    int64_t sparse_block_size, sparse_mode, attention_mode;
+    const char *layout_query; /* "BSND"; NULL means "BSND" */
+    const char *layout_kv;    /* "PA_BSND"; NULL means "PA_BSND" */
+    int64_t split_hint;
+    void *profile_event_begin; /* optional hipEvent_t pair recorded around the gather kernel */
+    void *profile_event_end;
+} sfa_mla_args;
+
+/* Phase 1: validate and return the workspace bytes the run call needs. */
+int ifa_decode_workspace_size(const ifa_decode_args *args, size_t *workspace_bytes);
+int ifa_decode_paged_workspace_size(const ifa_paged_args *args, size_t *workspace_bytes);
+int sfa_decode_mla_workspace_size(const sfa_mla_args *args, size_t *workspace_bytes);
+
+/* Phase 2: validate again and enqueue on `stream`.  workspace may be NULL
+ * only when the size query returned 0. */
+int ifa_decode(const ifa_decode_args *args, void *workspace, size_t workspace_bytes, ifa_stream_t stream);
+int ifa_decode_paged(const ifa_paged_args *args, void *workspace, size_t workspace_bytes, ifa_stream_t stream);
+int sfa_decode_mla(const sfa_mla_args *args, void *workspace, size_t workspace_bytes, ifa_stream_t stream);
+
+/* A static string naming a status code. */
+const char *ifa_status_string(int status);
+
+/* The library's ABI version (bumped when a struct changes). */
+int ifa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* IFA_DECODE_H */

@@ -1,0 +1,247 @@
+"""The C ABI without a GPU: symbols, status strings and argument validation.
+
+Validation runs before any HIP call, so every rejected call below returns its
+status code on a machine without a GPU.  Pointers are non-null dummies that
+the library must never dereference on these paths.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from decode_attention_kv_06_amd import binding as bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = ctypes.c_void_p(0x1000)
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "ifa_decode.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|const char \*)\s*\**\s*(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = header_functions()
+    assert {"ifa_decode", "ifa_decode_paged", "sfa_decode_mla", "ifa_decode_workspace_size",
+            "ifa_decode_paged_workspace_size", "sfa_decode_mla_workspace_size", "ifa_status_string",
+            "ifa_abi_version"} <= set(names)
+    L = bd.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings_and_version():
+    assert bd.lib().ifa_abi_version() >= 1
+    for code in (0, 161001, 161002, 361001):
+        assert bd.status_string(code).startswith("IFA_")
+    assert bd.status_string(42) == "unknown status"
+
+
+def test_struct_sizes_match_the_c_compiler(tmp_path):
+    src = tmp_path / "sz.c"
+    src.write_text('#include "ifa_decode.h"\n#include <stdio.h>\n#include <stddef.h>\n'
+                   'int main(void){printf("%zu %zu %zu\\n", sizeof(ifa_decode_args), sizeof(ifa_paged_args),'
+                   ' sizeof(sfa_mla_args)); return 0;}\n')
+    exe = tmp_path / "sz"
+    import subprocess
+    subprocess.check_call(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)])
+    a, b, c = map(int, subprocess.check_output([str(exe)]).split())
+    assert (a, b, c) == (ctypes.sizeof(bd.IfaDecodeArgs), ctypes.sizeof(bd.IfaPagedArgs),
+                         ctypes.sizeof(bd.SfaMlaArgs))
+
+
+# ---------------------------------------------------------------- dense IFA
+def dense_args(**kw):
+    a = bd.IfaDecodeArgs()
+    a.struct_size = ctypes.sizeof(bd.IfaDecodeArgs)
+    a.query = a.key = a.value = a.attention_out = FAKE
+    a.dtype_q = a.dtype_kv = a.dtype_out = bd.DT_BF16
+    a.input_layout = b"BSH"
+    a.batch, a.num_heads, a.num_key_value_heads, a.head_dim, a.kv_seq_len = 2, 8, 2, 128, 64
+    a.scale_value = 0.1
+    a.split_tokens = 64          # forced split: the size query needs no device
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def ws_size(fn, a):
+    n = ctypes.c_size_t(0)
+    return getattr(bd.lib(), fn)(ctypes.byref(a), ctypes.byref(n)), n.value
+
+
+def test_dense_valid_call_sizes_workspace_without_a_device():
+    rc, n = ws_size("ifa_decode_workspace_size", dense_args())
+    assert rc == 0
+    # 2 batches x 64 positions / 64 per chunk = 2 chunks; each holds N rows of D + 2 floats
+    assert n == 2 * 8 * 128 * 4 + 256
+
+
+LENS = (ctypes.c_int64 * 2)(10, 64)
+BAD_LENS = (ctypes.c_int64 * 2)(10, 65)
+PADS1 = (ctypes.c_int64 * 1)(3)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(query=None), 161001),
+    (dict(key=None), 161001),
+    (dict(value=None), 161001),
+    (dict(attention_out=None), 161001),
+    (dict(dtype_q=bd.DT_I8), 161002),
+    (dict(dtype_out=bd.DT_F16), 161002),
+    (dict(dtype_kv=bd.DT_F16), 161002),
+    (dict(input_layout=b"BNS"), 161002),
+    (dict(batch=0), 161002),
+    (dict(batch=65537), 161002),
+    (dict(num_heads=257), 161002),
+    (dict(num_key_value_heads=3), 161002),
+    (dict(num_key_value_heads=9), 161002),
+    (dict(head_dim=96), 161002),
+    (dict(kv_seq_len=0), 161002),
+    (dict(scale_value=float("nan")), 161002),
+    (dict(actual_seq_lengths=ctypes.cast(BAD_LENS, ctypes.c_void_p)), 161002),
+    (dict(kv_padding_size=ctypes.cast(PADS1, ctypes.c_void_p), kv_padding_size_count=3), 161002),
+    (dict(pse_shift=FAKE), 161002),
+    (dict(atten_mask=FAKE, dtype_mask=bd.DT_F16, mask_batch=2, mask_heads=1, mask_seq=64), 161002),
+    (dict(atten_mask=FAKE, dtype_mask=bd.DT_BOOL, mask_batch=3, mask_heads=1, mask_seq=64), 161002),
+    (dict(atten_mask=FAKE, dtype_mask=bd.DT_BOOL, mask_batch=2, mask_heads=4, mask_seq=64), 161002),
+    (dict(atten_mask=FAKE, dtype_mask=bd.DT_BOOL, mask_batch=2, mask_heads=1, mask_seq=63), 161002),
+    (dict(antiquant_scale=FAKE, antiquant_offset=FAKE, antiquant_mode=2), 161002),
+    (dict(dtype_kv=bd.DT_I8, antiquant_mode=0), 161002),
+    (dict(dtype_kv=bd.DT_I8, antiquant_mode=2), 161001),
+    (dict(split_tokens=24), 161002),
+    (dict(struct_size=8), 161002),
+])
+def test_dense_rejections(kw, code):
+    assert ws_size("ifa_decode_workspace_size", dense_args(**kw))[0] == code
+    # the run call validates identically and launches nothing
+    assert bd.lib().ifa_decode(ctypes.byref(dense_args(**kw)), None, 0, None) == code
+
+
+def test_dense_null_args_and_size_pointer():
+    assert bd.lib().ifa_decode_workspace_size(None, None) == 161001
+    n = ctypes.c_size_t()
+    assert bd.lib().ifa_decode_workspace_size(None, ctypes.byref(n)) == 161001
+
+
+def test_dense_left_padding_window_rules_accept():
+    a = dense_args(actual_seq_lengths=ctypes.cast(LENS, ctypes.c_void_p),
+                   kv_padding_size=ctypes.cast(PADS1, ctypes.c_void_p), kv_padding_size_count=1)
+    # batch 1: start = 64 - 3 - 64 < 0 -> zero row, no chunk; batch 0: [51, 61) -> 1 chunk
+    rc, n = ws_size("ifa_decode_workspace_size", a)
+    assert rc == 0 and n == 1 * 8 * 128 * 4 + 256
+
+
+def test_dense_workspace_too_small_is_rejected():
+    a = dense_args()
+    assert bd.lib().ifa_decode(ctypes.byref(a), FAKE, 16, None) == 161002
+
+
+# ---------------------------------------------------------------- paged IFA
+PLENS = (ctypes.c_int64 * 2)(100, 64)
+
+
+def paged_args(**kw):
+    a = bd.IfaPagedArgs()
+    a.struct_size = ctypes.sizeof(bd.IfaPagedArgs)
+    a.query = a.key_cache = a.value_cache = a.attention_out = a.block_table = FAKE
+    a.dtype_q = a.dtype_kv = a.dtype_out = bd.DT_F16
+    a.input_layout = b"BNSD"
+    a.batch, a.num_heads, a.num_key_value_heads, a.head_dim = 2, 4, 2, 64
+    a.scale_value = 0.125
+    a.actual_seq_lengths = ctypes.cast(PLENS, ctypes.c_void_p)
+    a.max_blocks_per_seq, a.block_size, a.num_blocks, a.kv_cache_layout = 4, 32, 8, 0
+    a.split_tokens = 32
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_paged_valid_call_sizes_workspace():
+    rc, n = ws_size("ifa_decode_paged_workspace_size", paged_args())
+    assert rc == 0
+    assert n == (4 + 2) * 4 * 64 * 4 + 256
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(block_table=None), 161001),
+    (dict(actual_seq_lengths=None), 161001),
+    (dict(key_cache=None), 161001),
+    (dict(block_size=8), 161002),
+    (dict(block_size=24), 161002),
+    (dict(block_size=528), 161002),
+    (dict(dtype_kv=bd.DT_I8, antiquant_scale=FAKE, antiquant_offset=FAKE, antiquant_mode=1, block_size=48), 161002),
+    (dict(max_blocks_per_seq=3), 161002),          # 100 positions need 4 blocks of 32
+    (dict(num_blocks=5), 161002),                  # 4 + 2 blocks needed
+    (dict(kv_cache_layout=2), 161002),
+    (dict(input_layout=b"BSH"), 161002),           # BSH pairs only with (blocknum, blocksize, H)
+])
+def test_paged_rejections(kw, code):
+    assert ws_size("ifa_decode_paged_workspace_size", paged_args(**kw))[0] == code
+
+
+def test_paged_bsh_with_hidden_layout_is_accepted():
+    assert ws_size("ifa_decode_paged_workspace_size", paged_args(input_layout=b"BSH", kv_cache_layout=1))[0] == 0
+
+
+def test_paged_int8_with_32_aligned_blocks_is_accepted():
+    a = paged_args(dtype_kv=bd.DT_I8, antiquant_scale=FAKE, antiquant_offset=FAKE, antiquant_mode=2, block_size=64,
+                   max_blocks_per_seq=2, num_blocks=4)
+    assert ws_size("ifa_decode_paged_workspace_size", a)[0] == 0
+
+
+# ---------------------------------------------------------------- SFA
+def sfa_args(**kw):
+    a = bd.SfaMlaArgs()
+    a.struct_size = ctypes.sizeof(bd.SfaMlaArgs)
+    a.query = a.query_rope = a.key = a.key_rope = a.value = a.sparse_indices = a.block_table = FAKE
+    a.actual_seq_lengths_kv = a.attention_out = FAKE
+    a.dtype = bd.DT_BF16
+    a.batch, a.q_seq, a.q_heads, a.kv_heads, a.head_dim, a.rope_dim = 2, 1, 16, 1, 512, 64
+    a.sparse_size, a.block_size, a.num_blocks, a.max_blocks = 100, 64, 10, 5
+    a.scale_value = 0.04
+    a.sparse_block_size, a.sparse_mode, a.attention_mode = 1, 0, 2
+    a.layout_query, a.layout_kv = b"BSND", b"PA_BSND"
+    a.split_hint = 2
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_sfa_valid_size_query():
+    assert ws_size("sfa_decode_mla_workspace_size", sfa_args())[0] == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(query=None), 161001),
+    (dict(query_rope=None), 161001),
+    (dict(key_rope=None), 161001),
+    (dict(sparse_indices=None), 161001),
+    (dict(block_table=None), 161001),
+    (dict(actual_seq_lengths_kv=None), 161001),
+    (dict(attention_out=None), 161001),
+    (dict(dtype=bd.DT_I8), 161002),
+    (dict(kv_heads=2), 161002),
+    (dict(head_dim=256), 161002),
+    (dict(rope_dim=32), 161002),
+    (dict(q_heads=129), 161002),
+    (dict(q_heads=0), 161002),
+    (dict(q_seq=2), 161002),
+    (dict(sparse_size=0), 161002),
+    (dict(block_size=24), 161002),
+    (dict(block_size=1040), 161002),
+    (dict(sparse_block_size=2), 161002),
+    (dict(sparse_mode=1), 161002),
+    (dict(attention_mode=1), 161002),
+    (dict(layout_query=b"TND"), 161002),
+    (dict(layout_kv=b"BSND"), 161002),
+    (dict(scale_value=float("inf")), 161002),
+])
+def test_sfa_rejections(kw, code):
+    assert ws_size("sfa_decode_mla_workspace_size", sfa_args(**kw))[0] == code
+
+
+def test_sfa_mode_three_is_accepted():
+    assert ws_size("sfa_decode_mla_workspace_size", sfa_args(sparse_mode=3))[0] == 0
