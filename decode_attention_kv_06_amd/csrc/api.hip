@@ -6,6 +6,8 @@
 // SparseFlashAttention README; it makes no HIP call, so an invalid call
 // returns before touching the device.
 #include <math.h>
+#include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -37,119 +39,96 @@ int parse_layout(const char *s, int *out) {
 
 struct Window { int32_t lo, hi; };
 
+// One launch covers up to kSliceBatches batches.
+struct SlicePlan {
+    int b0 = 0, nb = 0;
+    int64_t total = 0, piece = 0;
+    int n_pieces = 0;
+    std::vector<int64_t> pre;         // nb + 1 entries
+    std::vector<int32_t> sbase, maxseg;
+    int64_t slot_base = 0, slots = 0;
+};
+
 struct IfaPlan {
     int kv = 0, D = 0, G = 0, n_hg = 0, g = 0, N = 0, Nkv = 0, B = 0;
     bool paged = false;
-    int chunk = 0;
     std::vector<Window> win;             // per batch
-    std::vector<int32_t> nch;            // chunks per batch
-    int64_t total_chunks = 0;
+    std::vector<SlicePlan> slices;
+    int64_t total_slots = 0;
     size_t workspace = 0;
 };
 
-// Device facts used by the planner, cached per device.
-struct DeviceInfo { int cus = 0; };
-
 std::mutex g_mu;
-DeviceInfo g_dev[64];
-int g_resident[64][3][4][4][2];   // [dev][kv][log2 D/64][log2 G][paged] resident waves, 0 = unknown
+int g_resident[64][3][4][4][2][2];   // [dev][kv][log2 D/64][log2 G][paged][masked] resident waves, 0 = unknown
 
 int current_device(int *dev) { return hipGetDevice(dev) == hipSuccess ? IFA_OK : IFA_ERR_RUNTIME; }
 
-int resident_waves(int kv, int D, int G, bool paged) {
+int resident_waves(int kv, int D, int G, bool paged, bool masked) {
     int dev = 0;
     if (current_device(&dev) != IFA_OK || dev < 0 || dev >= 64) return 0;
     const int di = D == 64 ? 0 : D == 128 ? 1 : D == 256 ? 2 : 3;
     const int gi = G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3;
     std::lock_guard<std::mutex> lk(g_mu);
-    int &slot = g_resident[dev][kv][di][gi][paged ? 1 : 0];
-    if (!slot) slot = split_resident_waves(kv, D, G, paged);
+    int &slot = g_resident[dev][kv][di][gi][paged ? 1 : 0][masked ? 1 : 0];
+    if (!slot) slot = split_resident_waves(kv, D, G, paged, masked);
     return slot;
 }
 
-// Greedy list-scheduling estimate of the split kernel's makespan, in units of
-// KV positions, for a chunk size: workgroups (four consecutive work items)
-// are handed to the earliest free slot in grid order, as the dispatcher does.
-double simulate(const std::vector<Window> &win, int chunk, int heads_per_chunk, int slots, double item_cost) {
-    std::priority_queue<double, std::vector<double>, std::greater<double>> q;
-    for (int i = 0; i < slots; i++) q.push(0.0);
-    int pending = 0;
-    double wg_cost = 0.0;
-    double finish = 0.0;
-    auto emit = [&]() {
-        double t = q.top();
-        q.pop();
-        t += wg_cost + item_cost;
-        finish = std::max(finish, t);
-        q.push(t);
-        pending = 0;
-        wg_cost = 0.0;
-    };
-    for (const Window &w : win) {
-        const int len = w.hi - w.lo;
-        for (int c0 = 0; c0 < len; c0 += chunk) {
-            const double n = std::min(chunk, len - c0);
-            for (int h = 0; h < heads_per_chunk; h++) {
-                wg_cost = std::max(wg_cost, n);
-                if (++pending == kWavesPerBlock) emit();
-            }
-        }
-    }
-    if (pending) emit();
-    return finish;
-}
-
-int choose_chunk(const std::vector<Window> &win, int tt, int heads_per_chunk, int waves, double partial_cost) {
-    const int cands[] = {64, 96, 128, 192, 256, 384, 512, 768, 1024, 1536, 2048, 3072, 4096};
-    int64_t total = 0;
-    int maxlen = 0;
-    for (const Window &w : win) {
-        total += w.hi - w.lo;
-        maxlen = std::max(maxlen, w.hi - w.lo);
-    }
-    if (total == 0) return std::max(tt, 64);
-    const int slots = std::max(1, waves / kWavesPerBlock);
-    int best = 0;
-    double best_cost = 0.0;
-    for (int c : cands) {
-        if (c % tt) continue;
-        if (best && c > maxlen + tt) break;    // larger chunks no longer change the plan
-        // Fixed cost per work item (first-load latency, q load, state merge)
-        // plus the partial write and read-back, in position equivalents.
-        const double cost = simulate(win, c, heads_per_chunk, slots, 24.0 + partial_cost);
-        if (!best || cost < best_cost * 0.98) {
-            best = c;
-            best_cost = cost;
-        }
-    }
-    return best ? best : std::max(tt, 64);
-}
-
-int chunk_count(int len, int chunk) { return len > 0 ? (len + chunk - 1) / chunk : 0; }
-
-int finish_plan(IfaPlan &p, int64_t split_tokens, int eb) {
+// Exact balancing: the rows (b, j, hg) of a slice are laid end to end and cut
+// into n_pieces equal pieces, one per resident wave of the split kernel, so
+// every wave streams the same number of KV positions.  A row meets at most
+// ceil(len / piece) + 1 pieces, which bounds its partial slots.
+int finish_plan(IfaPlan &p, int64_t split_tokens, bool masked) {
     p.G = 1;
     while (p.G < p.g && p.G < 8) p.G <<= 1;
     p.n_hg = (p.g + p.G - 1) / p.G;
-    const int tt = split_tile_tokens(p.kv, p.D, p.G);
-    if (split_tokens > 0) {
-        p.chunk = (int)split_tokens;
-    } else {
-        const int waves = resident_waves(p.kv, p.D, p.G, p.paged);
+    int waves = 0;
+    if (split_tokens <= 0) {
+        waves = resident_waves(p.kv, p.D, p.G, p.paged, masked);
         if (waves <= 0) return IFA_ERR_RUNTIME;
-        const double per_pos_bytes = 2.0 * p.D * eb;
-        const double partial = 2.0 * p.G * (p.D + 2) * 4.0 / per_pos_bytes;
-        p.chunk = choose_chunk(p.win, tt, p.Nkv * p.n_hg, waves, partial);
     }
-    p.nch.resize(p.B);
-    p.total_chunks = 0;
-    for (int b = 0; b < p.B; b++) {
-        p.nch[b] = chunk_count(p.win[b].hi - p.win[b].lo, p.chunk);
-        p.total_chunks += p.nch[b];
+    const int64_t rows_per_batch = (int64_t)p.Nkv * p.n_hg;
+    p.slices.clear();
+    p.total_slots = 0;
+    for (int b0 = 0; b0 < p.B; b0 += kSliceBatches) {
+        SlicePlan sp;
+        sp.b0 = b0;
+        sp.nb = std::min(kSliceBatches, p.B - b0);
+        sp.pre.resize(sp.nb + 1);
+        sp.sbase.resize(sp.nb);
+        sp.maxseg.resize(sp.nb);
+        int64_t pos = 0;
+        for (int i = 0; i < sp.nb; i++) {
+            sp.pre[i] = pos;
+            pos += (int64_t)(p.win[b0 + i].hi - p.win[b0 + i].lo) * rows_per_batch;
+        }
+        sp.pre[sp.nb] = pos;
+        sp.total = pos;
+        if (split_tokens > 0) sp.piece = split_tokens;
+        else sp.piece = std::max<int64_t>(64, (pos + waves - 1) / std::max(1, waves));
+        sp.n_pieces = (int)((pos + sp.piece - 1) / sp.piece);
+        int64_t slots = 0;
+        for (int i = 0; i < sp.nb; i++) {
+            const int64_t len = p.win[b0 + i].hi - p.win[b0 + i].lo;
+            sp.maxseg[i] = len > 0 ? (int32_t)((len + sp.piece - 1) / sp.piece + 1) : 0;
+            sp.sbase[i] = (int32_t)slots;
+            slots += rows_per_batch * sp.maxseg[i];
+        }
+        if (slots > INT32_MAX || pos / sp.piece > INT32_MAX) return IFA_ERR_PARAM_INVALID;
+        sp.slot_base = p.total_slots;
+        sp.slots = slots;
+        p.total_slots += slots;
+        p.slices.push_back(std::move(sp));
     }
-    const size_t acc = (size_t)p.total_chunks * p.N * p.D * sizeof(float);
-    const size_t ml = (size_t)p.total_chunks * p.N * 2 * sizeof(float);
+    const size_t acc = (size_t)p.total_slots * p.G * p.D * sizeof(float);
+    const size_t ml = (size_t)p.total_slots * p.G * 2 * sizeof(float);
     p.workspace = (acc + 255) / 256 * 256 + (ml + 255) / 256 * 256;
+    if (getenv("IFA_DEBUG_PLAN")) {
+        for (const SlicePlan &sp : p.slices)
+            fprintf(stderr, "ifa plan: kv=%d D=%d g=%d G=%d n_hg=%d slice b0=%d nb=%d positions=%lld piece=%lld "
+                    "waves=%d slots=%lld\n", p.kv, p.D, p.g, p.G, p.n_hg, sp.b0, sp.nb, (long long)sp.total,
+                    (long long)sp.piece, sp.n_pieces, (long long)sp.slots);
+    }
     return IFA_OK;
 }
 
@@ -301,10 +280,10 @@ struct Launch {
 };
 
 int run(const IfaPlan &p, const Launch &L, void *ws, size_t ws_bytes, hipStream_t stream) {
-    if (p.workspace && (!ws || ws_bytes < p.workspace)) return p.workspace && !ws ? IFA_ERR_PARAM_NULLPTR
-                                                                                  : IFA_ERR_PARAM_INVALID;
+    if (p.workspace && !ws) return IFA_ERR_PARAM_NULLPTR;
+    if (ws_bytes < p.workspace) return IFA_ERR_PARAM_INVALID;
     float *part_acc = reinterpret_cast<float *>(ws);
-    const size_t acc_bytes = ((size_t)p.total_chunks * p.N * p.D * sizeof(float) + 255) / 256 * 256;
+    const size_t acc_bytes = ((size_t)p.total_slots * p.G * p.D * sizeof(float) + 255) / 256 * 256;
     float *part_ml = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + acc_bytes);
 
     SplitParams sp;
@@ -335,7 +314,6 @@ int run(const IfaPlan &p, const Launch &L, void *ws, size_t ws_bytes, hipStream_
     sp.aq_mode = L.aq_mode;
     sp.q_bf16 = L.q_bf16;
     sp.score_mul = (float)(L.scale * 1.4426950408889634);
-    sp.chunk = p.chunk;
 
     CombineParams cp;
     memset(&cp, 0, sizeof cp);
@@ -345,37 +323,38 @@ int run(const IfaPlan &p, const Launch &L, void *ws, size_t ws_bytes, hipStream_
     cp.N = p.N;
     cp.Nkv = p.Nkv;
     cp.g = p.g;
+    cp.G = p.G;
+    cp.n_hg = p.n_hg;
     cp.D = p.D;
     cp.out_bf16 = L.q_bf16;
     cp.aq_mode = L.aq_mode;
 
-    int64_t chunk_base = 0;
     const bool timed = L.ev_begin && L.ev_end;
     if (timed && hipEventRecord(L.ev_begin, stream) != hipSuccess) return IFA_ERR_RUNTIME;
-    for (int b0 = 0; b0 < p.B; b0 += kSliceBatches) {
-        const int nb = std::min(kSliceBatches, p.B - b0);
-        sp.nb = cp.nb = nb;
-        sp.b0 = cp.b0 = b0;
-        int32_t cum = 0;
-        for (int i = 0; i < nb; i++) {
-            sp.lo[i] = p.win[b0 + i].lo;
-            sp.hi[i] = p.win[b0 + i].hi;
-            sp.cum[i] = cp.cum[i] = cum;
-            cum += p.nch[b0 + i];
+    for (size_t si = 0; si < p.slices.size(); si++) {
+        const SlicePlan &s = p.slices[si];
+        sp.nb = cp.nb = s.nb;
+        sp.b0 = cp.b0 = s.b0;
+        sp.total = s.total;
+        sp.piece = cp.piece = s.piece;
+        sp.n_pieces = s.n_pieces;
+        for (int i = 0; i < s.nb; i++) {
+            sp.pre[i] = cp.pre[i] = s.pre[i];
+            sp.lo[i] = p.win[s.b0 + i].lo;
+            sp.len[i] = cp.len[i] = p.win[s.b0 + i].hi - p.win[s.b0 + i].lo;
+            sp.sbase[i] = cp.sbase[i] = s.sbase[i];
+            sp.maxseg[i] = cp.maxseg[i] = s.maxseg[i];
         }
-        sp.cum[nb] = cp.cum[nb] = cum;
-        sp.part_acc = part_acc + chunk_base * p.N * p.D;
-        sp.part_ml = part_ml + chunk_base * p.N * 2;
+        sp.pre[s.nb] = cp.pre[s.nb] = s.pre[s.nb];
+        sp.part_acc = part_acc + s.slot_base * p.G * p.D;
+        sp.part_ml = part_ml + s.slot_base * p.G * 2;
         cp.part_acc = sp.part_acc;
         cp.part_ml = sp.part_ml;
-        const int64_t items = (int64_t)cum * p.Nkv * p.n_hg;
-        if (items > INT32_MAX) return IFA_ERR_PARAM_INVALID;
-        sp.n_items = (int)items;
-        if (items > 0 && launch_split(sp, p.kv, p.D, p.G, p.paged, stream) != hipSuccess) return IFA_ERR_RUNTIME;
-        if (timed && b0 + kSliceBatches >= p.B && hipEventRecord(L.ev_end, stream) != hipSuccess)
+        if (s.total > 0 && launch_split(sp, p.kv, p.D, p.G, p.paged, L.mask_mode != 0, stream) != hipSuccess)
+            return IFA_ERR_RUNTIME;
+        if (timed && si + 1 == p.slices.size() && hipEventRecord(L.ev_end, stream) != hipSuccess)
             return IFA_ERR_RUNTIME;
         if (launch_combine(cp, stream) != hipSuccess) return IFA_ERR_RUNTIME;
-        chunk_base += cum;
     }
     return IFA_OK;
 }
@@ -449,8 +428,6 @@ Launch paged_launch(const ifa_paged_args *a, const IfaPlan &p) {
     return L;
 }
 
-int eb_of(int dkv) { return dkv == IFA_DT_I8 ? 1 : 2; }
-
 }  // namespace
 
 extern "C" {
@@ -473,7 +450,7 @@ int ifa_decode_workspace_size(const ifa_decode_args *a, size_t *bytes) {
     IfaCommon c;
     int rc = plan_dense(a, p, c);
     if (rc) return rc;
-    rc = finish_plan(p, a->split_tokens, eb_of(a->dtype_kv));
+    rc = finish_plan(p, a->split_tokens, a->atten_mask != nullptr);
     if (rc) return rc;
     *bytes = p.workspace;
     return IFA_OK;
@@ -484,7 +461,7 @@ int ifa_decode(const ifa_decode_args *a, void *ws, size_t ws_bytes, ifa_stream_t
     IfaCommon c;
     int rc = plan_dense(a, p, c);
     if (rc) return rc;
-    rc = finish_plan(p, a->split_tokens, eb_of(a->dtype_kv));
+    rc = finish_plan(p, a->split_tokens, a->atten_mask != nullptr);
     if (rc) return rc;
     return run(p, dense_launch(a, p, c), ws, ws_bytes, reinterpret_cast<hipStream_t>(stream));
 }
@@ -495,7 +472,7 @@ int ifa_decode_paged_workspace_size(const ifa_paged_args *a, size_t *bytes) {
     IfaCommon c;
     int rc = plan_paged(a, p, c);
     if (rc) return rc;
-    rc = finish_plan(p, a->split_tokens, eb_of(a->dtype_kv));
+    rc = finish_plan(p, a->split_tokens, a->atten_mask != nullptr);
     if (rc) return rc;
     *bytes = p.workspace;
     return IFA_OK;
@@ -506,7 +483,7 @@ int ifa_decode_paged(const ifa_paged_args *a, void *ws, size_t ws_bytes, ifa_str
     IfaCommon c;
     int rc = plan_paged(a, p, c);
     if (rc) return rc;
-    rc = finish_plan(p, a->split_tokens, eb_of(a->dtype_kv));
+    rc = finish_plan(p, a->split_tokens, a->atten_mask != nullptr);
     if (rc) return rc;
     return run(p, paged_launch(a, p), ws, ws_bytes, reinterpret_cast<hipStream_t>(stream));
 }

@@ -19,32 +19,105 @@ __device__ __forceinline__ float ld_param(const void *p, int64_t i, bool bf16) {
     return bf16 ? __builtin_bit_cast(float, bits << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
 }
 
+// Maximum over the 64 lanes: DPP within each 16-lane row, then the four row
+// results through readlane.
+__device__ __forceinline__ float wave_max(float x) {
+    auto dpp = [](float v, auto ctrl) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), decltype(ctrl)::value,
+                                                                  0xF, 0xF, true));
+    };
+    x = fmaxf(x, dpp(x, std::integral_constant<int, 0xB1>{}));
+    x = fmaxf(x, dpp(x, std::integral_constant<int, 0x4E>{}));
+    x = fmaxf(x, dpp(x, std::integral_constant<int, 0x141>{}));
+    x = fmaxf(x, dpp(x, std::integral_constant<int, 0x140>{}));
+    const int xi = __builtin_bit_cast(int, x);
+    const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 0));
+    const float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 16));
+    const float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 32));
+    const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 48));
+    return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+
+// One wave per (b, h) row.  The split states are read lane-parallel (lane i
+// holds split i, 64 at a time); the weighted sum over splits runs in split
+// order in every lane, so the result does not depend on timing.
 __global__ __launch_bounds__(256) void combine_kernel(const CombineParams P) {
     const int lane = threadIdx.x & 63;
     const int row = blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (row >= P.nb * P.N) return;
     const int bl = row / P.N, h = row % P.N;
     const int64_t b = P.b0 + bl;
-    const int c0 = P.cum[bl], nch = P.cum[bl + 1] - c0;
     const int D = P.D;
-
-    float M = -__builtin_huge_valf();
-    for (int i = 0; i < nch; i++) M = fmaxf(M, P.part_ml[((int64_t)(c0 + i) * P.N + h) * 2]);
-    float L = 0.f;
-    for (int i = 0; i < nch; i++) {
-        const float2 ml = *reinterpret_cast<const float2 *>(P.part_ml + ((int64_t)(c0 + i) * P.N + h) * 2);
-        L += __builtin_amdgcn_exp2f(ml.x - M) * ml.y;
+    // the segments of row (b, j, hg) sit in consecutive slots, one per piece
+    // that the row overlaps (the split kernel's slot rule)
+    const int jj = h / P.g, hin = h - jj * P.g;
+    const int hg = hin / P.G, hh = hin - hg * P.G;
+    const int rj = jj * P.n_hg + hg;
+    const int len = P.len[bl];
+    int nch = 0;
+    int64_t slot0 = 0;
+    if (len > 0) {
+        const int64_t start = P.pre[bl] + (int64_t)rj * len;
+        nch = (int)((start + len - 1) / P.piece - start / P.piece + 1);
+        slot0 = P.sbase[bl] + (int64_t)rj * P.maxseg[bl];
     }
+    // partial state i of this head lives at row (slot0 + i) * G + hh
+    auto prow = [&](int i) -> int64_t { return (slot0 + i) * P.G + hh; };
+    const float2 *ml = reinterpret_cast<const float2 *>(P.part_ml);
+
+    // (m, l) of up to 64 splits in one load round, lane i holding split i
     const bool bf = P.out_bf16 != 0;
-    for (int d = lane; d < D; d += 64) {
-        float o = 0.f;
-        for (int i = 0; i < nch; i++) {
-            const int64_t pr = (int64_t)(c0 + i) * P.N + h;
-            o += __builtin_amdgcn_exp2f(P.part_ml[pr * 2] - M) * P.part_acc[pr * D + d];
+    constexpr int kMaxPerLane = 8;          // D <= 512
+    const int per_lane = D / 64;            // D >= 64
+    float o[kMaxPerLane];
+#pragma unroll
+    for (int e = 0; e < kMaxPerLane; e++) o[e] = 0.f;
+    float L = 0.f;
+    float M = -__builtin_huge_valf();
+    for (int i0 = 0; i0 < nch; i0 += 64) {
+        const int i = i0 + lane;
+        if (i < nch) M = fmaxf(M, ml[prow(i)].x);
+    }
+    M = wave_max(M);
+    for (int i0 = 0; i0 < nch; i0 += 64) {
+        const int cnt = min(64, nch - i0);
+        float w = 0.f, lw = 0.f;
+        if (lane < cnt) {
+            const float2 v = ml[prow(i0 + lane)];
+            w = __builtin_amdgcn_exp2f(v.x - M);
+            lw = w * v.y;
         }
+        // Splits in order, eight at a time: their loads are issued together
+        // (indices past the last split re-read it and get weight 0), then
+        // accumulated in split order with the weight broadcast by readlane.
+        constexpr int U = 8;
+        for (int i = 0; i < cnt; i += U) {
+            float v[U][kMaxPerLane];
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                const float *acc = P.part_acc + prow(i0 + min(i + u, cnt - 1)) * D;
+#pragma unroll
+                for (int e = 0; e < kMaxPerLane; e++) v[u][e] = e < per_lane ? acc[lane + 64 * e] : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                const int iu = min(i + u, 63);
+                float wi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), iu));
+                float li = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lw), iu));
+                if (i + u >= cnt) wi = li = 0.f;
+                L += li;
+#pragma unroll
+                for (int e = 0; e < kMaxPerLane; e++) o[e] += wi * v[u][e];
+            }
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < kMaxPerLane; e++) {
+        if (e >= per_lane) break;
+        const int d = lane + 64 * e;
         float res = 0.f;
         if (nch > 0 && L > 0.f) {
-            res = o / L;
+            res = o[e] / L;
             if (P.aq_mode) {
                 const int j = h / P.g;
                 const int64_t pi = (P.aq_mode == 1) ? 1 : ((int64_t)P.Nkv + j) * D + d;

@@ -1,0 +1,7 @@
+// Split-KV decode kernels for f16 KV caches (instantiations of ifa_split_impl.h).
+#include "ifa_split_impl.h"
+
+namespace ifa {
+template hipError_t launch_split_kv<KV_F16>(const SplitParams &, int, int, bool, bool, hipStream_t);
+template const void *split_kernel_ptr<KV_F16>(int, int, bool, bool);
+}  // namespace ifa

@@ -1,0 +1,586 @@
+// Split-KV decode kernel for IncreFlashAttention on gfx950 (template body;
+// instantiated per KV dtype in ifa_split_{f16,bf16,i8}.hip).
+//
+// Computes, for one segment of KV positions of one (batch, KV head, head
+// group), the partial softmax state of
+//     softmax(scale * q K^T) V                (IncreFlashAttention README, "Formula")
+// as the running maximum m (log2 domain), the running sum l of exp2(x - m)
+// and the unnormalised sum of exp2(x - m) * v.  The split-combine kernel
+// merges the segments of a row.
+//
+// Mapping to the hardware: one wave64 per piece of work, four independent
+// waves per workgroup.  A KV row of D elements is read by D/8 consecutive
+// lanes, 16 bytes each (8 bytes for int8), so one load instruction covers
+// 64/(D/8) consecutive rows: whole 128-byte lines, no LDS staging.  Each lane
+// keeps the softmax state of the rows it reads; the lanes of one row hold
+// identical copies (their partial dot products are reduced with DPP inside
+// the 16-lane DPP row), and the row groups are merged once per segment.  Dot
+// products use v_dot2_f32_{f16,bf16} (two products per lane-op, fp32
+// accumulation); int8 rows are widened exactly to fp16 with byte permutes.
+// The next tile's K/V loads are in flight while the current tile computes.
+#pragma once
+
+#include "internal.h"
+
+namespace ifa {
+namespace split_detail {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kMaxInit = -1.0e30f;   // finite start value of the running max
+constexpr int kTblSlots = 256;        // staged block ids per wave (paged caches)
+// The running max is raised only when a tile's max exceeds it by more than
+// this many log2 units, so p = exp2(x - m) stays below 2^kLazy (exact: the
+// same m scales both l and the accumulator).
+constexpr float kLazy = 8.0f;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+
+__device__ __forceinline__ float swz_xor16(float x) {
+    // ds_swizzle bit mode: and 0x1f, or 0, xor 0x10 (within 32-lane halves).
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F));
+}
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c, std::integral_constant<int, KV_BF16>) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c, std::integral_constant<int, KV_F16>) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c, false);
+}
+
+__device__ __forceinline__ uint32_t pack_p(float a, float b, std::integral_constant<int, KV_BF16>) {
+    bf16x2 r;
+    r[0] = (__bf16)a;
+    r[1] = (__bf16)b;
+    return __builtin_bit_cast(uint32_t, r);
+}
+__device__ __forceinline__ uint32_t pack_p(float a, float b, std::integral_constant<int, KV_F16>) {
+    f16x2 r;
+    r[0] = (_Float16)a;
+    r[1] = (_Float16)b;
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// int8 -> fp16, exact: the byte b (two's complement) is xor'ed with 0x80 to
+// u = b + 128, placed under the fp16 exponent of 1024 (0x64 high byte) to
+// give 1024 + u, and 1152 is subtracted.  Values 1024..1279 are exact in fp16.
+__device__ __forceinline__ uint32_t i8pair_to_f16x2(uint32_t biased_pair) {
+    f16x2 h = __builtin_bit_cast(f16x2, biased_pair);
+    const f16x2 c = {(_Float16)1152.0f, (_Float16)1152.0f};
+    return __builtin_bit_cast(uint32_t, h - c);
+}
+constexpr uint32_t kF16Hi = 0x64646464u;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __builtin_bit_cast(float, bits16 << 16); }
+__device__ __forceinline__ float f16_to_f32(uint32_t bits16) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+// s / block_size for 32-bit s (Granlund-Montgomery, "Division by invariant
+// integers using multiplication", round-up multiplier, valid for divisors >= 2).
+__device__ __forceinline__ uint32_t div_bs(uint32_t s, uint32_t magic, int shift) {
+    uint32_t t1 = __umulhi(magic, s);
+    return (t1 + ((s - t1) >> 1)) >> (shift - 1);
+}
+
+template <int KV, int D, int G>
+struct Cfg {
+    static constexpr int LPR = D / 8;                      // lanes per KV row
+    static constexpr int RPI = 64 / LPR;                   // rows per load instruction
+    static constexpr int W = (KV == KV_I8) ? 2 : 4;        // dwords per lane per row
+    static constexpr int EB = (KV == KV_I8) ? 1 : 2;       // element bytes
+    static constexpr int RT = (G >= 8) ? 2 : (G >= 4) ? 4 : 8;   // row steps per tile
+    static constexpr int TT = RT * RPI;                    // positions per tile
+};
+
+// Waves per SIMD the register budget is sized for (G heads of state per lane).
+template <int G>
+constexpr int waves_per_eu() { return (G == 1 || G == 4) ? 3 : 2; }
+
+template <int KV, int D, int G, bool PAGED, bool MASKED>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_per_eu<G>(), 8)))
+void split_kernel(const SplitParams P) {
+    using C = Cfg<KV, D, G>;
+    constexpr int LPR = C::LPR, RPI = C::RPI, W = C::W, EB = C::EB, RT = C::RT, TT = C::TT;
+    constexpr bool I8 = KV == KV_I8;
+    using DotK = std::integral_constant<int, I8 ? KV_F16 : KV>;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wave_id = blockIdx.x * kWavesPerBlock + wave;
+    if (wave_id >= P.n_pieces) return;
+    const int r = lane / LPR;      // row group
+    const int c = lane % LPR;      // 8-element slot within the row
+    const char *kb = reinterpret_cast<const char *>(P.k);
+    const char *vb = reinterpret_cast<const char *>(P.v);
+    const int64_t lane_byte = (int64_t)8 * c * EB;
+    __shared__ int32_t s_tbl[kWavesPerBlock][kTblSlots];
+    int32_t *wtbl = s_tbl[wave];
+
+    // This wave's piece of the flattened (batch, KV head, head group,
+    // position) space; it is cut into segments at row boundaries, and every
+    // segment leaves one partial softmax state.
+    const int64_t f1 = min(P.total, (int64_t)(wave_id + 1) * P.piece);
+    for (int64_t f = (int64_t)wave_id * P.piece; f < f1;) {
+        // Batch of position f: the number of batches whose rows start at or before f.
+        int cnt = 0;
+        for (int e0 = 0; e0 < P.nb; e0 += 64) {
+            const int e = e0 + lane;
+            const bool le = e < P.nb && P.pre[e] <= f;
+            cnt += __popcll(__ballot(le));
+        }
+        const int bl = __builtin_amdgcn_readfirstlane(cnt - 1);
+        const int len = P.len[bl];
+        const int64_t within = f - P.pre[bl];
+        const int rj = (int)(within / len);               // row of the batch: j * n_hg + hg
+        const int t0 = (int)(within - (int64_t)rj * len);
+        const int nseg = (int)min((int64_t)(len - t0), f1 - f);
+        const int j = rj / P.n_hg, hg = rj - j * P.n_hg;
+        const int lo = P.lo[bl] + t0;
+        const int hi = lo + nseg;
+        const int64_t b = P.b0 + bl;
+        const int64_t row_start = P.pre[bl] + (int64_t)rj * len;
+        const int64_t slot = P.sbase[bl] + (int64_t)rj * P.maxseg[bl] + (wave_id - row_start / P.piece);
+
+        // ------------------------------------------------------ query
+        const int hbase = j * P.g + hg * G;
+        uint32_t qv[G][4];
+        float qmul = P.score_mul;
+        if constexpr (!I8) {
+#pragma unroll
+            for (int hh = 0; hh < G; hh++) {
+                const bool ok = hg * G + hh < P.g;
+                const int64_t off = ((b * P.N + hbase + (ok ? hh : 0)) * D + 8 * c) * 2;
+                u32x4 x = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(P.q) + off);
+#pragma unroll
+                for (int w = 0; w < 4; w++) qv[hh][w] = ok ? x[w] : 0u;
+            }
+        } else {
+            // q' = q * s_K (K's antiquant scale) in fp16, multiplied by a power
+            // of two so the largest |q'| of the wave sits just under 2^15; the
+            // score multiplier takes the inverse power.  The K offset adds a
+            // constant per row and drops out of the softmax.
+            float qf[G][8];
+            float amax = 0.f;
+#pragma unroll
+            for (int hh = 0; hh < G; hh++) {
+                const bool ok = hg * G + hh < P.g;
+                const int64_t off = ((b * P.N + hbase + (ok ? hh : 0)) * D + 8 * c) * 2;
+                const u32x4 x = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(P.q) + off);
+#pragma unroll
+                for (int e = 0; e < 8; e++) {
+                    const uint32_t bits = (x[e >> 1] >> (16 * (e & 1))) & 0xFFFF;
+                    float qe = P.q_bf16 ? bf16_to_f32(bits) : f16_to_f32(bits);
+                    const int64_t si = (P.aq_mode == 1) ? 0 : (int64_t)j * D + 8 * c + e;
+                    const uint32_t sb = reinterpret_cast<const uint16_t *>(P.k_scale)[si];
+                    const float sc = P.q_bf16 ? bf16_to_f32(sb) : f16_to_f32(sb);
+                    qe = ok ? qe * sc : 0.f;
+                    qf[hh][e] = qe;
+                    amax = fmaxf(amax, fabsf(qe));
+                }
+            }
+            for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+            int ex = 0;
+            if (amax > 0.f) (void)frexpf(amax, &ex);        // amax < 2^ex
+            const float up = ldexpf(1.f, 15 - ex), down = ldexpf(1.f, ex - 15);
+            qmul = P.score_mul * down;
+#pragma unroll
+            for (int hh = 0; hh < G; hh++)
+#pragma unroll
+                for (int w = 0; w < 4; w++) {
+                    f16x2 h2;
+                    h2[0] = (_Float16)(qf[hh][2 * w] * up);
+                    h2[1] = (_Float16)(qf[hh][2 * w + 1] * up);
+                    qv[hh][w] = __builtin_bit_cast(uint32_t, h2);
+                }
+        }
+
+        // ------------------------------------------------------ addressing
+        // Dense: this lane's pointers to row (lo + r) of K and V; row i of the
+        // tile at ts is (ts - lo + i*RPI) row strides further (a uniform offset).
+        const char *kp = nullptr, *vp_ = nullptr;
+        int64_t sS_b = 0;
+        if constexpr (!PAGED) {
+            sS_b = P.sS * EB;
+            const int64_t base = (b * P.sB + (int64_t)j * P.sN) * EB + lane_byte + (int64_t)(lo + r) * sS_b;
+            kp = kb + base;
+            vp_ = vb + base;
+        }
+        const int lim = hi - 1 - lo - r;     // last valid row index relative to row lo + r
+        // Paged: the block ids of the segment are staged into this wave's LDS
+        // slots (one coalesced load), so finding a row costs an LDS read.
+        const int32_t *btab = nullptr;
+        int q_first = 0;
+        bool tbl_in_lds = false;
+        uint32_t blk_b = 0, head_b = 0, row_b = 0;
+        if constexpr (PAGED) {
+            btab = P.block_table + b * P.max_blocks;
+            blk_b = (uint32_t)(P.blk_stride * EB);
+            head_b = (uint32_t)(P.head_stride * EB) * (uint32_t)j;
+            row_b = (uint32_t)(P.row_stride * EB);
+            q_first = (int)div_bs((uint32_t)lo, P.bs_magic, P.bs_shift);
+            const int q_last = (int)div_bs((uint32_t)(hi - 1), P.bs_magic, P.bs_shift);
+            tbl_in_lds = q_last - q_first < kTblSlots;
+            if (tbl_in_lds) {
+                for (int e = lane; e <= q_last - q_first; e += 64) wtbl[e] = btab[q_first + e];
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            }
+        }
+        const uint8_t *mrow = nullptr;
+        if constexpr (MASKED) mrow = P.mask + (P.mask_sB ? b * P.mask_sB : 0) + (int64_t)hbase * P.mask_sH;
+
+        // Rolling pipeline with one tile resident: the K rows of tile k+1 are
+        // requested as soon as QK of tile k has consumed the K registers, and
+        // its V rows as soon as PV of tile k has consumed the V registers.
+        constexpr int MB = MASKED ? G : 1;
+        uint32_t kr[RT][W], vr[RT][W];
+        bool okr[RT];
+        uint32_t mbr[MB];       // mask byte of position ts + lane (per head for per-head masks)
+        int64_t offs[RT];       // paged: byte offsets of the tile's rows
+
+        auto load_rows = [&](const char *const (&ptr)[RT], uint32_t (&dst)[RT][W]) {
+#pragma unroll
+            for (int i = 0; i < RT; i++) {
+                if constexpr (W == 4) {
+                    const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(ptr[i]));
+                    dst[i][0] = x[0]; dst[i][1] = x[1]; dst[i][2] = x[2]; dst[i][3] = x[3];
+                } else {
+                    const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(ptr[i]));
+                    dst[i][0] = x[0]; dst[i][1] = x[1];
+                }
+            }
+        };
+        auto row_ptrs = [&](int ts, const char *base, const char *(&ptr)[RT]) {
+            if constexpr (!PAGED) {
+                if (ts + TT <= hi) {
+#pragma unroll
+                    for (int i = 0; i < RT; i++) ptr[i] = base + (int64_t)(ts - lo + i * RPI) * sS_b;
+                } else {
+#pragma unroll
+                    for (int i = 0; i < RT; i++) ptr[i] = base + (int64_t)min(ts - lo + i * RPI, lim) * sS_b;
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < RT; i++) ptr[i] = base + offs[i];
+            }
+        };
+        auto issue_k = [&](int ts) {
+            if constexpr (PAGED) {
+#pragma unroll
+                for (int i = 0; i < RT; i++) {
+                    const int t = min(ts + i * RPI + r, hi - 1);
+                    const uint32_t q = div_bs((uint32_t)t, P.bs_magic, P.bs_shift);
+                    const uint32_t rr = (uint32_t)t - q * (uint32_t)P.block_size;
+                    const int blk = tbl_in_lds ? wtbl[q - q_first] : btab[q];
+                    okr[i] = (unsigned)blk < (unsigned)P.num_blocks;
+                    // never dereference an out-of-range block id: read block 0 instead
+                    offs[i] = okr[i] ? (int64_t)(uint32_t)blk * blk_b + (head_b + rr * row_b) + lane_byte : 0;
+                }
+            }
+            if constexpr (MASKED) {
+                const int tm = min(ts + lane, hi - 1);
+#pragma unroll
+                for (int hh = 0; hh < MB; hh++) {
+                    // shared mask: only entry 0; per-head mask: one byte per real head
+                    const bool want = lane < TT && (P.mask_mode == 2 ? hg * G + hh < P.g : hh == 0);
+                    uint32_t v = 0;
+                    if (want) v = mrow[(int64_t)hh * P.mask_sH + tm];
+                    mbr[hh] = v;
+                }
+            }
+            const char *ptr[RT];
+            row_ptrs(ts, PAGED ? kb : kp, ptr);
+            load_rows(ptr, kr);
+        };
+        auto issue_v = [&](int ts) {
+            const char *ptr[RT];
+            row_ptrs(ts, PAGED ? vb : vp_, ptr);
+            load_rows(ptr, vr);
+        };
+
+        float m[G], l[G], acc[G][8];
+#pragma unroll
+        for (int hh = 0; hh < G; hh++) {
+            m[hh] = kMaxInit;
+            l[hh] = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; e++) acc[hh][e] = 0.f;
+        }
+
+        // -------------------------------------------------- main loop
+        int ts = lo;
+        issue_k(ts);
+        issue_v(ts);
+        while (true) {
+            // QK: partial dot products of the resident K rows, then the DPP
+            // reductions one step at a time across all rows and heads
+            float s[RT][G];
+#pragma unroll
+            for (int i = 0; i < RT; i++) {
+                uint32_t kk[4];
+                if constexpr (I8) {
+                    const uint32_t w0 = kr[i][0] ^ 0x80808080u, w1 = kr[i][1] ^ 0x80808080u;
+                    kk[0] = i8pair_to_f16x2(__builtin_amdgcn_perm(kF16Hi, w0, 0x04010400u));
+                    kk[1] = i8pair_to_f16x2(__builtin_amdgcn_perm(kF16Hi, w0, 0x04030402u));
+                    kk[2] = i8pair_to_f16x2(__builtin_amdgcn_perm(kF16Hi, w1, 0x04010400u));
+                    kk[3] = i8pair_to_f16x2(__builtin_amdgcn_perm(kF16Hi, w1, 0x04030402u));
+                } else {
+#pragma unroll
+                    for (int w = 0; w < 4; w++) kk[w] = kr[i][w];
+                }
+#pragma unroll
+                for (int hh = 0; hh < G; hh++) {
+                    float a = dot2(qv[hh][0], kk[0], 0.f, DotK{});
+#pragma unroll
+                    for (int w = 1; w < 4; w++) a = dot2(qv[hh][w], kk[w], a, DotK{});
+                    s[i][hh] = a;
+                }
+            }
+            if constexpr (LPR >= 2) {
+#pragma unroll
+                for (int i = 0; i < RT; i++)
+#pragma unroll
+                    for (int hh = 0; hh < G; hh++) s[i][hh] += dpp<0xB1>(s[i][hh]);   // quad_perm [1,0,3,2]
+            }
+            if constexpr (LPR >= 4) {
+#pragma unroll
+                for (int i = 0; i < RT; i++)
+#pragma unroll
+                    for (int hh = 0; hh < G; hh++) s[i][hh] += dpp<0x4E>(s[i][hh]);   // quad_perm [2,3,0,1]
+            }
+            if constexpr (LPR >= 8) {
+#pragma unroll
+                for (int i = 0; i < RT; i++)
+#pragma unroll
+                    for (int hh = 0; hh < G; hh++) s[i][hh] += dpp<0x141>(s[i][hh]);  // row_half_mirror
+            }
+            if constexpr (LPR >= 16) {
+#pragma unroll
+                for (int i = 0; i < RT; i++)
+#pragma unroll
+                    for (int hh = 0; hh < G; hh++) s[i][hh] += dpp<0x140>(s[i][hh]);  // row_mirror
+            }
+            if constexpr (LPR >= 32) {
+#pragma unroll
+                for (int i = 0; i < RT; i++)
+#pragma unroll
+                    for (int hh = 0; hh < G; hh++) s[i][hh] += swz_xor16(s[i][hh]);
+            }
+            if constexpr (LPR >= 64) {
+#pragma unroll
+                for (int i = 0; i < RT; i++)
+#pragma unroll
+                    for (int hh = 0; hh < G; hh++) s[i][hh] += __shfl_xor(s[i][hh], 32);
+            }
+
+            // validity bitmaps of the tile, taken before the next tile's
+            // loads reuse the registers
+            uint64_t mbits[MB];
+            if constexpr (MASKED) {
+                if (P.mask_mode == 1) {
+                    mbits[0] = __ballot(mbr[0] != 0);
+#pragma unroll
+                    for (int hh = 1; hh < MB; hh++) mbits[hh] = mbits[0];
+                } else {
+#pragma unroll
+                    for (int hh = 0; hh < MB; hh++) mbits[hh] = __ballot(mbr[hh] != 0);
+                }
+            }
+            bool okc[RT];
+#pragma unroll
+            for (int i = 0; i < RT; i++) okc[i] = PAGED ? okr[i] : true;
+
+            const bool more = ts + TT < hi;
+            if (more) issue_k(ts + TT);
+
+            // scale; exclude positions past the segment, out-of-range blocks and masked ones
+#pragma unroll
+            for (int i = 0; i < RT; i++) {
+                const int pos = i * RPI + r;             // position within the tile
+                const bool in = ts + pos < hi && okc[i];
+#pragma unroll
+                for (int hh = 0; hh < G; hh++) {
+                    bool keep = in;
+                    if constexpr (MASKED) keep = keep && !((mbits[hh] >> pos) & 1);
+                    s[i][hh] = keep ? s[i][hh] * qmul : kNegInf;
+                }
+            }
+            // online softmax (log2 domain) with a lazily raised maximum
+            float mt[G];
+            bool raise = false;
+#pragma unroll
+            for (int hh = 0; hh < G; hh++) {
+                mt[hh] = s[0][hh];
+#pragma unroll
+                for (int i = 1; i < RT; i++) mt[hh] = fmaxf(mt[hh], s[i][hh]);
+                raise |= mt[hh] > m[hh] + kLazy;
+            }
+            if (__builtin_amdgcn_ballot_w64(raise)) {
+#pragma unroll
+                for (int hh = 0; hh < G; hh++) {
+                    const float mn = mt[hh] > m[hh] + kLazy ? mt[hh] : m[hh];
+                    const float alpha = __builtin_amdgcn_exp2f(m[hh] - mn);
+                    m[hh] = mn;
+                    l[hh] *= alpha;
+#pragma unroll
+                    for (int e = 0; e < 8; e++) acc[hh][e] *= alpha;
+                }
+            }
+#pragma unroll
+            for (int hh = 0; hh < G; hh++) {
+                float ls = 0.f;
+#pragma unroll
+                for (int i = 0; i < RT; i++) {
+                    s[i][hh] = __builtin_amdgcn_exp2f(s[i][hh] - m[hh]);
+                    ls += s[i][hh];
+                }
+                l[hh] += ls;
+            }
+            // P.V over pairs of row steps (two positions per dot2)
+#pragma unroll
+            for (int i = 0; i < RT; i += 2) {
+                uint32_t vp[8];     // vp[e] = {v_i[d_e], v_{i+1}[d_e]} as a 16-bit pair
+                if constexpr (I8) {
+#pragma unroll
+                    for (int w = 0; w < 2; w++) {
+                        const uint32_t a = vr[i][w] ^ 0x80808080u, bq = vr[i + 1][w] ^ 0x80808080u;
+                        const uint32_t x01 = __builtin_amdgcn_perm(bq, a, 0x05010400u);  // a0 b0 a1 b1
+                        const uint32_t x23 = __builtin_amdgcn_perm(bq, a, 0x07030602u);  // a2 b2 a3 b3
+                        vp[4 * w + 0] = i8pair_to_f16x2(__builtin_amdgcn_perm(kF16Hi, x01, 0x04010400u));
+                        vp[4 * w + 1] = i8pair_to_f16x2(__builtin_amdgcn_perm(kF16Hi, x01, 0x04030402u));
+                        vp[4 * w + 2] = i8pair_to_f16x2(__builtin_amdgcn_perm(kF16Hi, x23, 0x04010400u));
+                        vp[4 * w + 3] = i8pair_to_f16x2(__builtin_amdgcn_perm(kF16Hi, x23, 0x04030402u));
+                    }
+                } else {
+#pragma unroll
+                    for (int w = 0; w < 4; w++) {
+                        vp[2 * w] = __builtin_amdgcn_perm(vr[i + 1][w], vr[i][w], 0x05040100u);
+                        vp[2 * w + 1] = __builtin_amdgcn_perm(vr[i + 1][w], vr[i][w], 0x07060302u);
+                    }
+                }
+#pragma unroll
+                for (int hh = 0; hh < G; hh++) {
+                    const uint32_t pp = pack_p(s[i][hh], s[i + 1][hh], DotK{});
+#pragma unroll
+                    for (int e = 0; e < 8; e++) acc[hh][e] = dot2(pp, vp[e], acc[hh][e], DotK{});
+                }
+            }
+            if (!more) break;
+            issue_v(ts + TT);
+            ts += TT;
+        }
+
+        // ------------------------------------------------------ merge row groups
+#pragma unroll
+        for (int off = LPR; off < 64; off <<= 1) {
+#pragma unroll
+            for (int hh = 0; hh < G; hh++) {
+                const float mo = __shfl_xor(m[hh], off);
+                const float lo2 = __shfl_xor(l[hh], off);
+                const float mn = fmaxf(m[hh], mo);
+                const float a = __builtin_amdgcn_exp2f(m[hh] - mn), bb = __builtin_amdgcn_exp2f(mo - mn);
+                l[hh] = l[hh] * a + lo2 * bb;
+#pragma unroll
+                for (int e = 0; e < 8; e++) {
+                    const float ao = __shfl_xor(acc[hh][e], off);
+                    acc[hh][e] = acc[hh][e] * a + ao * bb;
+                }
+                m[hh] = mn;
+            }
+        }
+
+        if (r == 0) {
+#pragma unroll
+            for (int hh = 0; hh < G; hh++) {
+                if (hg * G + hh >= P.g) break;
+                const int64_t row = slot * G + hh;
+                float4 *dst = reinterpret_cast<float4 *>(P.part_acc + row * D + 8 * c);
+                dst[0] = make_float4(acc[hh][0], acc[hh][1], acc[hh][2], acc[hh][3]);
+                dst[1] = make_float4(acc[hh][4], acc[hh][5], acc[hh][6], acc[hh][7]);
+                if (c == 0) *reinterpret_cast<float2 *>(P.part_ml + row * 2) = make_float2(m[hh], l[hh]);
+            }
+        }
+        f += nseg;
+    }   // segments
+}
+
+template <int KV, int D, int G, bool PAGED, bool MASKED>
+hipError_t launch_one(const SplitParams &p, hipStream_t s) {
+    const int blocks = (p.n_pieces + kWavesPerBlock - 1) / kWavesPerBlock;
+    hipLaunchKernelGGL((split_kernel<KV, D, G, PAGED, MASKED>), dim3(blocks), dim3(64 * kWavesPerBlock), 0, s, p);
+    return hipGetLastError();
+}
+
+template <int KV, int D, int G>
+hipError_t launch_pm(const SplitParams &p, bool paged, bool masked, hipStream_t s) {
+    if (paged) return masked ? launch_one<KV, D, G, true, true>(p, s) : launch_one<KV, D, G, true, false>(p, s);
+    return masked ? launch_one<KV, D, G, false, true>(p, s) : launch_one<KV, D, G, false, false>(p, s);
+}
+
+template <int KV, int D, int G>
+const void *ptr_pm(bool paged, bool masked) {
+    void (*fp)(const SplitParams) = paged ? (masked ? split_kernel<KV, D, G, true, true>
+                                                    : split_kernel<KV, D, G, true, false>)
+                                          : (masked ? split_kernel<KV, D, G, false, true>
+                                                    : split_kernel<KV, D, G, false, false>);
+    return reinterpret_cast<const void *>(fp);
+}
+
+template <int KV, int D>
+hipError_t launch_g(const SplitParams &p, int G, bool paged, bool masked, hipStream_t s) {
+    switch (G) {
+    case 1: return launch_pm<KV, D, 1>(p, paged, masked, s);
+    case 2: return launch_pm<KV, D, 2>(p, paged, masked, s);
+    case 4: return launch_pm<KV, D, 4>(p, paged, masked, s);
+    case 8: return launch_pm<KV, D, 8>(p, paged, masked, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int KV, int D>
+const void *ptr_g(int G, bool paged, bool masked) {
+    switch (G) {
+    case 1: return ptr_pm<KV, D, 1>(paged, masked);
+    case 2: return ptr_pm<KV, D, 2>(paged, masked);
+    case 4: return ptr_pm<KV, D, 4>(paged, masked);
+    case 8: return ptr_pm<KV, D, 8>(paged, masked);
+    }
+    return nullptr;
+}
+
+}  // namespace split_detail
+
+template <int KV>
+hipError_t launch_split_kv(const SplitParams &p, int D, int G, bool paged, bool masked, hipStream_t s) {
+    using namespace split_detail;
+    switch (D) {
+    case 64: return launch_g<KV, 64>(p, G, paged, masked, s);
+    case 128: return launch_g<KV, 128>(p, G, paged, masked, s);
+    case 256: return launch_g<KV, 256>(p, G, paged, masked, s);
+    case 512: return launch_g<KV, 512>(p, G, paged, masked, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int KV>
+const void *split_kernel_ptr(int D, int G, bool paged, bool masked) {
+    using namespace split_detail;
+    switch (D) {
+    case 64: return ptr_g<KV, 64>(G, paged, masked);
+    case 128: return ptr_g<KV, 128>(G, paged, masked);
+    case 256: return ptr_g<KV, 256>(G, paged, masked);
+    case 512: return ptr_g<KV, 512>(G, paged, masked);
+    }
+    return nullptr;
+}
+
+}  // namespace ifa

@@ -13,37 +13,44 @@ constexpr int kWavesPerBlock = 4;
 
 enum KvKind { KV_F16 = 0, KV_BF16 = 1, KV_I8 = 2 };
 
-// Arguments of the split-KV decode kernel.  One wave processes one work item
-// (b, kv head j, head group hg, chunk c): the KV positions
-// [lo_b + c*chunk, min(hi_b, lo_b + (c+1)*chunk)) for query heads
-// j*g + hg*G .. j*g + hg*G + G-1.
+// Arguments of the split-KV decode kernel.
+//
+// Work is balanced exactly: the rows (b, kv head j, head group hg), each of
+// the batch's window length, are laid end to end, and wave w takes positions
+// [w*piece, (w+1)*piece) of that sequence, cut into segments at row
+// boundaries.  Each segment writes one partial softmax state (G heads) to
+// slot sbase[b] + (j*n_hg + hg)*maxseg[b] + (w - first piece of the row);
+// the combine kernel recomputes the same slots from the same tables.
 struct SplitParams {
     const void *q;          // [B, N, D] (any query layout, S = 1)
     const void *k;          // cache base
     const void *v;
-    float *part_acc;        // [chunks][N][D]  unnormalised sum p*v
-    float *part_ml;         // [chunks][N][2]  running max (log2 domain), sum p
+    float *part_acc;        // [slots][G][D]  unnormalised sum p*v
+    float *part_ml;         // [slots][G][2]  running max (log2 domain), sum p
     const uint8_t *mask;    // nullptr when absent
     const int32_t *block_table;
     const void *k_scale;    // int8 only: antiquant scale, q dtype
     int64_t sB, sN, sS;     // dense element strides of (b, j, s)
     int64_t blk_stride, head_stride, row_stride;   // paged element strides
     int64_t mask_sB, mask_sH;                      // mask strides (0 = broadcast)
+    int64_t total;          // positions over all rows of the slice
+    int64_t piece;          // positions per wave
+    int32_t n_pieces;
     int32_t N, Nkv, g, n_hg;
     int32_t max_blocks, block_size, num_blocks;
-    uint32_t bs_magic;      // s / block_size == (umulhi(s, magic) + s) >> bs_shift (or >> only)
-    int32_t bs_shift, bs_pow2;
+    uint32_t bs_magic;      // s / block_size via a round-up multiplier and shift
+    int32_t bs_shift;
     int32_t mask_mode;      // 0 none, 1 shared by the heads, 2 per head
     int32_t aq_mode;        // int8: 1 per-tensor, 2 per-channel
     int32_t q_bf16;         // int8 kernels: query dtype is bf16
     float score_mul;        // scale * log2(e)
-    int32_t chunk;          // positions per work item
     int32_t nb;             // batches in this slice
     int32_t b0;             // first batch of the slice
-    int32_t n_items;
-    int32_t lo[kSliceBatches];
-    int32_t hi[kSliceBatches];
-    int32_t cum[kSliceBatches + 1];   // chunk prefix sums
+    int64_t pre[kSliceBatches + 1];   // first flattened position of each batch's rows
+    int32_t lo[kSliceBatches];        // window start of each batch
+    int32_t len[kSliceBatches];       // window length of each batch
+    int32_t sbase[kSliceBatches];     // first partial slot of each batch
+    int32_t maxseg[kSliceBatches];    // slots reserved per row of each batch
 };
 
 // Arguments of the split-combine kernel: one wave per (b, h) row.
@@ -53,20 +60,27 @@ struct CombineParams {
     void *out;              // [B, N, D], query dtype
     const void *v_scale;    // int8: antiquant (scale, offset) of V, q dtype
     const void *v_offset;
-    int32_t N, Nkv, g, D;
+    int64_t piece;
+    int32_t N, Nkv, g, G, n_hg, D;
     int32_t out_bf16;
     int32_t aq_mode;
     int32_t nb, b0;
-    int32_t cum[kSliceBatches + 1];
+    int64_t pre[kSliceBatches + 1];
+    int32_t len[kSliceBatches];
+    int32_t sbase[kSliceBatches];
+    int32_t maxseg[kSliceBatches];
 };
 
-hipError_t launch_split(const SplitParams &p, int kv, int D, int G, bool paged, hipStream_t s);
+hipError_t launch_split(const SplitParams &p, int kv, int D, int G, bool paged, bool masked, hipStream_t s);
 hipError_t launch_combine(const CombineParams &p, hipStream_t s);
 
 // Resident waves of the split kernel for this shape (occupancy query).
-int split_resident_waves(int kv, int D, int G, bool paged);
+int split_resident_waves(int kv, int D, int G, bool paged, bool masked);
 
-// Positions one wave handles per tile (the planner keeps chunks a multiple of it).
-int split_tile_tokens(int kv, int D, int G);
+// Per-KV-dtype kernel sets (one translation unit each).
+template <int KV>
+hipError_t launch_split_kv(const SplitParams &p, int D, int G, bool paged, bool masked, hipStream_t s);
+template <int KV>
+const void *split_kernel_ptr(int D, int G, bool paged, bool masked);
 
 }  // namespace ifa

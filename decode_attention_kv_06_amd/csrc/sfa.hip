@@ -1,7 +1,10 @@
 // Host side of the sparse MLA-absorb decode path (SparseFlashAttention README:
 // parameter table and constraints).
 #include <math.h>
+#include <stdint.h>
 #include <string.h>
+
+#include <algorithm>
 
 #include "sfa.h"
 
@@ -25,7 +28,7 @@ int validate(const sfa_mla_args *a) {
     if (a->q_heads < 1 || a->q_heads > 128) return IFA_ERR_PARAM_INVALID;
     if (a->sparse_size < 1 || a->sparse_size > (1 << 24)) return IFA_ERR_PARAM_INVALID;
     if (a->block_size < 16 || a->block_size > 1024 || a->block_size % 16) return IFA_ERR_PARAM_INVALID;
-    if (a->num_blocks < 1 || a->num_blocks > (int64_t)1 << 31) return IFA_ERR_PARAM_INVALID;
+    if (a->num_blocks < 1 || a->num_blocks * a->block_size > INT32_MAX) return IFA_ERR_PARAM_INVALID;
     if (a->max_blocks < 1 || a->max_blocks * a->block_size > ((int64_t)1 << 31) - 1) return IFA_ERR_PARAM_INVALID;
     if (a->sparse_block_size != 1) return IFA_ERR_PARAM_INVALID;
     if (a->sparse_mode != 0 && a->sparse_mode != 3) return IFA_ERR_PARAM_INVALID;
@@ -35,23 +38,104 @@ int validate(const sfa_mla_args *a) {
     return IFA_OK;
 }
 
+struct SfaPlan {
+    int n_hb = 0, n_sc = 0, chunk = 0, grid = 0;
+    size_t workspace = 0;
+};
+
+// Work split: workgroups of 64 heads x one chunk of indices, about one per
+// compute unit; chunks hold at most 1024 indices and are a multiple of the
+// 32-row tile.
+int plan(const sfa_mla_args *a, SfaPlan &p) {
+    p.n_hb = (int)((a->q_heads + 63) / 64);
+    int n_sc;
+    if (a->split_hint > 0) {
+        n_sc = (int)a->split_hint;
+    } else {
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return IFA_ERR_RUNTIME;
+        const int64_t per = a->batch * p.n_hb;
+        n_sc = (int)std::max<int64_t>(1, (cus + per / 2) / per);
+    }
+    int64_t chunk = (a->sparse_size + n_sc - 1) / n_sc;
+    chunk = (chunk + 31) / 32 * 32;
+    if (chunk > 1024) chunk = 1024;
+    n_sc = (int)((a->sparse_size + chunk - 1) / chunk);
+    p.chunk = (int)chunk;
+    p.n_sc = n_sc;
+    const int64_t groups = a->batch * n_sc;
+    const int64_t grid = (groups + 7) / 8 * 8 * p.n_hb;
+    if (grid > INT32_MAX) return IFA_ERR_PARAM_INVALID;
+    p.grid = (int)grid;
+    p.workspace = 0;
+    if (n_sc > 1) {
+        const size_t rows = (size_t)a->batch * n_sc * a->q_heads;
+        p.workspace = (rows * 512 * sizeof(float) + 255) / 256 * 256 + (rows * 2 * sizeof(float) + 255) / 256 * 256;
+    }
+    return IFA_OK;
+}
+
+uint32_t magic_for(uint32_t d, int *shift) {
+    int l = 0;
+    while (((uint64_t)1 << l) < d) l++;
+    *shift = l;
+    return (uint32_t)((((uint64_t)1 << 32) * (((uint64_t)1 << l) - d)) / d + 1);
+}
+
 }  // namespace
 
 int sfa_workspace_size(const sfa_mla_args *a, size_t *bytes) {
     if (!bytes) return IFA_ERR_PARAM_NULLPTR;
     int rc = validate(a);
     if (rc) return rc;
-    *bytes = 0;
+    SfaPlan p;
+    rc = plan(a, p);
+    if (rc) return rc;
+    *bytes = p.workspace;
     return IFA_OK;
 }
 
 int sfa_run(const sfa_mla_args *a, void *ws, size_t ws_bytes, hipStream_t stream) {
-    (void)ws;
-    (void)ws_bytes;
-    (void)stream;
     int rc = validate(a);
     if (rc) return rc;
-    return IFA_ERR_PARAM_INVALID;   // kernel not built yet
+    SfaPlan pl;
+    rc = plan(a, pl);
+    if (rc) return rc;
+    if (pl.workspace && !ws) return IFA_ERR_PARAM_NULLPTR;
+    if (ws_bytes < pl.workspace) return IFA_ERR_PARAM_INVALID;
+    SfaParams p;
+    memset(&p, 0, sizeof p);
+    p.q = a->query;
+    p.q_rope = a->query_rope;
+    p.key = a->key;
+    p.key_rope = a->key_rope;
+    p.value = a->value;
+    p.idx = a->sparse_indices;
+    p.bt = a->block_table;
+    p.lkv = a->actual_seq_lengths_kv;
+    p.lq = a->actual_seq_lengths_query;
+    p.out = a->attention_out;
+    const size_t rows = (size_t)a->batch * pl.n_sc * a->q_heads;
+    p.part_acc = reinterpret_cast<float *>(ws);
+    p.part_ml = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + (rows * 512 * sizeof(float) + 255) / 256 * 256);
+    p.sparse_size = a->sparse_size;
+    p.B = (int)a->batch;
+    p.QN = (int)a->q_heads;
+    p.bs = (int)a->block_size;
+    p.max_blocks = (int)a->max_blocks;
+    p.num_blocks = (int)a->num_blocks;
+    p.bs_magic = magic_for((uint32_t)a->block_size, &p.bs_shift);
+    p.n_hb = pl.n_hb;
+    p.n_sc = pl.n_sc;
+    p.chunk = pl.chunk;
+    p.direct = pl.n_sc == 1;
+    p.score_mul = (float)((double)a->scale_value * 1.4426950408889634);
+    if (sfa_launch(p, a->dtype == IFA_DT_BF16, pl.grid, stream, reinterpret_cast<hipEvent_t>(a->profile_event_begin),
+                   reinterpret_cast<hipEvent_t>(a->profile_event_end)) != hipSuccess)
+        return IFA_ERR_RUNTIME;
+    return IFA_OK;
 }
 
 }  // namespace ifa

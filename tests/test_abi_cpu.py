@@ -75,8 +75,10 @@ def ws_size(fn, a):
 def test_dense_valid_call_sizes_workspace_without_a_device():
     rc, n = ws_size("ifa_decode_workspace_size", dense_args())
     assert rc == 0
-    # 2 batches x 64 positions / 64 per chunk = 2 chunks; each holds N rows of D + 2 floats
-    assert n == 2 * 8 * 128 * 4 + 256
+    # g = 4 -> one head group of G = 4; 2 rows (KV heads) per batch of 64 positions and
+    # pieces of 64 -> a row meets at most 2 pieces: 2 batches x 2 rows x 2 slots = 8 slots,
+    # each G x D floats of sums plus G x 2 floats of (max, sum), both rounded up to 256 B
+    assert n == 8 * 4 * 128 * 4 + 256
 
 
 LENS = (ctypes.c_int64 * 2)(10, 64)
@@ -129,9 +131,9 @@ def test_dense_null_args_and_size_pointer():
 def test_dense_left_padding_window_rules_accept():
     a = dense_args(actual_seq_lengths=ctypes.cast(LENS, ctypes.c_void_p),
                    kv_padding_size=ctypes.cast(PADS1, ctypes.c_void_p), kv_padding_size_count=1)
-    # batch 1: start = 64 - 3 - 64 < 0 -> zero row, no chunk; batch 0: [51, 61) -> 1 chunk
+    # batch 1: start = 64 - 3 - 64 < 0 -> zero row, no slots; batch 0: [51, 61) -> 2 rows x 2 slots
     rc, n = ws_size("ifa_decode_workspace_size", a)
-    assert rc == 0 and n == 1 * 8 * 128 * 4 + 256
+    assert rc == 0 and n == 4 * 4 * 128 * 4 + 256
 
 
 def test_dense_workspace_too_small_is_rejected():
@@ -162,7 +164,8 @@ def paged_args(**kw):
 def test_paged_valid_call_sizes_workspace():
     rc, n = ws_size("ifa_decode_paged_workspace_size", paged_args())
     assert rc == 0
-    assert n == (4 + 2) * 4 * 64 * 4 + 256
+    # g = 2 -> G = 2; lengths 100 and 64 with pieces of 32 -> 5 and 3 slots per row, 2 rows each
+    assert n == (2 * 5 + 2 * 3) * 2 * 64 * 4 + 256
 
 
 @pytest.mark.parametrize("kw,code", [
