@@ -44,24 +44,34 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kD = 512, kDR = 64, kDK = kD + kDR;   // value/key width, rope width, score width
 constexpr int kT = 32;                  // gathered rows per tile
-constexpr int kKP = 1168;               // LDS pitch of a K~ row: 1024 B key + 128 B rope + 16 B pad
-constexpr int kVP = 1056;               // LDS pitch of a V~ row: 1024 B + 32 B pad
-constexpr int kKReg = kT * kKP;         // 37376 B
-constexpr int kVReg = kT * kVP;         // 33792 B
-constexpr int kBuf = kKReg + kVReg;     // one tile buffer
-constexpr int kKIns = (kKReg + 1023) / 1024;   // 1 KiB DMA instructions for K~ (last one partial)
-constexpr int kVIns = kVReg / 1024;            // for V~
-constexpr int kIns = kKIns + kVIns;
+// LDS row pitch of K~ and V~ rows: 1024 B + 32 B.  With 64 four-byte banks this
+// is conflict-free both for the 16-byte A-operand reads (row = lane % 16) and
+// for the transposed 8-byte V~ reads (row = 4 (lane / 16) + (lane % 16) / 4).
+constexpr int kRP = 1056;
+constexpr int kRopeOff = kT * kRP;      // rope rows of a key slot: 32 x 128 B, columns swizzled
+constexpr int kSlot = kRopeOff + kT * 128;   // one ring slot (the key half of a tile is the larger)
 constexpr int kChunkMax = 1024;         // sparse entries per workgroup
+constexpr int kKIns = 9;                // DMA instructions per wave for a key half-tile (8 rows + rope)
+constexpr int kVIns = 8;                // ... for a value half-tile
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kMaxInit = -1.0e30f;
 constexpr float kLazy = 8.0f;           // raise the running max only past this many log2 units
 
-static_assert(kKReg % 16 == 0 && kVReg % 1024 == 0, "DMA granularity");
+static_assert(kT == 8 * kWavesPerBlock, "each wave copies 8 rows of a tile");
+static_assert(4 * kSlot + 4 * kChunkMax + 16 <= 160 * 1024, "LDS budget");
 
 __device__ __forceinline__ uint32_t div_bs(uint32_t s, uint32_t magic, int shift) {
     uint32_t t1 = __umulhi(magic, s);
     return (t1 + ((s - t1) >> 1)) >> (shift - 1);
+}
+
+// 16-byte chunk c of rope row r sits at chunk c ^ rope_swz(r) of that row, so
+// that the A-operand reads of 16 rows spread over all banks.
+__device__ __forceinline__ int rope_swz(int r) { return 2 * ((r >> 1) & 3); }
+
+// HBM -> LDS copy of 16 bytes per lane: lane l writes LDS bytes [dst + 16 l, dst + 16 l + 16).
+__device__ __forceinline__ void dma16(const void *src, char *dst) {
+    __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
 }
 
 template <bool BF>
@@ -114,14 +124,31 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// lgkmcnt(0) with the other counters left alone.  The compiler's own waits
+// before an LDS read's first use are lgkmcnt(0) whenever LDS-DMA copies are in
+// flight; waiting explicitly before issuing the next operand group keeps that
+// group's reads in flight during the current MFMAs.
+__device__ __forceinline__ void lds_wait() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Half-tile h (key rows of tile h/2 for even h, value rows for odd h) lives in
+// ring slot h % 4.  Before computing half-tile h a wave waits until only its
+// copies of halves h+1 and h+2 may still be in flight.
+__device__ __forceinline__ void wait_half(int h, int n_half) {
+    if (h + 2 < n_half) wait_vmcnt<kKIns + kVIns>();
+    else if (h + 1 < n_half) wait_vmcnt<kVIns>();     // h + 1 is then the last, a value half
+    else wait_vmcnt<0>();
+}
+
 template <bool BF>
 __global__ __launch_bounds__(256, 1) void sfa_kernel(const SfaParams P) {
     using M = Mfma<BF>;
     using vec8 = typename M::vec8;
-    // two tile buffers as distinct objects, so the compiler can tell a read of
-    // one from the copies in flight into the other
-    __shared__ __attribute__((aligned(16))) char s_buf0[kBuf];
-    __shared__ __attribute__((aligned(16))) char s_buf1[kBuf];
+    // the four ring slots as distinct objects, so the compiler can tell a read
+    // of one from the copies in flight into another
+    __shared__ __attribute__((aligned(16))) char s_slot0[kSlot];
+    __shared__ __attribute__((aligned(16))) char s_slot1[kSlot];
+    __shared__ __attribute__((aligned(16))) char s_slot2[kSlot];
+    __shared__ __attribute__((aligned(16))) char s_slot3[kSlot];
     __shared__ int32_t s_rows[kChunkMax];
     __shared__ int32_t s_cnt[kWavesPerBlock];
 
@@ -176,6 +203,7 @@ __global__ __launch_bounds__(256, 1) void sfa_kernel(const SfaParams P) {
     // ---------------------------------------------------- this wave's 16 heads
     const int h = hb * 64 + wave * 16 + l16;          // head of lanes l16 (score layout)
     const bool h_ok = h < P.QN;
+    const bool wave_active = hb * 64 + wave * 16 < P.QN;   // wave-uniform
     vec8 qreg[kDK / 32];
 #pragma unroll
     for (int ks = 0; ks < kDK / 32; ks++) {
@@ -189,41 +217,33 @@ __global__ __launch_bounds__(256, 1) void sfa_kernel(const SfaParams P) {
         qreg[ks] = __builtin_bit_cast(vec8, x);
     }
 
-    // ---------------------------------------------------- gather tiles into LDS
+    // ---------------------------------------------------- gather copies
+    // Wave w copies tile rows 8w .. 8w+7: one 1 KiB instruction per key row and
+    // per value row (the row base is wave-uniform) and one instruction for the
+    // eight rope rows (lane l: row 8w + l/8, 16-byte chunk l%8).  `rows` holds,
+    // in lane l, the physical row of tile row 8w + l/8.
     const char *keyb = reinterpret_cast<const char *>(P.key);
     const char *ropeb = reinterpret_cast<const char *>(P.key_rope);
     const char *valb = reinterpret_cast<const char *>(P.value);
     const int n_tiles = (nv + kT - 1) / kT;
-    // Every wave issues the DMA instructions ins = wave, wave + 4, ...; each
-    // instruction fills 1 KiB of the buffer, lane l bytes [16 l, 16 l + 16).
-    constexpr int kInsW0 = (kIns + kWavesPerBlock - 1) / kWavesPerBlock;   // waves 0..(kIns % 4 - 1)
-    auto issue_tile = [&](int tile, char *bufp) {
-        char *kreg = bufp;
-        char *vreg = kreg + kKReg;
-        const int rbase = tile * kT;
-        for (int ins = wave; ins < kIns; ins += kWavesPerBlock) {
-            const char *src;
-            char *dst;
-            bool on = true;
-            if (ins < kKIns) {
-                const int o = ins * 1024 + lane * 16;
-                on = o < kKReg;
-                const int rr = min(o / kKP, kT - 1), col = o - rr * kKP;
-                const int r = rbase + rr;
-                const int64_t row = s_rows[r < nv ? r : 0];
-                src = col < 1024 ? keyb + row * 1024 + col
-                    : col < 1152 ? ropeb + row * 128 + (col - 1024) : keyb + row * 1024;
-                dst = kreg + ins * 1024;
-            } else {
-                const int o = (ins - kKIns) * 1024 + lane * 16;
-                const int rr = o / kVP, col = o - rr * kVP;
-                const int r = rbase + rr;
-                const int64_t row = s_rows[r < nv ? r : 0];
-                src = col < 1024 ? valb + row * 1024 + col : valb + row * 1024;
-                dst = vreg + (ins - kKIns) * 1024;
-            }
-            if (on)
-                __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(src), dst, 16, 0, 0);
+    const int n_half = 2 * n_tiles;
+    auto rows_of = [&](int tile) -> int {
+        return s_rows[min(tile * kT + 8 * wave + (lane >> 3), nv - 1)];
+    };
+    auto issue_k = [&](char *slot, int rows) {
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const int64_t row = __builtin_amdgcn_readlane(rows, 8 * j);
+            dma16(keyb + row * 1024 + lane * 16, slot + (8 * wave + j) * kRP);
+        }
+        const int r = 8 * wave + (lane >> 3);
+        dma16(ropeb + (int64_t)rows * 128 + 16 * ((lane & 7) ^ rope_swz(r)), slot + kRopeOff + wave * 1024);
+    };
+    auto issue_v = [&](char *slot, int rows) {
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const int64_t row = __builtin_amdgcn_readlane(rows, 8 * j);
+            dma16(valb + row * 1024 + lane * 16, slot + (8 * wave + j) * kRP);
         }
     };
 
@@ -232,36 +252,45 @@ __global__ __launch_bounds__(256, 1) void sfa_kernel(const SfaParams P) {
     for (int nb = 0; nb < kD / 16; nb++) acc[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
     float m_run = kMaxInit, l_run = 0.f;    // per head l16 (lanes of one head agree on m_run)
     const float smul = P.score_mul;
+    vec8 pa;                                // P of the current tile, A operand of P.V
 
-    // one tile: wait for its copies, issue the next tile's copies into the
-    // other buffer, compute
-    auto step = [&](int tile, const char *cur, char *nxt) {
-        if (tile + 1 < n_tiles) {
-            issue_tile(tile + 1, nxt);
-            // this wave's copies of the current tile are complete once at most
-            // the next tile's copies are outstanding
-            if (wave < kIns % kWavesPerBlock || kIns % kWavesPerBlock == 0) wait_vmcnt<kInsW0>();
-            else wait_vmcnt<kInsW0 - 1>();
-        } else {
-            wait_vmcnt<0>();
-        }
-        // Every wave's copies of this tile have landed.  A bare s_barrier (no
-        // fence) keeps the next tile's copies in flight across it.
-        __builtin_amdgcn_s_barrier();
-        const char *kreg = cur;
-        const char *vreg = kreg + kKReg;
-        // S^T for the two 16-row blocks of the tile
-        floatx4 sc2[2];
+    // scores of tile `tile` from its key slot, then the online-softmax update
+    auto qk = [&](int tile, const char *ks_) {
+        // 36 products: step i takes row block i % 2 and k-step i / 2, so the
+        // two accumulation chains interleave.
+        constexpr int kSteps = 2 * (kDK / 32);
+        auto a_ptr = [&](int i) -> const char * {
+            const int tb = i & 1, ks = i >> 1;
+            const int r = tb * 16 + l16;
+            if (ks < kD / 32) return ks_ + r * kRP + 64 * ks + 16 * g;
+            return ks_ + kRopeOff + r * 128 + 16 * ((4 * (ks - kD / 32) + g) ^ rope_swz(r));
+        };
+        floatx4 sc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        // groups of kGrp steps: the reads of group j + 1 are issued before the
+        // MFMAs of group j (the scheduling fences keep that order)
+        constexpr int kGrp = 6, kGroups = kSteps / kGrp;
+        static_assert(kSteps % kGrp == 0, "group size");
+        vec8 abuf[2][kGrp];
 #pragma unroll
-        for (int tb = 0; tb < 2; tb++) {
-            floatx4 cacc = {0.f, 0.f, 0.f, 0.f};
-            const char *arow = kreg + (tb * 16 + l16) * kKP + 16 * g;
+        for (int i = 0; i < kGrp; i++) abuf[0][i] = *reinterpret_cast<const vec8 *>(a_ptr(i));
 #pragma unroll
-            for (int ks = 0; ks < kDK / 32; ks++) {
-                const vec8 a = *reinterpret_cast<const vec8 *>(arow + 64 * ks);
-                cacc = M::run(a, qreg[ks], cacc);
+        for (int j = 0; j < kGroups; j++) {
+            // operands of group j have arrived; only then issue group j + 1, so
+            // that its reads stay in flight during the MFMAs of group j
+            lds_wait();
+            __builtin_amdgcn_sched_barrier(0);
+            if (j + 1 < kGroups) {
+#pragma unroll
+                for (int i = 0; i < kGrp; i++)
+                    abuf[(j + 1) & 1][i] = *reinterpret_cast<const vec8 *>(a_ptr((j + 1) * kGrp + i));
             }
-            sc2[tb] = cacc;
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < kGrp; i++) {
+                const int st = j * kGrp + i;
+                sc2[st & 1] = M::run(abuf[j & 1][i], qreg[st >> 1], sc2[st & 1]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
         // scale, exclude rows past the valid count
         float p[8];
@@ -298,28 +327,89 @@ __global__ __launch_bounds__(256, 1) void sfa_kernel(const SfaParams P) {
             p[i] = __builtin_amdgcn_exp2f(p[i] - m_run);
             l_run += p[i];
         }
-        const vec8 pa = M::pack(p);
-
-        // O[h][d] += P[h][t] V~[t][d]: B operand read transposed from LDS
-        // (lane j of a 16-lane group points at row 4g + j/4, columns 4(j%4)..+3
-        // of the 16-column block; the second read covers rows 16 + 4g + j/4)
-        const char *v0 = vreg + (4 * g + (l16 >> 2)) * kVP + 8 * (l16 & 3);
-        const char *v1 = v0 + 16 * kVP;
-#pragma unroll
-        for (int nb = 0; nb < kD / 16; nb++) {
-            const vec8 bv = M::tr2(v0 + 32 * nb, v1 + 32 * nb);
-            acc[nb] = M::run(pa, bv, acc[nb]);
-        }
-        // all LDS reads of this buffer are done (their results fed the MFMAs
-        // above) before any wave starts the copy two tiles ahead into it
-        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), vmcnt/expcnt untouched
-        __builtin_amdgcn_s_barrier();
+        pa = M::pack(p);
     };
-    if (n_tiles > 0) issue_tile(0, s_buf0);
-    for (int tile = 0; tile < n_tiles; tile += 2) {
-        step(tile, s_buf0, s_buf1);
-        if (tile + 1 < n_tiles) step(tile + 1, s_buf1, s_buf0);
+    // O[h][d] += P[h][t] V~[t][d]: B operand read transposed from LDS
+    // (lane j of a 16-lane group points at row 4g + j/4, columns 4(j%4)..+3
+    // of the 16-column block; the second read covers rows 16 + 4g + j/4)
+    auto pv = [&](const char *vs_) {
+        constexpr int kNb = kD / 16, kPfV = 4;
+        const char *v0 = vs_ + (4 * g + (l16 >> 2)) * kRP + 8 * (l16 & 3);
+        const char *v1 = v0 + 16 * kRP;
+        // groups of kPfV column blocks: the reads of group j + 1 are issued
+        // before the MFMAs of group j
+        constexpr int kGroups = kNb / kPfV;
+        vec8 bbuf[2][kPfV];
+#pragma unroll
+        for (int i = 0; i < kPfV; i++) bbuf[0][i] = M::tr2(v0 + 32 * i, v1 + 32 * i);
+#pragma unroll
+        for (int j = 0; j < kGroups; j++) {
+            lds_wait();
+            __builtin_amdgcn_sched_barrier(0);
+            if (j + 1 < kGroups) {
+#pragma unroll
+                for (int i = 0; i < kPfV; i++) {
+                    const int nb = (j + 1) * kPfV + i;
+                    bbuf[(j + 1) & 1][i] = M::tr2(v0 + 32 * nb, v1 + 32 * nb);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < kPfV; i++) acc[j * kPfV + i] = M::run(pa, bbuf[j & 1][i], acc[j * kPfV + i]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    // End of a half step: this wave's LDS reads of the slot have returned
+    // (their results fed the MFMAs) before any wave may overwrite it.
+    auto end_half = [&]() { lds_wait(); };
+
+    // ---------------------------------------------------- pipeline
+    // Half-tiles h = 0, 1, 2 are issued up front; step h waits for half h,
+    // synchronises the workgroup (every wave's copies of half h have landed and
+    // every wave is done with half h - 1, whose slot half h + 3 reuses),
+    // issues half h + 3 and computes half h.  `rows_n` holds the rows of the
+    // next tile whose halves are still to be issued.
+    int rows_n = 0;
+    if (n_tiles > 0) {
+        rows_n = rows_of(0);
+        issue_k(s_slot0, rows_n);
+        issue_v(s_slot1, rows_n);
+        if (n_tiles > 1) {
+            rows_n = rows_of(1);
+            issue_k(s_slot2, rows_n);
+        }
     }
+    // two tiles (four half steps, one per slot) per iteration
+    for (int t = 0; t < n_tiles; t += 2) {
+        // h = 2t: scores of tile t (slot 0); issue V(t+1) into slot 3
+        wait_half(2 * t, n_half);
+        __builtin_amdgcn_s_barrier();
+        if (t + 1 < n_tiles) issue_v(s_slot3, rows_n);
+        if (t + 2 < n_tiles) rows_n = rows_of(t + 2);
+        if (wave_active) qk(t, s_slot0);
+        end_half();
+        // h = 2t+1: P.V of tile t (slot 1); issue K(t+2) into slot 0
+        wait_half(2 * t + 1, n_half);
+        __builtin_amdgcn_s_barrier();
+        if (t + 2 < n_tiles) issue_k(s_slot0, rows_n);
+        if (wave_active) pv(s_slot1);
+        end_half();
+        if (t + 1 >= n_tiles) break;
+        // h = 2t+2: scores of tile t+1 (slot 2); issue V(t+2) into slot 1
+        wait_half(2 * t + 2, n_half);
+        __builtin_amdgcn_s_barrier();
+        if (t + 2 < n_tiles) issue_v(s_slot1, rows_n);
+        if (t + 3 < n_tiles) rows_n = rows_of(t + 3);
+        if (wave_active) qk(t + 1, s_slot2);
+        end_half();
+        // h = 2t+3: P.V of tile t+1 (slot 3); issue K(t+3) into slot 2
+        wait_half(2 * t + 3, n_half);
+        __builtin_amdgcn_s_barrier();
+        if (t + 3 < n_tiles) issue_k(s_slot2, rows_n);
+        if (wave_active) pv(s_slot3);
+        end_half();
+    }
+    if (!wave_active) return;
 
     // ---------------------------------------------------- epilogue
     // l of head l16 summed over the four lane groups (m_run already agrees)
