@@ -6,6 +6,9 @@
 
 namespace ifa {
 
+// Sparse entries handled by one workgroup at most (the kernel's LDS row table).
+constexpr int kSfaChunkMax = 512;
+
 // Arguments of the gather + MFMA kernel and its chunk combine.
 struct SfaParams {
     const void *q, *q_rope, *key, *key_rope, *value;

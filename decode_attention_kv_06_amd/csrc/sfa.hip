@@ -44,8 +44,8 @@ struct SfaPlan {
 };
 
 // Work split: workgroups of 64 heads x one chunk of indices, about one per
-// compute unit; chunks hold at most 1024 indices and are a multiple of the
-// 32-row tile.
+// compute unit; chunks hold at most kSfaChunkMax indices and are a multiple
+// of the 32-row tile.
 int plan(const sfa_mla_args *a, SfaPlan &p) {
     p.n_hb = (int)((a->q_heads + 63) / 64);
     int n_sc;
@@ -61,7 +61,7 @@ int plan(const sfa_mla_args *a, SfaPlan &p) {
     }
     int64_t chunk = (a->sparse_size + n_sc - 1) / n_sc;
     chunk = (chunk + 31) / 32 * 32;
-    if (chunk > 1024) chunk = 1024;
+    if (chunk > kSfaChunkMax) chunk = kSfaChunkMax;
     n_sc = (int)((a->sparse_size + chunk - 1) / chunk);
     p.chunk = (int)chunk;
     p.n_sc = n_sc;

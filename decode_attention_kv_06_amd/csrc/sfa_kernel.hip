@@ -50,7 +50,7 @@ constexpr int kT = 32;                  // gathered rows per tile
 constexpr int kRP = 1056;
 constexpr int kRopeOff = kT * kRP;      // rope rows of a key slot: 32 x 128 B, columns swizzled
 constexpr int kSlot = kRopeOff + kT * 128;   // one ring slot (the key half of a tile is the larger)
-constexpr int kChunkMax = 1024;         // sparse entries per workgroup
+constexpr int kChunkMax = kSfaChunkMax;   // sparse entries per workgroup (a multiple of 256)
 constexpr int kKIns = 9;                // DMA instructions per wave for a key half-tile (8 rows + rope)
 constexpr int kVIns = 8;                // ... for a value half-tile
 constexpr float kNegInf = -__builtin_huge_valf();
@@ -58,7 +58,8 @@ constexpr float kMaxInit = -1.0e30f;
 constexpr float kLazy = 8.0f;           // raise the running max only past this many log2 units
 
 static_assert(kT == 8 * kWavesPerBlock, "each wave copies 8 rows of a tile");
-static_assert(4 * kSlot + 4 * kChunkMax + 16 <= 160 * 1024, "LDS budget");
+static_assert(4 * kSlot + kWavesPerBlock * 64 * 16 + 4 * kChunkMax + 4 * 64 * 2 + 4 * 4 * 3 <= 160 * 1024, "LDS budget");
+static_assert(kChunkMax % 256 == 0, "two entries per thread");
 
 __device__ __forceinline__ uint32_t div_bs(uint32_t s, uint32_t magic, int shift) {
     uint32_t t1 = __umulhi(magic, s);
@@ -69,9 +70,19 @@ __device__ __forceinline__ uint32_t div_bs(uint32_t s, uint32_t magic, int shift
 // that the A-operand reads of 16 rows spread over all banks.
 __device__ __forceinline__ int rope_swz(int r) { return 2 * ((r >> 1) & 3); }
 
-// HBM -> LDS copy of 16 bytes per lane: lane l writes LDS bytes [dst + 16 l, dst + 16 l + 16).
+// HBM -> LDS copy of 16 bytes per lane: lane l writes LDS bytes
+// [dst + 16 l, dst + 16 l + 16); dst is wave-uniform.  Issued as assembly, so
+// the compiler neither tracks nor waits for these copies: every wait on them
+// is an explicit vmcnt below.  (The compiler's own tracking of LDS-DMA stores
+// loses the slot a read belongs to across the ring loop and then drains all
+// copies in flight.)  M0 takes the LDS address; one wait state separates its
+// write from the copy that reads it.
 __device__ __forceinline__ void dma16(const void *src, char *dst) {
-    __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+    const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)dst;
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(lds)
+                 : "memory", "m0");
 }
 
 template <bool BF>
@@ -124,6 +135,15 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// Workgroup barrier without a memory fence (the copies in flight must stay in
+// flight across it).  The empty assembly statements keep the compiler from
+// moving LDS accesses across the barrier.
+__device__ __forceinline__ void ring_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // lgkmcnt(0) with the other counters left alone.  The compiler's own waits
 // before an LDS read's first use are lgkmcnt(0) whenever LDS-DMA copies are in
 // flight; waiting explicitly before issuing the next operand group keeps that
@@ -132,12 +152,9 @@ __device__ __forceinline__ void lds_wait() { __builtin_amdgcn_s_waitcnt(0xC07F);
 
 // Half-tile h (key rows of tile h/2 for even h, value rows for odd h) lives in
 // ring slot h % 4.  Before computing half-tile h a wave waits until only its
-// copies of halves h+1 and h+2 may still be in flight.
-__device__ __forceinline__ void wait_half(int h, int n_half) {
-    if (h + 2 < n_half) wait_vmcnt<kKIns + kVIns>();
-    else if (h + 1 < n_half) wait_vmcnt<kVIns>();     // h + 1 is then the last, a value half
-    else wait_vmcnt<0>();
-}
+// copies of halves h+1 and h+2 may still be in flight.  Halves past the last
+// tile are still copied (the last valid row again, never read), so that count
+// is the same at every step.
 
 template <bool BF>
 __global__ __launch_bounds__(256, 1) void sfa_kernel(const SfaParams P) {
@@ -149,8 +166,12 @@ __global__ __launch_bounds__(256, 1) void sfa_kernel(const SfaParams P) {
     __shared__ __attribute__((aligned(16))) char s_slot1[kSlot];
     __shared__ __attribute__((aligned(16))) char s_slot2[kSlot];
     __shared__ __attribute__((aligned(16))) char s_slot3[kSlot];
+    __shared__ __attribute__((aligned(16))) char s_p[kWavesPerBlock * 64 * 16];   // P of each head group
     __shared__ int32_t s_rows[kChunkMax];
-    __shared__ int32_t s_cnt[kWavesPerBlock];
+    __shared__ float s_alpha[64];           // rescale factor of each head for the current tile
+    __shared__ float s_linv[64];            // 1 / l of each head (single-chunk output)
+    __shared__ __attribute__((aligned(16))) int32_t s_flag[kWavesPerBlock];   // group raised its running max this tile
+    __shared__ int32_t s_cnt[2][kWavesPerBlock];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -164,46 +185,17 @@ __global__ __launch_bounds__(256, 1) void sfa_kernel(const SfaParams P) {
     if (grp >= P.B * P.n_sc) return;               // whole workgroup leaves together
     const int b = grp / P.n_sc, sc = grp - b * P.n_sc;
 
-    // ---------------------------------------------------- compact the chunk's valid rows
-    const int64_t e_begin = (int64_t)sc * P.chunk;
-    const int n_entries = (int)min((int64_t)P.chunk, P.sparse_size - e_begin);
-    const int Lkv = P.lkv[b];
-    const bool q_present = P.lq == nullptr || P.lq[b] > 0;
-    const int32_t *ind = P.idx + (int64_t)b * P.sparse_size + e_begin;
-    const int32_t *btab = P.bt + (int64_t)b * P.max_blocks;
-    int nv = 0;
-    for (int base = 0; base < n_entries; base += 256) {
-        const int e = base + tid;
-        bool valid = false;
-        int32_t row = 0;
-        if (e < n_entries && q_present) {
-            const int t = ind[e];
-            if (t >= 0 && t < Lkv) {
-                const uint32_t qb = div_bs((uint32_t)t, P.bs_magic, P.bs_shift);
-                // the kv length is device data: an index past the block table is left out
-                const int blk = qb < (uint32_t)P.max_blocks ? btab[qb] : -1;
-                if (blk >= 0 && blk < P.num_blocks) {
-                    valid = true;
-                    row = blk * P.bs + (t - (int)qb * P.bs);
-                }
-            }
-        }
-        const uint64_t bal = __ballot(valid);
-        const int before = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
-        if (lane == 0) s_cnt[wave] = __popcll(bal);
-        __syncthreads();
-        int off = nv;
-        for (int w = 0; w < wave; w++) off += s_cnt[w];
-        if (valid) s_rows[off + before] = row;
-        for (int w = 0; w < kWavesPerBlock; w++) nv += s_cnt[w];
-        __syncthreads();
-    }
-    nv = __builtin_amdgcn_readfirstlane(nv);
+    // Head groups of 16: wave w computes the scores of group w; every wave
+    // accumulates P.V for all four groups over its own 128 output columns.  A
+    // group past the head count keeps P = 0 and is never stored.
+    const int n_act = min(kWavesPerBlock, (P.QN - hb * 64 + 15) / 16);   // >= 1
+    const bool qk_wave = wave < n_act;
+    if (!qk_wave) *reinterpret_cast<u32x4 *>(s_p + (wave * 64 + lane) * 16) = u32x4{0, 0, 0, 0};
+    if (lane == 0) s_flag[wave] = 0;
 
-    // ---------------------------------------------------- this wave's 16 heads
+    // ---------------------------------------------------- query rows (issued first)
     const int h = hb * 64 + wave * 16 + l16;          // head of lanes l16 (score layout)
     const bool h_ok = h < P.QN;
-    const bool wave_active = hb * 64 + wave * 16 < P.QN;   // wave-uniform
     vec8 qreg[kDK / 32];
 #pragma unroll
     for (int ks = 0; ks < kDK / 32; ks++) {
@@ -217,6 +209,52 @@ __global__ __launch_bounds__(256, 1) void sfa_kernel(const SfaParams P) {
         qreg[ks] = __builtin_bit_cast(vec8, x);
     }
 
+    // ---------------------------------------------------- compact the chunk's valid rows
+    // Entry e = 256 k + tid (k = 0, 1); all index loads, then all block-table
+    // loads, are issued together.  Valid entries keep their order.
+    const int64_t e_begin = (int64_t)sc * P.chunk;
+    const int n_entries = (int)min((int64_t)P.chunk, P.sparse_size - e_begin);
+    const int Lkv = P.lkv[b];
+    const bool q_present = P.lq == nullptr || P.lq[b] > 0;
+    const int32_t *ind = P.idx + (int64_t)b * P.sparse_size + e_begin;
+    const int32_t *btab = P.bt + (int64_t)b * P.max_blocks;
+    constexpr int kPer = kChunkMax / 256;
+    int tv[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; k++) {
+        const int e = 256 * k + tid;
+        tv[k] = (e < n_entries && q_present) ? ind[e] : -1;
+    }
+    uint32_t qbv[kPer];
+    int blk[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; k++) {
+        qbv[k] = div_bs((uint32_t)max(tv[k], 0), P.bs_magic, P.bs_shift);
+        // the kv length is device data: an index past the block table is left out
+        const bool look = tv[k] >= 0 && tv[k] < Lkv && qbv[k] < (uint32_t)P.max_blocks;
+        blk[k] = look ? btab[qbv[k]] : -1;
+    }
+    bool valid[kPer];
+    int before[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; k++) {
+        valid[k] = blk[k] >= 0 && blk[k] < P.num_blocks;
+        const uint64_t bal = __ballot(valid[k]);
+        before[k] = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+        if (lane == 0) s_cnt[k][wave] = __popcll(bal);
+    }
+    __syncthreads();
+    int nv = 0;
+#pragma unroll
+    for (int k = 0; k < kPer; k++) {
+        int off = nv;
+        for (int w = 0; w < wave; w++) off += s_cnt[k][w];
+        if (valid[k]) s_rows[off + before[k]] = blk[k] * P.bs + (tv[k] - (int)qbv[k] * P.bs);
+        for (int w = 0; w < kWavesPerBlock; w++) nv += s_cnt[k][w];
+    }
+    __syncthreads();
+    nv = __builtin_amdgcn_readfirstlane(nv);
+
     // ---------------------------------------------------- gather copies
     // Wave w copies tile rows 8w .. 8w+7: one 1 KiB instruction per key row and
     // per value row (the row base is wave-uniform) and one instruction for the
@@ -227,7 +265,7 @@ __global__ __launch_bounds__(256, 1) void sfa_kernel(const SfaParams P) {
     const char *valb = reinterpret_cast<const char *>(P.value);
     const int n_tiles = (nv + kT - 1) / kT;
     const int n_half = 2 * n_tiles;
-    auto rows_of = [&](int tile) -> int {
+    auto rows_of = [&](int tile) -> int {      // tiles past the last repeat its last row
         return s_rows[min(tile * kT + 8 * wave + (lane >> 3), nv - 1)];
     };
     auto issue_k = [&](char *slot, int rows) {
@@ -247,14 +285,19 @@ __global__ __launch_bounds__(256, 1) void sfa_kernel(const SfaParams P) {
         }
     };
 
-    floatx4 acc[kD / 16];
+    // acc[hg][j]: heads 16 hg + 4g + i (i = 0..3) of the block, output column
+    // 128 wave + 16 j + l16
+    floatx4 acc[kWavesPerBlock][8];
 #pragma unroll
-    for (int nb = 0; nb < kD / 16; nb++) acc[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
-    float m_run = kMaxInit, l_run = 0.f;    // per head l16 (lanes of one head agree on m_run)
+    for (int hg = 0; hg < kWavesPerBlock; hg++)
+#pragma unroll
+        for (int j = 0; j < 8; j++) acc[hg][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    float m_run = kMaxInit, l_run = 0.f;    // head l16 of group `wave` (lanes of one head agree on m_run)
     const float smul = P.score_mul;
-    vec8 pa;                                // P of the current tile, A operand of P.V
 
-    // scores of tile `tile` from its key slot, then the online-softmax update
+    // scores of tile `tile` for head group `wave` from its key slot, the
+    // online-softmax update, and P (A-operand layout) and the rescale factors
+    // published in LDS
     auto qk = [&](int tile, const char *ks_) {
         // 36 products: step i takes row block i % 2 and k-step i / 2, so the
         // two accumulation chains interleave.
@@ -307,141 +350,158 @@ __global__ __launch_bounds__(256, 1) void sfa_kernel(const SfaParams P) {
         mt = fmaxf(mt, __shfl_xor(mt, 16));
         mt = fmaxf(mt, __shfl_xor(mt, 32));
         const bool raise = mt > m_run + kLazy;
+        float alpha = 1.f;
+        int flag = 0;
         if (__builtin_amdgcn_ballot_w64(raise)) {
             const float mn = raise ? mt : m_run;
-            const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+            alpha = __builtin_amdgcn_exp2f(m_run - mn);
+            // nothing has been accumulated before the first tile
+            flag = tile > 0;
             m_run = mn;
             l_run *= alpha;
-            // the accumulator rows of this lane are heads 4g + i; their alpha
-            // lives in lanes 4g + i (score layout: head = lane % 16)
-            float ai[4];
-#pragma unroll
-            for (int i = 0; i < 4; i++) ai[i] = __shfl(alpha, 4 * g + i);
-#pragma unroll
-            for (int nb = 0; nb < kD / 16; nb++)
-#pragma unroll
-                for (int i = 0; i < 4; i++) acc[nb][i] *= ai[i];
         }
 #pragma unroll
         for (int i = 0; i < 8; i++) {
             p[i] = __builtin_amdgcn_exp2f(p[i] - m_run);
             l_run += p[i];
         }
-        pa = M::pack(p);
+        *reinterpret_cast<vec8 *>(s_p + (wave * 64 + lane) * 16) = M::pack(p);
+        if (g == 0) s_alpha[wave * 16 + l16] = alpha;
+        if (lane == 0) s_flag[wave] = flag;
     };
-    // O[h][d] += P[h][t] V~[t][d]: B operand read transposed from LDS
-    // (lane j of a 16-lane group points at row 4g + j/4, columns 4(j%4)..+3
-    // of the 16-column block; the second read covers rows 16 + 4g + j/4)
+    // O[h][d] += P[h][t] V~[t][d] over this wave's 128 columns and every active
+    // head group.  The V~ operand is read transposed from LDS (lane j of a
+    // 16-lane group points at row 4g + j/4, columns 4(j%4)..+3 of the 16-column
+    // block; the second read covers rows 16 + 4g + j/4) and serves all groups.
     auto pv = [&](const char *vs_) {
-        constexpr int kNb = kD / 16, kPfV = 4;
-        const char *v0 = vs_ + (4 * g + (l16 >> 2)) * kRP + 8 * (l16 & 3);
+        const u32x4 fl = *reinterpret_cast<const u32x4 *>(s_flag);
+        vec8 pa[kWavesPerBlock];
+#pragma unroll
+        for (int hg = 0; hg < kWavesPerBlock; hg++) pa[hg] = *reinterpret_cast<const vec8 *>(s_p + (hg * 64 + lane) * 16);
+        const char *v0 = vs_ + (4 * g + (l16 >> 2)) * kRP + 8 * (l16 & 3) + 256 * wave;
         const char *v1 = v0 + 16 * kRP;
-        // groups of kPfV column blocks: the reads of group j + 1 are issued
-        // before the MFMAs of group j
-        constexpr int kGroups = kNb / kPfV;
+        constexpr int kPfV = 2, kGroups = 8 / kPfV;
         vec8 bbuf[2][kPfV];
 #pragma unroll
         for (int i = 0; i < kPfV; i++) bbuf[0][i] = M::tr2(v0 + 32 * i, v1 + 32 * i);
+        // a raised running max rescales what the group accumulated so far
+        if (fl[0] | fl[1] | fl[2] | fl[3]) {
 #pragma unroll
-        for (int j = 0; j < kGroups; j++) {
+            for (int hg = 0; hg < kWavesPerBlock; hg++) {
+                if (!fl[hg]) continue;
+                float ai[4];
+#pragma unroll
+                for (int i = 0; i < 4; i++) ai[i] = s_alpha[hg * 16 + 4 * g + i];
+#pragma unroll
+                for (int j = 0; j < 8; j++)
+#pragma unroll
+                    for (int i = 0; i < 4; i++) acc[hg][j][i] *= ai[i];
+            }
+        }
+#pragma unroll
+        for (int jg = 0; jg < kGroups; jg++) {
             lds_wait();
             __builtin_amdgcn_sched_barrier(0);
-            if (j + 1 < kGroups) {
+            if (jg + 1 < kGroups) {
 #pragma unroll
                 for (int i = 0; i < kPfV; i++) {
-                    const int nb = (j + 1) * kPfV + i;
-                    bbuf[(j + 1) & 1][i] = M::tr2(v0 + 32 * nb, v1 + 32 * nb);
+                    const int j = (jg + 1) * kPfV + i;
+                    bbuf[(jg + 1) & 1][i] = M::tr2(v0 + 32 * j, v1 + 32 * j);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int i = 0; i < kPfV; i++) acc[j * kPfV + i] = M::run(pa, bbuf[j & 1][i], acc[j * kPfV + i]);
+            for (int i = 0; i < kPfV; i++)
+#pragma unroll
+                for (int hg = 0; hg < kWavesPerBlock; hg++)
+                    acc[hg][jg * kPfV + i] = M::run(pa[hg], bbuf[jg & 1][i], acc[hg][jg * kPfV + i]);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    // End of a half step: this wave's LDS reads of the slot have returned
-    // (their results fed the MFMAs) before any wave may overwrite it.
+    // End of a half step: this wave's LDS reads of the slot have returned and
+    // its LDS writes are done before any wave may overwrite or read them.
     auto end_half = [&]() { lds_wait(); };
 
     // ---------------------------------------------------- pipeline
     // Half-tiles h = 0, 1, 2 are issued up front; step h waits for half h,
-    // synchronises the workgroup (every wave's copies of half h have landed and
-    // every wave is done with half h - 1, whose slot half h + 3 reuses),
-    // issues half h + 3 and computes half h.  `rows_n` holds the rows of the
-    // next tile whose halves are still to be issued.
+    // synchronises the workgroup (every wave's copies of half h have landed,
+    // every wave is done with half h - 1, whose slot half h + 3 reuses, and P
+    // of the tile is visible), issues half h + 3 and computes half h.
+    // `rows_n` holds the rows of the next tile whose halves are still to be
+    // issued.
+    // The compiler's own vector-memory loads (query, indices, block table) are
+    // consumed by now; the copies below are the only ones in flight from here.
     int rows_n = 0;
     if (n_tiles > 0) {
         rows_n = rows_of(0);
         issue_k(s_slot0, rows_n);
         issue_v(s_slot1, rows_n);
-        if (n_tiles > 1) {
-            rows_n = rows_of(1);
-            issue_k(s_slot2, rows_n);
-        }
+        rows_n = rows_of(1);
+        issue_k(s_slot2, rows_n);
     }
     // two tiles (four half steps, one per slot) per iteration
     for (int t = 0; t < n_tiles; t += 2) {
         // h = 2t: scores of tile t (slot 0); issue V(t+1) into slot 3
-        wait_half(2 * t, n_half);
-        __builtin_amdgcn_s_barrier();
-        if (t + 1 < n_tiles) issue_v(s_slot3, rows_n);
-        if (t + 2 < n_tiles) rows_n = rows_of(t + 2);
-        if (wave_active) qk(t, s_slot0);
+        wait_vmcnt<kKIns + kVIns>();
+        ring_barrier();
+        issue_v(s_slot3, rows_n);
+        rows_n = rows_of(t + 2);
+        if (qk_wave) qk(t, s_slot0);
         end_half();
         // h = 2t+1: P.V of tile t (slot 1); issue K(t+2) into slot 0
-        wait_half(2 * t + 1, n_half);
-        __builtin_amdgcn_s_barrier();
-        if (t + 2 < n_tiles) issue_k(s_slot0, rows_n);
-        if (wave_active) pv(s_slot1);
+        wait_vmcnt<kKIns + kVIns>();
+        ring_barrier();
+        issue_k(s_slot0, rows_n);
+        pv(s_slot1);
         end_half();
         if (t + 1 >= n_tiles) break;
         // h = 2t+2: scores of tile t+1 (slot 2); issue V(t+2) into slot 1
-        wait_half(2 * t + 2, n_half);
-        __builtin_amdgcn_s_barrier();
-        if (t + 2 < n_tiles) issue_v(s_slot1, rows_n);
-        if (t + 3 < n_tiles) rows_n = rows_of(t + 3);
-        if (wave_active) qk(t + 1, s_slot2);
+        wait_vmcnt<kKIns + kVIns>();
+        ring_barrier();
+        issue_v(s_slot1, rows_n);
+        rows_n = rows_of(t + 3);
+        if (qk_wave) qk(t + 1, s_slot2);
         end_half();
         // h = 2t+3: P.V of tile t+1 (slot 3); issue K(t+3) into slot 2
-        wait_half(2 * t + 3, n_half);
-        __builtin_amdgcn_s_barrier();
-        if (t + 3 < n_tiles) issue_k(s_slot2, rows_n);
-        if (wave_active) pv(s_slot3);
+        wait_vmcnt<kKIns + kVIns>();
+        ring_barrier();
+        issue_k(s_slot2, rows_n);
+        pv(s_slot3);
         end_half();
     }
-    if (!wave_active) return;
+
+    // the copies past the last tile land before the workgroup's LDS is released
+    wait_vmcnt<0>();
 
     // ---------------------------------------------------- epilogue
-    // l of head l16 summed over the four lane groups (m_run already agrees)
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
-    float li[4], mi[4];
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        li[i] = __shfl(l_run, 4 * g + i);
-        mi[i] = __shfl(m_run, 4 * g + i);
-    }
-    const int hrow0 = hb * 64 + wave * 16 + 4 * g;     // heads of this lane's accumulator rows
-    if (P.direct) {
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int hh = hrow0 + i;
-            if (hh >= P.QN) continue;
-            const float inv = li[i] > 0.f ? 1.f / li[i] : 0.f;
-#pragma unroll
-            for (int nb = 0; nb < kD / 16; nb++)
-                M::store(P.out, ((int64_t)b * P.QN + hh) * kD + 16 * nb + l16, acc[nb][i] * inv);
+    const int64_t prow = ((int64_t)b * P.n_sc + sc) * P.QN;   // partial rows of this chunk
+    if (qk_wave) {
+        // l of head l16 summed over the four lane groups (m_run already agrees)
+        l_run += __shfl_xor(l_run, 16);
+        l_run += __shfl_xor(l_run, 32);
+        if (g == 0) {
+            if (P.direct) s_linv[wave * 16 + l16] = l_run > 0.f ? 1.f / l_run : 0.f;
+            else if (h_ok) *reinterpret_cast<float2 *>(P.part_ml + (prow + h) * 2) = make_float2(m_run, l_run);
         }
-    } else {
-        const int64_t prow = ((int64_t)b * P.n_sc + sc) * P.QN;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int hg = 0; hg < kWavesPerBlock; hg++) {
+        if (hg >= n_act) continue;
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-            const int hh = hrow0 + i;
+            const int hh = hb * 64 + hg * 16 + 4 * g + i;
             if (hh >= P.QN) continue;
-            float *dst = P.part_acc + (prow + hh) * kD + l16;
+            const int64_t col = 128 * wave + l16;
+            if (P.direct) {
+                const float inv = s_linv[hg * 16 + 4 * g + i];
 #pragma unroll
-            for (int nb = 0; nb < kD / 16; nb++) dst[16 * nb] = acc[nb][i];
-            if (l16 == 0) *reinterpret_cast<float2 *>(P.part_ml + (prow + hh) * 2) = make_float2(mi[i], li[i]);
+                for (int j = 0; j < 8; j++) M::store(P.out, ((int64_t)b * P.QN + hh) * kD + col + 16 * j, acc[hg][j][i] * inv);
+            } else {
+                float *dst = P.part_acc + (prow + hh) * kD + col;
+#pragma unroll
+                for (int j = 0; j < 8; j++) dst[16 * j] = acc[hg][j][i];
+            }
         }
     }
 }
