@@ -30,6 +30,36 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode attention µs/call + achieved HBM GB/s (% of MI355X peak) at 1 GPU"
 HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.txt")
+
+
+def sources_sha() -> str:
+    """Hash of the library's kernel sources and build flags; counter-based
+    traffic figures are only reported for the sources they were taken on."""
+    import hashlib
+    pkg = os.path.join(ROOT, "decode_attention_kv_06_amd")
+    h = hashlib.sha256()
+    files = sorted(os.path.join("csrc", f) for f in os.listdir(os.path.join(pkg, "csrc"))) + ["build.py"]
+    for rel in files:
+        h.update(rel.encode())
+        with open(os.path.join(pkg, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the workload's dominant kernel, from the
+    FETCH_SIZE / WRITE_SIZE counter summary (already scaled by the copy-kernel
+    calibration), or None when absent or taken on other sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    sha = sources_sha()
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            parts = line.split()
+            if len(parts) >= 4 and not line.startswith("#") and parts[0] == workload and parts[-1] == sha:
+                return int(parts[-2])
+    return None
 
 
 def algorithmic_bytes(inp) -> dict:
@@ -248,7 +278,7 @@ def main() -> int:
         "flush_between_calls": bool(args.flush),
         "roofline": {"bound": "hbm", "kernel": kernel_name, "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "kernel_us_mean": round(kern_mean * 1e3, 2)},
+                     "traffic": measured_traffic(args.workload), "kernel_us_mean": round(kern_mean * 1e3, 2)},
     }
     if not args.no_cpu_baseline:
         print("bench: timing the fp64 CPU oracle", file=sys.stderr, flush=True)

@@ -35,6 +35,11 @@
  * row; duplicate sparse indices each count; sparse_mode 3 with one query row
  * equals mode 0.
  *
+ * Parity unpinned (conventions the pages do not fix): the GQA head map
+ * h -> h / (N / N_kv) and the antiquant form (x + offset) * scale.  The tests
+ * pin the rest of the arithmetic around them; the conventions themselves are
+ * shared by both sides, not checked against the pages.
+ *
  * Arithmetic: stored fp16/bf16/int8 values are widened exactly to double;
  * exp is libm exp in double; softmax subtracts the row maximum.
  *
