@@ -175,7 +175,9 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=50, help="untimed calls first: the GPU takes tens of calls to reach steady clocks")
+    ap.add_argument("--warmup", type=int, default=50, help="untimed calls first (at least this many)")
+    ap.add_argument("--warmup-ms", type=float, default=100.0,
+                    help="...and at least this long: the GPU takes tens of milliseconds of calls to reach steady clocks")
     ap.add_argument("--workload", default="dense_gqa_bf16_bsh")
     ap.add_argument("--flush", action="store_true", help="evict caches between calls (outside the timed events)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -224,10 +226,17 @@ def main() -> int:
         if rc != 0:
             raise binding.IfaError(rc, name)
 
-    for _ in range(args.warmup):
+    # warm-up: at least W calls and at least --warmup-ms of them (short calls
+    # need hundreds before the clocks settle)
+    t_w = time.perf_counter()
+    n_warm = 0
+    while n_warm < args.warmup or (time.perf_counter() - t_w) * 1e3 < args.warmup_ms:
         if flush_buf is not None:
             flush_buf.zero_()
         one_call()
+        n_warm += 1
+        if n_warm % 64 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
 
     K = args.steps
@@ -284,6 +293,7 @@ def main() -> int:
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
+        "warmup_calls_run": n_warm,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",

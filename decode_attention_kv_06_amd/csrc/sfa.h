@@ -17,8 +17,8 @@ struct SfaParams {
     const int32_t *lkv;       // [B]
     const int32_t *lq;        // [B] or nullptr
     void *out;                // [B, QN, 512]
-    float *part_acc;          // [B, n_sc, QN, 512] when the chunks are combined afterwards
-    float *part_ml;           // [B, n_sc, QN, 2]
+    void *part_o;             // [B, n_sc, QN, 512], input dtype: each chunk's output normalised by its own sum
+    float *part_ml;           // [B, n_sc, QN, 2]: the chunk's running max (log2 domain) and sum
     int64_t sparse_size;
     int32_t B, QN, bs, max_blocks, num_blocks;
     uint32_t bs_magic;

@@ -38,6 +38,9 @@ int validate(const sfa_mla_args *a) {
     return IFA_OK;
 }
 
+// Chunk outputs are kept in the input dtype (2 bytes), 256-byte aligned.
+size_t part_o_bytes(size_t rows) { return (rows * 512 * 2 + 255) / 256 * 256; }
+
 struct SfaPlan {
     int n_hb = 0, n_sc = 0, chunk = 0, grid = 0;
     size_t workspace = 0;
@@ -72,7 +75,7 @@ int plan(const sfa_mla_args *a, SfaPlan &p) {
     p.workspace = 0;
     if (n_sc > 1) {
         const size_t rows = (size_t)a->batch * n_sc * a->q_heads;
-        p.workspace = (rows * 512 * sizeof(float) + 255) / 256 * 256 + (rows * 2 * sizeof(float) + 255) / 256 * 256;
+        p.workspace = part_o_bytes(rows) + (rows * 2 * sizeof(float) + 255) / 256 * 256;
     }
     return IFA_OK;
 }
@@ -118,8 +121,8 @@ int sfa_run(const sfa_mla_args *a, void *ws, size_t ws_bytes, hipStream_t stream
     p.lq = a->actual_seq_lengths_query;
     p.out = a->attention_out;
     const size_t rows = (size_t)a->batch * pl.n_sc * a->q_heads;
-    p.part_acc = reinterpret_cast<float *>(ws);
-    p.part_ml = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + (rows * 512 * sizeof(float) + 255) / 256 * 256);
+    p.part_o = ws;
+    p.part_ml = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + part_o_bytes(rows));
     p.sparse_size = a->sparse_size;
     p.B = (int)a->batch;
     p.QN = (int)a->q_heads;

@@ -105,6 +105,7 @@ struct Mfma<true> {
         return r;
     }
     __device__ static void store(void *out, int64_t i, float v) { reinterpret_cast<__bf16 *>(out)[i] = (__bf16)v; }
+    __device__ static float load(const void *in, int64_t i) { return (float)reinterpret_cast<const __bf16 *>(in)[i]; }
 };
 template <>
 struct Mfma<false> {
@@ -126,6 +127,7 @@ struct Mfma<false> {
         return r;
     }
     __device__ static void store(void *out, int64_t i, float v) { reinterpret_cast<_Float16 *>(out)[i] = (_Float16)v; }
+    __device__ static float load(const void *in, int64_t i) { return (float)reinterpret_cast<const _Float16 *>(in)[i]; }
 };
 
 // vmcnt(n) with the other counters left alone (gfx9 s_waitcnt encoding).
@@ -474,17 +476,22 @@ __global__ __launch_bounds__(256, 1) void sfa_kernel(const SfaParams P) {
     wait_vmcnt<0>();
 
     // ---------------------------------------------------- epilogue
+    // Every chunk writes its output normalised by its own sum: directly when
+    // the batch has one chunk, else in the input dtype to the workspace with
+    // (m, l) beside it for the combine.
     const int64_t prow = ((int64_t)b * P.n_sc + sc) * P.QN;   // partial rows of this chunk
     if (qk_wave) {
         // l of head l16 summed over the four lane groups (m_run already agrees)
         l_run += __shfl_xor(l_run, 16);
         l_run += __shfl_xor(l_run, 32);
         if (g == 0) {
-            if (P.direct) s_linv[wave * 16 + l16] = l_run > 0.f ? 1.f / l_run : 0.f;
-            else if (h_ok) *reinterpret_cast<float2 *>(P.part_ml + (prow + h) * 2) = make_float2(m_run, l_run);
+            s_linv[wave * 16 + l16] = l_run > 0.f ? 1.f / l_run : 0.f;
+            if (!P.direct && h_ok) *reinterpret_cast<float2 *>(P.part_ml + (prow + h) * 2) = make_float2(m_run, l_run);
         }
     }
     __syncthreads();
+    void *dst = P.direct ? P.out : P.part_o;
+    const int64_t row0 = P.direct ? (int64_t)b * P.QN : prow;
 #pragma unroll
     for (int hg = 0; hg < kWavesPerBlock; hg++) {
         if (hg >= n_act) continue;
@@ -492,21 +499,16 @@ __global__ __launch_bounds__(256, 1) void sfa_kernel(const SfaParams P) {
         for (int i = 0; i < 4; i++) {
             const int hh = hb * 64 + hg * 16 + 4 * g + i;
             if (hh >= P.QN) continue;
-            const int64_t col = 128 * wave + l16;
-            if (P.direct) {
-                const float inv = s_linv[hg * 16 + 4 * g + i];
+            const float inv = s_linv[hg * 16 + 4 * g + i];
+            const int64_t base = (row0 + hh) * kD + 128 * wave + l16;
 #pragma unroll
-                for (int j = 0; j < 8; j++) M::store(P.out, ((int64_t)b * P.QN + hh) * kD + col + 16 * j, acc[hg][j][i] * inv);
-            } else {
-                float *dst = P.part_acc + (prow + hh) * kD + col;
-#pragma unroll
-                for (int j = 0; j < 8; j++) dst[16 * j] = acc[hg][j][i];
-            }
+            for (int j = 0; j < 8; j++) M::store(dst, base + 16 * j, acc[hg][j][i] * inv);
         }
     }
 }
 
-// Merges the chunk states of one (b, h) row in chunk order and rounds.
+// Merges the chunk outputs of one (b, h) row in chunk order:
+// out = sum_s w_s o_s / sum_s w_s with w_s = l_s 2^(m_s - max m), and rounds.
 template <bool BF>
 __global__ __launch_bounds__(256) void sfa_combine_kernel(const SfaParams P) {
     using M = Mfma<BF>;
@@ -523,11 +525,11 @@ __global__ __launch_bounds__(256) void sfa_combine_kernel(const SfaParams P) {
     for (int e = 0; e < kD / 64; e++) o[e] = 0.f;
     for (int s = 0; s < P.n_sc; s++) {
         const float2 v = ml[prow(s)];
-        const float w = __builtin_amdgcn_exp2f(v.x - Mx);
-        L += w * v.y;
-        const float *a = P.part_acc + prow(s) * kD;
+        const float w = v.y * __builtin_amdgcn_exp2f(v.x - Mx);
+        L += w;
+        const int64_t base = prow(s) * kD + lane;
 #pragma unroll
-        for (int e = 0; e < kD / 64; e++) o[e] += w * a[lane + 64 * e];
+        for (int e = 0; e < kD / 64; e++) o[e] += w * M::load(P.part_o, base + 64 * e);
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll

@@ -248,3 +248,12 @@ def test_sfa_rejections(kw, code):
 
 def test_sfa_mode_three_is_accepted():
     assert ws_size("sfa_decode_mla_workspace_size", sfa_args(sparse_mode=3))[0] == 0
+
+
+def test_sfa_workspace_holds_chunk_outputs_in_input_dtype():
+    # sparse_size 100 in 2 chunks of 64 entries: 2 batches x 2 chunks x 16 heads rows,
+    # 512 two-byte values each, then (m, l) as two floats per row
+    rc, n = ws_size("sfa_decode_mla_workspace_size", sfa_args(split_hint=2))
+    assert rc == 0 and n == 2 * 2 * 16 * 512 * 2 + 2 * 2 * 16 * 2 * 4
+    rc, n = ws_size("sfa_decode_mla_workspace_size", sfa_args(split_hint=1))
+    assert rc == 0 and n == 0
