@@ -137,6 +137,18 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// max(x, x of lane ^ 16) and max(x, x of lane ^ 32) with the gfx950 row-swap
+// permutes: one swap returns, in every lane, the values of both rows of the
+// pair, so their max (or sum) is the pairwise reduction.  No LDS round trip.
+__device__ __forceinline__ float max_xor16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x), false, false);
+    return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x), false, false);
+    return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+}
+
 // Workgroup barrier without a memory fence (the copies in flight must stay in
 // flight across it).  The empty assembly statements keep the compiler from
 // moving LDS accesses across the barrier.
@@ -300,7 +312,7 @@ __global__ __launch_bounds__(256, 1) void sfa_kernel(const SfaParams P) {
     // scores of tile `tile` for head group `wave` from its key slot, the
     // online-softmax update, and P (A-operand layout) and the rescale factors
     // published in LDS
-    auto qk = [&](int tile, const char *ks_) {
+    auto qk = [&](int tile, const char *ks_, auto &&pre) {
         // 36 products: step i takes row block i % 2 and k-step i / 2, so the
         // two accumulation chains interleave.
         constexpr int kSteps = 2 * (kDK / 32);
@@ -318,6 +330,7 @@ __global__ __launch_bounds__(256, 1) void sfa_kernel(const SfaParams P) {
         vec8 abuf[2][kGrp];
 #pragma unroll
         for (int i = 0; i < kGrp; i++) abuf[0][i] = *reinterpret_cast<const vec8 *>(a_ptr(i));
+        pre();      // the step's copies issue while the first operands are read
 #pragma unroll
         for (int j = 0; j < kGroups; j++) {
             // operands of group j have arrived; only then issue group j + 1, so
@@ -349,8 +362,8 @@ __global__ __launch_bounds__(256, 1) void sfa_kernel(const SfaParams P) {
                 p[tb * 4 + i] = s;
                 mt = fmaxf(mt, s);
             }
-        mt = fmaxf(mt, __shfl_xor(mt, 16));
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        mt = max_xor16(mt);
+        mt = max_xor32(mt);
         const bool raise = mt > m_run + kLazy;
         float alpha = 1.f;
         int flag = 0;
@@ -375,17 +388,18 @@ __global__ __launch_bounds__(256, 1) void sfa_kernel(const SfaParams P) {
     // head group.  The V~ operand is read transposed from LDS (lane j of a
     // 16-lane group points at row 4g + j/4, columns 4(j%4)..+3 of the 16-column
     // block; the second read covers rows 16 + 4g + j/4) and serves all groups.
-    auto pv = [&](const char *vs_) {
+    auto pv = [&](const char *vs_, auto &&pre) {
         const u32x4 fl = *reinterpret_cast<const u32x4 *>(s_flag);
         vec8 pa[kWavesPerBlock];
 #pragma unroll
         for (int hg = 0; hg < kWavesPerBlock; hg++) pa[hg] = *reinterpret_cast<const vec8 *>(s_p + (hg * 64 + lane) * 16);
         const char *v0 = vs_ + (4 * g + (l16 >> 2)) * kRP + 8 * (l16 & 3) + 256 * wave;
         const char *v1 = v0 + 16 * kRP;
-        constexpr int kPfV = 2, kGroups = 8 / kPfV;
+        constexpr int kPfV = 4, kGroups = 8 / kPfV;
         vec8 bbuf[2][kPfV];
 #pragma unroll
         for (int i = 0; i < kPfV; i++) bbuf[0][i] = M::tr2(v0 + 32 * i, v1 + 32 * i);
+        pre();      // the step's copies issue while the first operands are read
         // a raised running max rescales what the group accumulated so far
         if (fl[0] | fl[1] | fl[2] | fl[3]) {
 #pragma unroll
@@ -446,29 +460,31 @@ __global__ __launch_bounds__(256, 1) void sfa_kernel(const SfaParams P) {
         // h = 2t: scores of tile t (slot 0); issue V(t+1) into slot 3
         wait_vmcnt<kKIns + kVIns>();
         ring_barrier();
-        issue_v(s_slot3, rows_n);
-        rows_n = rows_of(t + 2);
-        if (qk_wave) qk(t, s_slot0);
+        {
+            auto pre = [&]() { issue_v(s_slot3, rows_n); rows_n = rows_of(t + 2); };
+            if (qk_wave) qk(t, s_slot0, pre);
+            else pre();
+        }
         end_half();
         // h = 2t+1: P.V of tile t (slot 1); issue K(t+2) into slot 0
         wait_vmcnt<kKIns + kVIns>();
         ring_barrier();
-        issue_k(s_slot0, rows_n);
-        pv(s_slot1);
+        pv(s_slot1, [&]() { issue_k(s_slot0, rows_n); });
         end_half();
         if (t + 1 >= n_tiles) break;
         // h = 2t+2: scores of tile t+1 (slot 2); issue V(t+2) into slot 1
         wait_vmcnt<kKIns + kVIns>();
         ring_barrier();
-        issue_v(s_slot1, rows_n);
-        rows_n = rows_of(t + 3);
-        if (qk_wave) qk(t + 1, s_slot2);
+        {
+            auto pre = [&]() { issue_v(s_slot1, rows_n); rows_n = rows_of(t + 3); };
+            if (qk_wave) qk(t + 1, s_slot2, pre);
+            else pre();
+        }
         end_half();
         // h = 2t+3: P.V of tile t+1 (slot 3); issue K(t+3) into slot 2
         wait_vmcnt<kKIns + kVIns>();
         ring_barrier();
-        issue_k(s_slot2, rows_n);
-        pv(s_slot3);
+        pv(s_slot3, [&]() { issue_k(s_slot2, rows_n); });
         end_half();
     }
 
