@@ -48,6 +48,64 @@ __device__ __forceinline__ float swz_xor16(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F));
 }
 
+// Value of lane n of this lane's 16-lane DPP row (row_newbcast).
+template <int N>
+__device__ __forceinline__ float row_bcast(float x) { return dpp<0x150 + N>(x); }
+
+// Reduce-scatter of G per-lane partial sums over the 16 lanes of a DPP row.
+// Each level pairs lanes differing in one lane bit (row mirror: bit 3, half
+// mirror: bit 2, quad xor 2: bit 1) and halves the heads a lane keeps: the
+// lane with the bit set keeps the upper half and sends the lower half.  After
+// log2(G) levels lane c holds one head, head_of_lane(c); the remaining in-row
+// levels (and the cross-row ones for rows longer than 16 lanes) are plain.
+template <int CTRL, int BIT, int N>
+__device__ __forceinline__ void scatter_level(float (&v)[8], int lane) {
+    const bool up = (lane >> BIT) & 1;
+#pragma unroll
+    for (int j = 0; j < N / 2; j++) {
+        const float keep = up ? v[j + N / 2] : v[j];
+        const float send = up ? v[j] : v[j + N / 2];
+        v[j] = keep + dpp<CTRL>(send);
+    }
+}
+template <int G, int LPR>
+__device__ __forceinline__ float scatter_reduce(const float (&s)[G], int lane) {
+    static_assert(G == 2 || G == 4 || G == 8, "head group");
+    static_assert(LPR >= 16, "whole DPP rows");
+    float v[8];
+#pragma unroll
+    for (int h = 0; h < G; h++) v[h] = s[h];
+    scatter_level<0x140, 3, G>(v, lane);
+    if constexpr (G >= 4) scatter_level<0x141, 2, G / 2>(v, lane);
+    else v[0] += dpp<0x141>(v[0]);
+    if constexpr (G >= 8) scatter_level<0x4E, 1, G / 4>(v, lane);
+    else v[0] += dpp<0x4E>(v[0]);
+    v[0] += dpp<0xB1>(v[0]);
+    if constexpr (LPR >= 32) v[0] += swz_xor16(v[0]);
+    if constexpr (LPR >= 64) v[0] += __shfl_xor(v[0], 32);
+    return v[0];
+}
+template <int G>
+__device__ __forceinline__ int head_of_lane(int lane) {
+    int h = ((lane >> 3) & 1) * (G / 2);
+    if constexpr (G >= 4) h += ((lane >> 2) & 1) * (G / 4);
+    if constexpr (G >= 8) h += (lane >> 1) & 1;
+    return h;
+}
+// the lane of a DPP row that holds head H after scatter_reduce
+template <int G, int H>
+constexpr int lane_of_head() {
+    return ((H / (G / 2)) & 1) * 8 + (G >= 4 ? ((H / (G >= 4 ? G / 4 : 1)) & 1) * 4 : 0) + (G >= 8 ? (H & 1) * 2 : 0);
+}
+// every head's value from the lanes that hold them
+template <int G, int H = 0>
+__device__ __forceinline__ void gather_heads(float x, float (&out)[G]) {
+    if constexpr (H < G) {
+        out[H] = row_bcast<lane_of_head<G, H>()>(x);
+        gather_heads<G, H + 1>(x, out);
+    }
+}
+
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c, std::integral_constant<int, KV_BF16>) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
 }
@@ -111,11 +169,15 @@ void split_kernel(const SplitParams P) {
     constexpr int LPR = C::LPR, RPI = C::RPI, W = C::W, EB = C::EB, RT = C::RT, TT = C::TT;
     constexpr bool I8 = KV == KV_I8;
     using DotK = std::integral_constant<int, I8 ? KV_F16 : KV>;
+    // heads reduced by reduce-scatter (one head per lane through the softmax)
+    // when a KV row fills whole DPP rows and the group has several heads
+    constexpr bool SCATTER = LPR >= 16 && G >= 2;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wave_id = blockIdx.x * kWavesPerBlock + wave;
     if (wave_id >= P.n_pieces) return;
+    const int hl = SCATTER ? head_of_lane<(G >= 2 ? G : 2)>(lane) : 0;   // scatter path: this lane's head
     const int r = lane / LPR;      // row group
     const int c = lane % LPR;      // 8-element slot within the row
     const char *kb = reinterpret_cast<const char *>(P.k);
@@ -315,6 +377,7 @@ void split_kernel(const SplitParams P) {
 #pragma unroll
             for (int e = 0; e < 8; e++) acc[hh][e] = 0.f;
         }
+        float m1 = kMaxInit, l1 = 0.f;      // scatter path: state of this lane's head hl
 
         // -------------------------------------------------- main loop
         int ts = lo;
@@ -345,37 +408,42 @@ void split_kernel(const SplitParams P) {
                     s[i][hh] = a;
                 }
             }
-            if constexpr (LPR >= 2) {
+            float x[RT];        // scatter path: this lane's head, per row step
+            if constexpr (SCATTER) {
+#pragma unroll
+                for (int i = 0; i < RT; i++) x[i] = scatter_reduce<G, LPR>(s[i], lane);
+            }
+            if constexpr (!SCATTER && LPR >= 2) {
 #pragma unroll
                 for (int i = 0; i < RT; i++)
 #pragma unroll
                     for (int hh = 0; hh < G; hh++) s[i][hh] += dpp<0xB1>(s[i][hh]);   // quad_perm [1,0,3,2]
             }
-            if constexpr (LPR >= 4) {
+            if constexpr (!SCATTER && LPR >= 4) {
 #pragma unroll
                 for (int i = 0; i < RT; i++)
 #pragma unroll
                     for (int hh = 0; hh < G; hh++) s[i][hh] += dpp<0x4E>(s[i][hh]);   // quad_perm [2,3,0,1]
             }
-            if constexpr (LPR >= 8) {
+            if constexpr (!SCATTER && LPR >= 8) {
 #pragma unroll
                 for (int i = 0; i < RT; i++)
 #pragma unroll
                     for (int hh = 0; hh < G; hh++) s[i][hh] += dpp<0x141>(s[i][hh]);  // row_half_mirror
             }
-            if constexpr (LPR >= 16) {
+            if constexpr (!SCATTER && LPR >= 16) {
 #pragma unroll
                 for (int i = 0; i < RT; i++)
 #pragma unroll
                     for (int hh = 0; hh < G; hh++) s[i][hh] += dpp<0x140>(s[i][hh]);  // row_mirror
             }
-            if constexpr (LPR >= 32) {
+            if constexpr (!SCATTER && LPR >= 32) {
 #pragma unroll
                 for (int i = 0; i < RT; i++)
 #pragma unroll
                     for (int hh = 0; hh < G; hh++) s[i][hh] += swz_xor16(s[i][hh]);
             }
-            if constexpr (LPR >= 64) {
+            if constexpr (!SCATTER && LPR >= 64) {
 #pragma unroll
                 for (int i = 0; i < RT; i++)
 #pragma unroll
@@ -402,48 +470,89 @@ void split_kernel(const SplitParams P) {
             const bool more = ts + TT < hi;
             if (more) issue_k(ts + TT);
 
-            // scale; exclude positions past the segment, out-of-range blocks and masked ones
+            if constexpr (SCATTER) {
+                // this lane's head: mask bitmap, scale, online softmax, then
+                // every head's p fetched back from the lanes that hold them
+                uint64_t mbl = 0;
+                if constexpr (MASKED) {
+                    mbl = mbits[0];
 #pragma unroll
-            for (int i = 0; i < RT; i++) {
-                const int pos = i * RPI + r;             // position within the tile
-                const bool in = ts + pos < hi && okc[i];
-#pragma unroll
-                for (int hh = 0; hh < G; hh++) {
-                    bool keep = in;
-                    if constexpr (MASKED) keep = keep && !((mbits[hh] >> pos) & 1);
-                    s[i][hh] = keep ? s[i][hh] * qmul : kNegInf;
+                    for (int hh = 1; hh < MB; hh++) mbl = hl == hh ? mbits[hh] : mbl;
                 }
-            }
-            // online softmax (log2 domain) with a lazily raised maximum
-            float mt[G];
-            bool raise = false;
+                float mt = kNegInf;
 #pragma unroll
-            for (int hh = 0; hh < G; hh++) {
-                mt[hh] = s[0][hh];
-#pragma unroll
-                for (int i = 1; i < RT; i++) mt[hh] = fmaxf(mt[hh], s[i][hh]);
-                raise |= mt[hh] > m[hh] + kLazy;
-            }
-            if (__builtin_amdgcn_ballot_w64(raise)) {
-#pragma unroll
-                for (int hh = 0; hh < G; hh++) {
-                    const float mn = mt[hh] > m[hh] + kLazy ? mt[hh] : m[hh];
-                    const float alpha = __builtin_amdgcn_exp2f(m[hh] - mn);
-                    m[hh] = mn;
-                    l[hh] *= alpha;
-#pragma unroll
-                    for (int e = 0; e < 8; e++) acc[hh][e] *= alpha;
+                for (int i = 0; i < RT; i++) {
+                    const int pos = i * RPI + r;
+                    bool keep = ts + pos < hi && okc[i];
+                    if constexpr (MASKED) keep = keep && !((mbl >> pos) & 1);
+                    x[i] = keep ? x[i] * qmul : kNegInf;
+                    mt = fmaxf(mt, x[i]);
                 }
-            }
+                const bool raise = mt > m1 + kLazy;
+                if (__builtin_amdgcn_ballot_w64(raise)) {
+                    const float mn = raise ? mt : m1;
+                    const float alpha = __builtin_amdgcn_exp2f(m1 - mn);
+                    m1 = mn;
+                    l1 *= alpha;
+                    float ah[G];
+                    gather_heads<G>(alpha, ah);
 #pragma unroll
-            for (int hh = 0; hh < G; hh++) {
+                    for (int hh = 0; hh < G; hh++)
+#pragma unroll
+                        for (int e = 0; e < 8; e++) acc[hh][e] *= ah[hh];
+                }
                 float ls = 0.f;
 #pragma unroll
                 for (int i = 0; i < RT; i++) {
-                    s[i][hh] = __builtin_amdgcn_exp2f(s[i][hh] - m[hh]);
-                    ls += s[i][hh];
+                    x[i] = __builtin_amdgcn_exp2f(x[i] - m1);
+                    ls += x[i];
+                    gather_heads<G>(x[i], s[i]);
                 }
-                l[hh] += ls;
+                l1 += ls;
+            } else {
+                // scale; exclude positions past the segment, out-of-range blocks and masked ones
+#pragma unroll
+                for (int i = 0; i < RT; i++) {
+                    const int pos = i * RPI + r;             // position within the tile
+                    const bool in = ts + pos < hi && okc[i];
+#pragma unroll
+                    for (int hh = 0; hh < G; hh++) {
+                        bool keep = in;
+                        if constexpr (MASKED) keep = keep && !((mbits[hh] >> pos) & 1);
+                        s[i][hh] = keep ? s[i][hh] * qmul : kNegInf;
+                    }
+                }
+                // online softmax (log2 domain) with a lazily raised maximum
+                float mt[G];
+                bool raise = false;
+#pragma unroll
+                for (int hh = 0; hh < G; hh++) {
+                    mt[hh] = s[0][hh];
+#pragma unroll
+                    for (int i = 1; i < RT; i++) mt[hh] = fmaxf(mt[hh], s[i][hh]);
+                    raise |= mt[hh] > m[hh] + kLazy;
+                }
+                if (__builtin_amdgcn_ballot_w64(raise)) {
+#pragma unroll
+                    for (int hh = 0; hh < G; hh++) {
+                        const float mn = mt[hh] > m[hh] + kLazy ? mt[hh] : m[hh];
+                        const float alpha = __builtin_amdgcn_exp2f(m[hh] - mn);
+                        m[hh] = mn;
+                        l[hh] *= alpha;
+#pragma unroll
+                        for (int e = 0; e < 8; e++) acc[hh][e] *= alpha;
+                    }
+                }
+#pragma unroll
+                for (int hh = 0; hh < G; hh++) {
+                    float ls = 0.f;
+#pragma unroll
+                    for (int i = 0; i < RT; i++) {
+                        s[i][hh] = __builtin_amdgcn_exp2f(s[i][hh] - m[hh]);
+                        ls += s[i][hh];
+                    }
+                    l[hh] += ls;
+                }
             }
             // P.V over pairs of row steps (two positions per dot2)
 #pragma unroll
@@ -477,6 +586,11 @@ void split_kernel(const SplitParams P) {
             if (!more) break;
             issue_v(ts + TT);
             ts += TT;
+        }
+
+        if constexpr (SCATTER) {
+            gather_heads<G>(m1, m);
+            gather_heads<G>(l1, l);
         }
 
         // ------------------------------------------------------ merge row groups
