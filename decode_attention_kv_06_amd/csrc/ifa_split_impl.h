@@ -154,13 +154,15 @@ struct Cfg {
     static constexpr int RPI = 64 / LPR;                   // rows per load instruction
     static constexpr int W = (KV == KV_I8) ? 2 : 4;        // dwords per lane per row
     static constexpr int EB = (KV == KV_I8) ? 1 : 2;       // element bytes
-    static constexpr int RT = (G >= 8) ? 2 : (G >= 4) ? 4 : 8;   // row steps per tile
+    static constexpr int RT = (G >= 8) ? 4 : 8;                  // row steps per tile
     static constexpr int TT = RT * RPI;                    // positions per tile
 };
 
-// Waves per SIMD the register budget is sized for (G heads of state per lane).
+// Waves per SIMD the register budget is sized for (G heads of state per lane
+// and RT rows of K and V in flight): longer tiles at two waves per SIMD keep
+// more bytes in flight than shorter ones at three.
 template <int G>
-constexpr int waves_per_eu() { return (G == 1 || G == 4) ? 3 : 2; }
+constexpr int waves_per_eu() { return G == 1 ? 3 : 2; }
 
 template <int KV, int D, int G, bool PAGED, bool MASKED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_per_eu<G>(), 8)))
