@@ -74,7 +74,23 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineParams P) {
     for (int e = 0; e < kMaxPerLane; e++) o[e] = 0.f;
     float L = 0.f;
     float M = -__builtin_huge_valf();
-    for (int i0 = 0; i0 < nch; i0 += 64) {
+    // The accumulators of the first U splits are requested together with the
+    // (m, l) pairs (one memory round trip for rows of up to U splits).
+    constexpr int U = 8;
+    float v[U][kMaxPerLane];
+    auto load_acc = [&](int first, int cnt_total) {
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const float *acc = P.part_acc + prow(min(first + u, cnt_total - 1)) * D;
+#pragma unroll
+            for (int e = 0; e < kMaxPerLane; e++) v[u][e] = e < per_lane ? acc[lane + 64 * e] : 0.f;
+        }
+    };
+    float2 ml0 = make_float2(-__builtin_huge_valf(), 0.f);
+    if (lane < nch) ml0 = ml[prow(lane)];
+    if (nch > 0) load_acc(0, nch);
+    M = ml0.x;
+    for (int i0 = 64; i0 < nch; i0 += 64) {
         const int i = i0 + lane;
         if (i < nch) M = fmaxf(M, ml[prow(i)].x);
     }
@@ -83,22 +99,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineParams P) {
         const int cnt = min(64, nch - i0);
         float w = 0.f, lw = 0.f;
         if (lane < cnt) {
-            const float2 v = ml[prow(i0 + lane)];
-            w = __builtin_amdgcn_exp2f(v.x - M);
-            lw = w * v.y;
+            const float2 mv = i0 == 0 ? ml0 : ml[prow(i0 + lane)];
+            w = __builtin_amdgcn_exp2f(mv.x - M);
+            lw = w * mv.y;
         }
-        // Splits in order, eight at a time: their loads are issued together
+        // Splits in order, U at a time: their loads are issued together
         // (indices past the last split re-read it and get weight 0), then
         // accumulated in split order with the weight broadcast by readlane.
-        constexpr int U = 8;
         for (int i = 0; i < cnt; i += U) {
-            float v[U][kMaxPerLane];
-#pragma unroll
-            for (int u = 0; u < U; u++) {
-                const float *acc = P.part_acc + prow(i0 + min(i + u, cnt - 1)) * D;
-#pragma unroll
-                for (int e = 0; e < kMaxPerLane; e++) v[u][e] = e < per_lane ? acc[lane + 64 * e] : 0.f;
-            }
+            if (i0 + i > 0) load_acc(i0 + i, nch);
 #pragma unroll
             for (int u = 0; u < U; u++) {
                 const int iu = min(i + u, 63);
