@@ -11,7 +11,7 @@ order in which tensors are made.  Tensor ids:
 
     0 lengths  1 q  2 k  3 v  4 mask  5 block permutation  6 padding offsets
     7 antiquant scale  8 antiquant offset  9 q_rope  10 k_rope
-    11 sparse valid counts  12 sparse indices
+    11 sparse valid counts  12 sparse indices  13 positional bias (pseShift)
 
 Normals are float32 ``standard_normal`` draws rounded to nearest-even into
 fp16/bf16; integers are uniform and inclusive.  Whole buffers are filled,
@@ -29,6 +29,7 @@ import torch
 
 TID_LEN, TID_Q, TID_K, TID_V, TID_MASK, TID_PERM, TID_PAD = 0, 1, 2, 3, 4, 5, 6
 TID_AQ_SCALE, TID_AQ_OFFSET, TID_QROPE, TID_KROPE, TID_NVALID, TID_IDX = 7, 8, 9, 10, 11, 12
+TID_PSE = 13
 
 _TORCH_DT = {"f16": torch.float16, "bf16": torch.bfloat16, "i8": torch.int8}
 _CHUNK = 1 << 24
@@ -100,6 +101,10 @@ class IfaSpec:
     aq_scale: tuple = (0.005, 0.02)
     aq_offset: tuple = (-2.0, 2.0)
     q_mult: float = 1.0          # multiplies q after rounding (a "peaky" variant), re-rounded
+    # positional bias (pseShift): (pse_batch, N, 1, S_pse), query dtype, N(0,1) * pse_scale
+    pse: bool = False
+    pse_batch: int = 0           # 0 -> B, else 1
+    pse_scale: float = 1.0
 
     @property
     def nkv(self) -> int:
@@ -216,6 +221,16 @@ def make_ifa(spec: IfaSpec) -> dict:
             out["mask"] = torch.from_numpy(m.astype(np.uint8))
     else:
         out["mask"] = None
+
+    if spec.pse:
+        pb = 1 if spec.pse_batch == 1 else B
+        ps = out["max_blocks"] * spec.block_size if spec.paged else smax
+        bias = normal_tensor(rng_for(k_id, TID_PSE), (pb * N * ps,), spec.q_dtype)
+        if spec.pse_scale != 1.0:
+            bias = (bias.float() * spec.pse_scale).to(bias.dtype)
+        out["pse"] = bias.view(pb, N, 1, ps)
+    else:
+        out["pse"] = None
 
     if spec.antiquant is not None:
         shp = (2,) if spec.antiquant == "per_tensor" else (2, nkv, 1, D)

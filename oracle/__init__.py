@@ -40,7 +40,7 @@ def bind(path: str) -> ctypes.CDLL:
     lb = ctypes.CDLL(path)
     P, I64, I, D = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double
     lb.oracle_ifa.argtypes = [P, I, P, P, I, I, I64, I64, I64, I64, I64, D, P, P, P, I64, I64, I64,
-                                    P, I64, I64, I64, I, P, P, I, P, I64, P]
+                                    P, I64, I64, I64, I, P, P, I, P, I64, P, P, I64, I64]
     lb.oracle_ifa.restype = I
     lb.oracle_sfa.argtypes = [P, P, P, P, P, I, P, P, P, I64, I64, I64, I64, I64, I64, I64, I64, D, P, I64, P]
     lb.oracle_sfa.restype = I
@@ -90,12 +90,17 @@ def ifa(inp: dict, rows=None, scale=None, use=None) -> np.ndarray:
     out = np.empty((n, D), dtype=np.float64)
     aqs = inp["aq_scale"].contiguous() if inp["aq_scale"] is not None else None
     aqo = inp["aq_offset"].contiguous() if inp["aq_offset"] is not None else None
+    pse = inp.get("pse")
+    pB = pS = 0
+    if pse is not None:
+        pB, pS = pse.shape[0], pse.shape[3]
+        pse = pse.contiguous()
     rc = (use or lib()).oracle_ifa(
         _ptr(q), DT[q.dtype], _ptr(k), _ptr(v), DT[k.dtype], LAYOUT[s.layout], B, N, s.nkv, D, inp["S"],
         float(s.scale_value if scale is None else scale), _ptr(actual), _ptr(pad), _ptr(mask), mB, mN, mS,
         _ptr(bt), inp.get("max_blocks", 0) if bt is not None else 0, s.block_size if bt is not None else 0,
         inp.get("num_blocks", 0) if bt is not None else 0, s.cache_layout,
-        _ptr(aqs), _ptr(aqo), int(inp["aq_mode"]), _ptr(rows_a), n, _ptr(out))
+        _ptr(aqs), _ptr(aqo), int(inp["aq_mode"]), _ptr(rows_a), n, _ptr(out), _ptr(pse), pB, pS)
     if rc != 0:
         raise ValueError("oracle_ifa rejected its input (code %d)" % rc)
     return out.reshape(B, N, D) if rows is None else out

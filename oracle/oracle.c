@@ -18,6 +18,10 @@
  *       start or end < 0 gives an all-zero row; pad < 0 counts as 0
  *                                   (README "Constraints > kv left padding")
  *     - attenMask: a nonzero byte excludes the position            (reading, see below)
+ *     - pseShift: an additive bias pse[b|0, h, 0, s] in the query dtype, added
+ *       after the scale, at the same position coordinate as the mask
+ *                                   (README "Function > Formula" and
+ *                                    "Constraints"; placement is a reading)
  *     - GQA: query head h reads KV head h / (N / N_kv)              (reading)
  *     - page attention: logical position s lives in block
  *       blockTable[b][s / blockSize], row s % blockSize   (README "Constraints > page attention")
@@ -155,7 +159,7 @@ int oracle_ifa(const void *q, int q_dtype, const void *k, const void *v, int kv_
                const int64_t *pad, const uint8_t *mask, int64_t mB, int64_t mN, int64_t mS,
                const int32_t *block_table, int64_t max_blocks, int64_t block_size, int64_t num_blocks,
                int cache_layout, const void *aq_scale, const void *aq_offset, int aq_mode,
-               const int64_t *rows, int64_t nrows, double *out) {
+               const int64_t *rows, int64_t nrows, double *out, const void *pse, int64_t pB, int64_t pS) {
     if (Nkv == 0) Nkv = N;
     if (N % Nkv) return -1;
     const int64_t g = N / Nkv;
@@ -213,6 +217,10 @@ int oracle_ifa(const void *q, int q_dtype, const void *k, const void *v, int kv_
                 dot += elem(q, q_dtype, (b * N + h) * D + d) * kv;
             }
             x[cnt] = scale * dot;
+            if (pse) {
+                if (s >= pS) { err |= 1; break; }
+                x[cnt] += elem(pse, q_dtype, ((pB == 1 ? 0 : b) * N + h) * pS + s);
+            }
             ko[cnt] = off;
             cnt++;
         }

@@ -17,7 +17,10 @@ from test_oracle_pins import _sfa_gather_ref, _sfa_small, dense_kv_bnsd, sdpa_re
 
 MUTANTS = {
     "gqa_mapping_modulo": ("j = h / g;", "j = h % Nkv;"),
-    "scale_dropped": ("x[cnt] = scale * dot;\n            ko[cnt] = off;", "x[cnt] = dot;\n            ko[cnt] = off;"),
+    "scale_dropped": ("x[cnt] = scale * dot;\n            if (pse)", "x[cnt] = dot;\n            if (pse)"),
+    "pse_before_scale": ("x[cnt] += elem(pse,", "x[cnt] += scale * elem(pse,"),
+    "pse_batch_not_broadcast": ("((pB == 1 ? 0 : b) * N + h) * pS + s", "(b * N + h) * pS + s"),
+    "pse_indexed_by_kv_head": ("((pB == 1 ? 0 : b) * N + h) * pS + s", "((pB == 1 ? 0 : b) * N + j) * pS + s"),
     "mask_polarity": ("if (mask[mi]) continue;", "if (!mask[mi]) continue;"),
     "bnsd_read_as_bsh": ("off = ((b * Nkv + j) * S + s) * D;", "off = (b * S + s) * Nkv * D + j * D;"),
     "padding_not_clamped": ("int64_t p = pad[b] < 0 ? 0 : pad[b];", "int64_t p = pad[b];"),
@@ -67,6 +70,10 @@ def _battery(lib):
     kdq = (k64 + of[0].view(1, 2, 1, 16)) * sc[0].view(1, 2, 1, 16)
     vdq = (v64 + of[1].view(1, 2, 1, 16)) * sc[1].view(1, 2, 1, 16)
     res.append(("antiquant", close(oracle.ifa(inp, use=lib), sdpa_ref(inp, kdq, vdq))))
+    for pb in (0, 1):
+        inp = make_ifa(IfaSpec("m", 935, "bf16", "bf16", B=3, N=4, Nkv=2, D=16, S=40, len_range=(1, 40),
+                               pse=True, pse_batch=pb, pse_scale=2.0))
+        res.append(("pse_batch%d" % pb, close(oracle.ifa(inp, use=lib), sdpa_ref(inp))))
     inp = make_sfa(_sfa_small())
     res.append(("sfa", close(oracle.sfa(inp, use=lib), _sfa_gather_ref(inp))))
     inp = make_sfa(_sfa_small(n_valid=[40, 50]))

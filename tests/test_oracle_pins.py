@@ -3,7 +3,8 @@
 - exhaustive decoding of every fp16 / bf16 bit pattern against numpy / torch;
 - torch's scaled_dot_product_attention in float64 (a library routine) on tiny
   inputs, with the operator's mask polarity inverted into SDPA's
-  "True = attend" convention and GQA through SDPA's own enable_gqa;
+  "True = attend" convention, GQA through SDPA's own enable_gqa, and the
+  positional bias as SDPA's float attn_mask (added to the scaled scores);
 - closed forms: constant V, a single valid position, scale 0, the zero rule
   of left padding, the V-offset shift of antiquant;
 - the one worked call on the aclnnIncreFlashAttentionV2 page ("Example").
@@ -66,7 +67,14 @@ def sdpa_ref(inp, k64=None, v64=None, scale=None):
     if k64 is None:
         k64, v64 = dense_kv_bnsd(inp)
     m = attend_mask(inp)
-    out = F.scaled_dot_product_attention(q, k64, v64, attn_mask=m, scale=s.scale_value if scale is None else scale,
+    attn = m
+    if inp.get("pse") is not None:
+        # SDPA adds a float attn_mask to the scaled scores: the bias, with
+        # -inf where the operator does not attend
+        S = m.shape[-1]
+        attn = to64(inp["pse"]).expand(s.B, s.N, 1, inp["pse"].shape[-1])[..., :S].clone()
+        attn[~m] = float("-inf")
+    out = F.scaled_dot_product_attention(q, k64, v64, attn_mask=attn, scale=s.scale_value if scale is None else scale,
                                          enable_gqa=True)
     out = out.reshape(s.B, s.N, s.D)
     empty = ~m.any(dim=-1).reshape(s.B, s.N)
@@ -359,3 +367,73 @@ def test_sfa_out_of_range_entries_are_ignored():
     idx[0, 0, 0, 45] = 10 ** 6
     inp2["sparse_indices"] = idx
     np.testing.assert_allclose(oracle.sfa(inp2), ref, rtol=0, atol=0)
+
+
+# ------------------------------------------------------- positional bias ----
+@pytest.mark.parametrize("layout", ["BNSD", "BSH"])
+@pytest.mark.parametrize("pse_batch", [0, 1])
+def test_pse_matches_sdpa_float_bias(layout, pse_batch):
+    spec = IfaSpec("pin", 930, "bf16", "bf16", B=3, N=4, Nkv=2, D=16, layout=layout, S=40, len_range=(1, 40),
+                   mask="u8", mask_p=0.2, pse=True, pse_batch=pse_batch, pse_scale=2.0)
+    inp = make_ifa(spec)
+    np.testing.assert_allclose(oracle.ifa(inp), sdpa_ref(inp), rtol=0, atol=1e-12)
+
+
+def test_pse_with_left_padding_uses_physical_positions():
+    spec = IfaSpec("pin", 931, "f16", "f16", B=3, N=2, Nkv=1, D=8, layout="BNSD", S=48, len_range=(4, 30),
+                   pad_off=(0, 10), pse=True)
+    inp = make_ifa(spec)
+    np.testing.assert_allclose(oracle.ifa(inp), sdpa_ref(inp), rtol=0, atol=1e-12)
+
+
+def test_pse_zero_and_per_row_constant_change_nothing():
+    spec = IfaSpec("pin", 932, "bf16", "bf16", B=2, N=4, Nkv=2, D=16, S=33, len_range=(3, 33), pse=True)
+    inp = make_ifa(spec)
+    base = dict(inp)
+    base["pse"] = None
+    ref = oracle.ifa(base)
+    zero = dict(inp)
+    zero["pse"] = torch.zeros_like(inp["pse"])
+    assert (oracle.ifa(zero) == ref).all()
+    const = dict(inp)
+    c = torch.arange(inp["pse"].shape[0] * inp["pse"].shape[1], dtype=torch.float64).reshape(
+        inp["pse"].shape[0], inp["pse"].shape[1], 1, 1) * 0.75 - 3.0     # exact in bf16
+    const["pse"] = c.expand_as(inp["pse"]).to(inp["pse"].dtype).contiguous()
+    np.testing.assert_allclose(oracle.ifa(const), ref, rtol=0, atol=1e-12)
+
+
+def test_pse_minus_infinity_equals_masking():
+    spec = IfaSpec("pin", 933, "f16", "f16", B=2, N=2, Nkv=2, D=8, S=30, len_range=(10, 30), mask="bool",
+                   mask_p=0.3, mask_heads=2, pse=True)
+    inp = make_ifa(spec)
+    m = inp["mask"].to(torch.bool)                    # (B, N, 1, S): True = excluded
+    as_bias = dict(inp)
+    as_bias["mask"] = None
+    as_bias["pse"] = torch.where(m, torch.tensor(float("-inf"), dtype=inp["pse"].dtype), inp["pse"]).contiguous()
+    np.testing.assert_allclose(oracle.ifa(as_bias), oracle.ifa(inp), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("cache_layout", [0, 1])
+def test_paged_pse_uses_logical_positions(cache_layout):
+    bs = 16
+    spec = IfaSpec("pin", 934, "bf16", "bf16", B=3, N=4, Nkv=2, D=16, S=6 * bs, len_range=(1, 6 * bs),
+                   paged=True, block_size=bs, max_blocks=6, num_blocks=20, cache_layout=cache_layout, pse=True)
+    inp = make_ifa(spec)
+    B, nkv, D, mb = 3, 2, 16, 6
+    bt = inp["block_table"].long()
+    k, v = to64(inp["k"]), to64(inp["v"])
+    if cache_layout == 1:
+        k = k.view(-1, bs, nkv, D).permute(0, 2, 1, 3)
+        v = v.view(-1, bs, nkv, D).permute(0, 2, 1, 3)
+    kd = k[bt].permute(0, 2, 1, 3, 4).reshape(B, nkv, mb * bs, D)
+    vd = v[bt].permute(0, 2, 1, 3, 4).reshape(B, nkv, mb * bs, D)
+    np.testing.assert_allclose(oracle.ifa(inp), sdpa_ref(inp, kd, vd), rtol=0, atol=1e-12)
+
+
+def test_pse_shorter_than_attended_range_is_rejected():
+    spec = IfaSpec("pin", 936, "bf16", "bf16", B=2, N=2, Nkv=2, D=8, S=24, len_range=(24, 24), pse=True)
+    inp = make_ifa(spec)
+    short = dict(inp)
+    short["pse"] = inp["pse"][..., :20].contiguous()
+    with pytest.raises(ValueError):
+        oracle.ifa(short)
