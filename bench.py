@@ -11,7 +11,8 @@ stream), and the fp64 CPU oracle timed on the host cores as a baseline.
 
 Algorithmic bytes count what the method must move: the K/V rows of the
 attended window (unmasked rows only when a mask is given), the mask bytes of
-the window, block-table entries used, antiquant parameters, q and the output;
+the window, block-table entries used, antiquant parameters, the positional
+bias of the window, q and the output;
 for the sparse path the selected rows (512 + 64 + 512 elements), the indices,
 the block-table entries used, q, q_rope and the output.
 """
@@ -105,6 +106,9 @@ def algorithmic_bytes(inp) -> dict:
         extra += int(sum(math.ceil(int(x) / s.block_size) for x in n_win)) * 4
     if inp["aq_scale"] is not None:
         extra += 2 * inp["aq_scale"].numel() * 2
+    if inp.get("pse") is not None:
+        # per-batch bias: every window position of every head; a shared one once
+        extra += (int(n_win.sum()) if inp["pse"].shape[0] == B else int(hi.max(initial=0))) * N * 2
     return {"total": kv + extra + qo, "kv": kv, "streamed": streamed + extra + qo}
 
 
@@ -123,6 +127,8 @@ def describe_config(inp) -> dict:
         c.update(block_size=s.block_size, num_blocks=inp["num_blocks"], cache_layout=s.cache_layout)
     if s.mask:
         c["mask"] = "%s p=%.2f" % (s.mask, s.mask_p)
+    if s.pse:
+        c["pse_shift"] = "shared" if s.pse_batch == 1 else "per batch"
     if s.antiquant:
         c["antiquant"] = s.antiquant
     if s.pad_off:
@@ -159,6 +165,7 @@ def build_args(d: dict, o, split: int, keep: list):
         a = binding.ifa_paged_args(d["q"], d["k"], d["v"], o, d["block_table"], num_heads=s.N,
                                    num_key_value_heads=s.Nkv, input_layout=s.layout, scale_value=s.scale_value,
                                    actual_seq_lengths=d["actual_seq_lengths"], atten_mask=d["mask"],
+                                   pse_shift=d.get("pse"),
                                    antiquant_scale=d["aq_scale"], antiquant_offset=d["aq_offset"],
                                    antiquant_mode=d["aq_mode"], kv_cache_layout=s.cache_layout,
                                    split_tokens=split, keep=keep)
@@ -167,6 +174,7 @@ def build_args(d: dict, o, split: int, keep: list):
                                 input_layout=s.layout, scale_value=s.scale_value,
                                 actual_seq_lengths=d["actual_seq_lengths"],
                                 kv_padding_size=d["kv_padding_size"], atten_mask=d["mask"],
+                                pse_shift=d.get("pse"),
                                 antiquant_scale=d["aq_scale"], antiquant_offset=d["aq_offset"],
                                 antiquant_mode=d["aq_mode"], split_tokens=split, keep=keep)
     return "ifa_decode", a

@@ -37,7 +37,8 @@ class IfaDecodeArgs(ctypes.Structure):
         ("scale_value", ctypes.c_double), ("actual_seq_lengths", P), ("kv_padding_size", P),
         ("kv_padding_size_count", I64), ("atten_mask", P), ("dtype_mask", I32), ("mask_batch", I64),
         ("mask_heads", I64), ("mask_seq", I64), ("pse_shift", P), ("antiquant_scale", P), ("antiquant_offset", P),
-        ("antiquant_mode", I32), ("split_tokens", I64), ("profile_event_begin", P), ("profile_event_end", P)]
+        ("antiquant_mode", I32), ("split_tokens", I64), ("profile_event_begin", P), ("profile_event_end", P),
+        ("pse_batch", I64), ("pse_seq", I64)]
 
 
 class IfaPagedArgs(ctypes.Structure):
@@ -49,7 +50,7 @@ class IfaPagedArgs(ctypes.Structure):
         ("mask_batch", I64), ("mask_heads", I64), ("mask_seq", I64), ("pse_shift", P), ("antiquant_scale", P),
         ("antiquant_offset", P), ("antiquant_mode", I32), ("block_table", P), ("max_blocks_per_seq", I64),
         ("block_size", I64), ("num_blocks", I64), ("kv_cache_layout", I32), ("split_tokens", I64),
-        ("profile_event_begin", P), ("profile_event_end", P)]
+        ("profile_event_begin", P), ("profile_event_end", P), ("pse_batch", I64), ("pse_seq", I64)]
 
 
 class SfaMlaArgs(ctypes.Structure):
@@ -141,9 +142,20 @@ def _mask_fields(mask):
     return mask, _DT[mask.dtype], mask.shape[0], mask.shape[1], mask.shape[3]
 
 
+def _pse_fields(pse, q, num_heads):
+    """(pointer, pse_batch, pse_seq) of a pseShift tensor (pse_batch, N, 1, pse_seq) in the query dtype."""
+    if pse is None:
+        return None, 0, 0
+    if pse.dim() != 4 or pse.shape[1] != num_heads or pse.shape[2] != 1:
+        raise ValueError("pse_shift must be (B|1, N, 1, S_pse)")
+    if pse.dtype != q.dtype or not pse.is_contiguous():
+        raise ValueError("pse_shift must be contiguous, in the query dtype")
+    return pse, pse.shape[0], pse.shape[3]
+
+
 def ifa_decode_args(q, k, v, out, *, num_heads, num_key_value_heads=0, input_layout="BSH", scale_value=None,
-                    actual_seq_lengths=None, kv_padding_size=None, atten_mask=None, antiquant_scale=None,
-                    antiquant_offset=None, antiquant_mode=0, split_tokens=0, keep=None):
+                    actual_seq_lengths=None, kv_padding_size=None, atten_mask=None, pse_shift=None,
+                    antiquant_scale=None, antiquant_offset=None, antiquant_mode=0, split_tokens=0, keep=None):
     """Fill an IfaDecodeArgs from tensors; `keep` collects host arrays that must outlive the call."""
     N = int(num_heads)
     if input_layout == "BSH":
@@ -158,6 +170,7 @@ def ifa_decode_args(q, k, v, out, *, num_heads, num_key_value_heads=0, input_lay
     lens = _host_i64(actual_seq_lengths)
     pads = _host_i64(kv_padding_size)
     mask, dmask, mB, mN, mS = _mask_fields(atten_mask)
+    pse, pB, pS = _pse_fields(pse_shift, q, N)
     if keep is not None:
         keep.extend([lens, pads, input_layout.encode()])
     a = IfaDecodeArgs()
@@ -171,7 +184,7 @@ def ifa_decode_args(q, k, v, out, *, num_heads, num_key_value_heads=0, input_lay
     a.kv_padding_size = None if pads is None else pads.ctypes.data
     a.kv_padding_size_count = 0 if pads is None else len(pads)
     a.atten_mask, a.dtype_mask, a.mask_batch, a.mask_heads, a.mask_seq = _ptr(mask), dmask, mB, mN, mS
-    a.pse_shift = None
+    a.pse_shift, a.pse_batch, a.pse_seq = _ptr(pse), pB, pS
     a.antiquant_scale, a.antiquant_offset = _ptr(antiquant_scale), _ptr(antiquant_offset)
     a.antiquant_mode = int(antiquant_mode)
     a.split_tokens = int(split_tokens)
@@ -187,7 +200,7 @@ def ifa_decode(q, k, v, out, *, workspace=None, stream=None, **kw) -> int:
 
 def ifa_paged_args(q, key_cache, value_cache, out, block_table, *, num_heads, num_key_value_heads=0,
                    input_layout="BNSD", scale_value=None, actual_seq_lengths=None, atten_mask=None,
-                   antiquant_scale=None, antiquant_offset=None, antiquant_mode=0, kv_cache_layout=0,
+                   pse_shift=None, antiquant_scale=None, antiquant_offset=None, antiquant_mode=0, kv_cache_layout=0,
                    split_tokens=0, keep=None):
     N = int(num_heads)
     nkv = int(num_key_value_heads) or N
@@ -198,6 +211,7 @@ def ifa_paged_args(q, key_cache, value_cache, out, block_table, *, num_heads, nu
         D = key_cache.shape[2] // nkv
     lens = _host_i64(actual_seq_lengths)
     mask, dmask, mB, mN, mS = _mask_fields(atten_mask)
+    pse, pB, pS = _pse_fields(pse_shift, q, N)
     if keep is not None:
         keep.extend([lens, input_layout.encode()])
     a = IfaPagedArgs()
@@ -209,7 +223,7 @@ def ifa_paged_args(q, key_cache, value_cache, out, block_table, *, num_heads, nu
     a.scale_value = float(scale_value if scale_value is not None else 1.0 / float(D) ** 0.5)
     a.actual_seq_lengths = None if lens is None else lens.ctypes.data
     a.atten_mask, a.dtype_mask, a.mask_batch, a.mask_heads, a.mask_seq = _ptr(mask), dmask, mB, mN, mS
-    a.pse_shift = None
+    a.pse_shift, a.pse_batch, a.pse_seq = _ptr(pse), pB, pS
     a.antiquant_scale, a.antiquant_offset = _ptr(antiquant_scale), _ptr(antiquant_offset)
     a.antiquant_mode = int(antiquant_mode)
     a.block_table = _ptr(block_table)

@@ -10,6 +10,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <stddef.h>
+
 #include <algorithm>
 #include <functional>
 #include <mutex>
@@ -24,7 +26,7 @@ namespace {
 
 using namespace ifa;
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 
 bool is_float_dt(int dt) { return dt == IFA_DT_F16 || dt == IFA_DT_BF16; }
 
@@ -52,6 +54,7 @@ struct SlicePlan {
 struct IfaPlan {
     int kv = 0, D = 0, G = 0, n_hg = 0, g = 0, N = 0, Nkv = 0, B = 0;
     bool paged = false;
+    int extra = EX_NONE;                 // split kernel variant (mask / positional bias)
     std::vector<Window> win;             // per batch
     std::vector<SlicePlan> slices;
     int64_t total_slots = 0;
@@ -59,18 +62,18 @@ struct IfaPlan {
 };
 
 std::mutex g_mu;
-int g_resident[64][3][4][4][2][2];   // [dev][kv][log2 D/64][log2 G][paged][masked] resident waves, 0 = unknown
+int g_resident[64][3][4][4][2][3];   // [dev][kv][log2 D/64][log2 G][paged][extra] resident waves, 0 = unknown
 
 int current_device(int *dev) { return hipGetDevice(dev) == hipSuccess ? IFA_OK : IFA_ERR_RUNTIME; }
 
-int resident_waves(int kv, int D, int G, bool paged, bool masked) {
+int resident_waves(int kv, int D, int G, bool paged, int extra) {
     int dev = 0;
     if (current_device(&dev) != IFA_OK || dev < 0 || dev >= 64) return 0;
     const int di = D == 64 ? 0 : D == 128 ? 1 : D == 256 ? 2 : 3;
     const int gi = G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3;
     std::lock_guard<std::mutex> lk(g_mu);
-    int &slot = g_resident[dev][kv][di][gi][paged ? 1 : 0][masked ? 1 : 0];
-    if (!slot) slot = split_resident_waves(kv, D, G, paged, masked);
+    int &slot = g_resident[dev][kv][di][gi][paged ? 1 : 0][extra];
+    if (!slot) slot = split_resident_waves(kv, D, G, paged, extra);
     return slot;
 }
 
@@ -78,13 +81,13 @@ int resident_waves(int kv, int D, int G, bool paged, bool masked) {
 // into n_pieces equal pieces, one per resident wave of the split kernel, so
 // every wave streams the same number of KV positions.  A row meets at most
 // ceil(len / piece) + 1 pieces, which bounds its partial slots.
-int finish_plan(IfaPlan &p, int64_t split_tokens, bool masked) {
+int finish_plan(IfaPlan &p, int64_t split_tokens) {
     p.G = 1;
     while (p.G < p.g && p.G < 8) p.G <<= 1;
     p.n_hg = (p.g + p.G - 1) / p.G;
     int waves = 0;
     if (split_tokens <= 0) {
-        waves = resident_waves(p.kv, p.D, p.G, p.paged, masked);
+        waves = resident_waves(p.kv, p.D, p.G, p.paged, p.extra);
         if (waves <= 0) return IFA_ERR_RUNTIME;
     }
     const int64_t rows_per_batch = (int64_t)p.Nkv * p.n_hg;
@@ -141,8 +144,8 @@ struct IfaCommon {
 
 int check_common(const void *q, const void *out, int dq, int dkv, int dout, const char *layout, int64_t B, int64_t N,
                  int64_t Nkv_in, int64_t D, double scale, const void *mask, int dmask, int64_t mB, int64_t mN,
-                 const void *pse, const void *aqs, const void *aqo, int aq_mode, int64_t split_tokens,
-                 IfaCommon *c) {
+                 const void *pse, int64_t pse_b, const void *aqs, const void *aqo, int aq_mode,
+                 int64_t split_tokens, IfaCommon *c) {
     if (!q || !out) return IFA_ERR_PARAM_NULLPTR;
     if (!is_float_dt(dq) || dout != dq) return IFA_ERR_PARAM_INVALID;
     if (dkv != dq && dkv != IFA_DT_I8) return IFA_ERR_PARAM_INVALID;
@@ -157,7 +160,7 @@ int check_common(const void *q, const void *out, int dq, int dkv, int dout, cons
         if (dmask != IFA_DT_BOOL && dmask != IFA_DT_I8 && dmask != IFA_DT_U8) return IFA_ERR_PARAM_INVALID;
         if ((mB != 1 && mB != B) || (mN != 1 && mN != N)) return IFA_ERR_PARAM_INVALID;
     }
-    if (pse) return IFA_ERR_PARAM_INVALID;
+    if (pse && pse_b != 1 && pse_b != B) return IFA_ERR_PARAM_INVALID;
     if (dkv == IFA_DT_I8) {
         if (aq_mode != IFA_ANTIQUANT_PER_TENSOR && aq_mode != IFA_ANTIQUANT_PER_CHANNEL) return IFA_ERR_PARAM_INVALID;
         if (!aqs || !aqo) return IFA_ERR_PARAM_NULLPTR;
@@ -172,11 +175,14 @@ int kv_kind(int dkv) { return dkv == IFA_DT_F16 ? KV_F16 : dkv == IFA_DT_BF16 ? 
 
 int plan_dense(const ifa_decode_args *a, IfaPlan &p, IfaCommon &c) {
     if (!a) return IFA_ERR_PARAM_NULLPTR;
-    if (a->struct_size < sizeof(ifa_decode_args)) return IFA_ERR_PARAM_INVALID;
+    if (a->struct_size < offsetof(ifa_decode_args, pse_batch)) return IFA_ERR_PARAM_INVALID;
+    const bool has_pse_dims = a->struct_size >= sizeof(ifa_decode_args);
+    if (a->pse_shift && !has_pse_dims) return IFA_ERR_PARAM_INVALID;
     int rc = check_common(a->query, a->attention_out, a->dtype_q, a->dtype_kv, a->dtype_out, a->input_layout,
                           a->batch, a->num_heads, a->num_key_value_heads, a->head_dim, a->scale_value, a->atten_mask,
-                          a->dtype_mask, a->mask_batch, a->mask_heads, a->pse_shift, a->antiquant_scale,
-                          a->antiquant_offset, a->antiquant_mode, a->split_tokens, &c);
+                          a->dtype_mask, a->mask_batch, a->mask_heads, a->pse_shift,
+                          has_pse_dims ? a->pse_batch : 0, a->antiquant_scale, a->antiquant_offset,
+                          a->antiquant_mode, a->split_tokens, &c);
     if (rc) return rc;
     if (!a->key || !a->value) return IFA_ERR_PARAM_NULLPTR;
     const int64_t S = a->kv_seq_len;
@@ -211,16 +217,21 @@ int plan_dense(const ifa_decode_args *a, IfaPlan &p, IfaCommon &c) {
         max_hi = std::max(max_hi, hi);
     }
     if (a->atten_mask && a->mask_seq < max_hi) return IFA_ERR_PARAM_INVALID;
+    if (a->pse_shift && a->pse_seq < max_hi) return IFA_ERR_PARAM_INVALID;
+    p.extra = a->pse_shift ? EX_PSE : a->atten_mask ? EX_MASK : EX_NONE;
     return IFA_OK;
 }
 
 int plan_paged(const ifa_paged_args *a, IfaPlan &p, IfaCommon &c) {
     if (!a) return IFA_ERR_PARAM_NULLPTR;
-    if (a->struct_size < sizeof(ifa_paged_args)) return IFA_ERR_PARAM_INVALID;
+    if (a->struct_size < offsetof(ifa_paged_args, pse_batch)) return IFA_ERR_PARAM_INVALID;
+    const bool has_pse_dims = a->struct_size >= sizeof(ifa_paged_args);
+    if (a->pse_shift && !has_pse_dims) return IFA_ERR_PARAM_INVALID;
     int rc = check_common(a->query, a->attention_out, a->dtype_q, a->dtype_kv, a->dtype_out, a->input_layout,
                           a->batch, a->num_heads, a->num_key_value_heads, a->head_dim, a->scale_value, a->atten_mask,
-                          a->dtype_mask, a->mask_batch, a->mask_heads, a->pse_shift, a->antiquant_scale,
-                          a->antiquant_offset, a->antiquant_mode, a->split_tokens, &c);
+                          a->dtype_mask, a->mask_batch, a->mask_heads, a->pse_shift,
+                          has_pse_dims ? a->pse_batch : 0, a->antiquant_scale, a->antiquant_offset,
+                          a->antiquant_mode, a->split_tokens, &c);
     if (rc) return rc;
     if (!a->key_cache || !a->value_cache || !a->block_table || !a->actual_seq_lengths) return IFA_ERR_PARAM_NULLPTR;
     const int64_t bs = a->block_size;
@@ -251,6 +262,8 @@ int plan_paged(const ifa_paged_args *a, IfaPlan &p, IfaCommon &c) {
     // README: blocknum may not be smaller than the blocks the lengths need.
     if (blocks_needed > a->num_blocks) return IFA_ERR_PARAM_INVALID;
     if (a->atten_mask && a->mask_seq < max_hi) return IFA_ERR_PARAM_INVALID;
+    if (a->pse_shift && a->pse_seq < max_hi) return IFA_ERR_PARAM_INVALID;
+    p.extra = a->pse_shift ? EX_PSE : a->atten_mask ? EX_MASK : EX_NONE;
     return IFA_OK;
 }
 
@@ -269,6 +282,8 @@ struct Launch {
     const uint8_t *mask;
     int64_t mask_sB, mask_sH;
     int mask_mode;
+    const void *pse;
+    int64_t pse_sB, pse_sH;
     const int32_t *block_table;
     int64_t sB, sN, sS, blk_stride, head_stride, row_stride;
     int max_blocks, block_size, num_blocks;
@@ -292,6 +307,9 @@ int run(const IfaPlan &p, const Launch &L, void *ws, size_t ws_bytes, hipStream_
     sp.k = L.k;
     sp.v = L.v;
     sp.mask = L.mask;
+    sp.pse = L.pse;
+    sp.pse_sB = L.pse_sB;
+    sp.pse_sH = L.pse_sH;
     sp.block_table = L.block_table;
     sp.k_scale = L.aqs;
     sp.sB = L.sB;
@@ -350,7 +368,7 @@ int run(const IfaPlan &p, const Launch &L, void *ws, size_t ws_bytes, hipStream_
         sp.part_ml = part_ml + s.slot_base * p.G * 2;
         cp.part_acc = sp.part_acc;
         cp.part_ml = sp.part_ml;
-        if (s.total > 0 && launch_split(sp, p.kv, p.D, p.G, p.paged, L.mask_mode != 0, stream) != hipSuccess)
+        if (s.total > 0 && launch_split(sp, p.kv, p.D, p.G, p.paged, p.extra, stream) != hipSuccess)
             return IFA_ERR_RUNTIME;
         if (timed && si + 1 == p.slices.size() && hipEventRecord(L.ev_end, stream) != hipSuccess)
             return IFA_ERR_RUNTIME;
@@ -381,6 +399,11 @@ Launch dense_launch(const ifa_decode_args *a, const IfaPlan &p, const IfaCommon 
         L.mask_sB = a->mask_batch == 1 ? 0 : a->mask_heads * a->mask_seq;
         L.mask_sH = a->mask_heads == 1 ? 0 : a->mask_seq;
         L.mask_mode = a->mask_heads == 1 ? 1 : 2;
+    }
+    if (a->pse_shift) {
+        L.pse = a->pse_shift;
+        L.pse_sB = a->pse_batch == 1 ? 0 : a->num_heads * a->pse_seq;
+        L.pse_sH = a->pse_seq;
     }
     L.aqs = a->antiquant_scale;
     L.aqo = a->antiquant_offset;
@@ -418,6 +441,11 @@ Launch paged_launch(const ifa_paged_args *a, const IfaPlan &p) {
         L.mask_sH = a->mask_heads == 1 ? 0 : a->mask_seq;
         L.mask_mode = a->mask_heads == 1 ? 1 : 2;
     }
+    if (a->pse_shift) {
+        L.pse = a->pse_shift;
+        L.pse_sB = a->pse_batch == 1 ? 0 : a->num_heads * a->pse_seq;
+        L.pse_sH = a->pse_seq;
+    }
     L.aqs = a->antiquant_scale;
     L.aqo = a->antiquant_offset;
     L.aq_mode = a->dtype_kv == IFA_DT_I8 ? a->antiquant_mode : 0;
@@ -450,7 +478,7 @@ int ifa_decode_workspace_size(const ifa_decode_args *a, size_t *bytes) {
     IfaCommon c;
     int rc = plan_dense(a, p, c);
     if (rc) return rc;
-    rc = finish_plan(p, a->split_tokens, a->atten_mask != nullptr);
+    rc = finish_plan(p, a->split_tokens);
     if (rc) return rc;
     *bytes = p.workspace;
     return IFA_OK;
@@ -461,7 +489,7 @@ int ifa_decode(const ifa_decode_args *a, void *ws, size_t ws_bytes, ifa_stream_t
     IfaCommon c;
     int rc = plan_dense(a, p, c);
     if (rc) return rc;
-    rc = finish_plan(p, a->split_tokens, a->atten_mask != nullptr);
+    rc = finish_plan(p, a->split_tokens);
     if (rc) return rc;
     return run(p, dense_launch(a, p, c), ws, ws_bytes, reinterpret_cast<hipStream_t>(stream));
 }
@@ -472,7 +500,7 @@ int ifa_decode_paged_workspace_size(const ifa_paged_args *a, size_t *bytes) {
     IfaCommon c;
     int rc = plan_paged(a, p, c);
     if (rc) return rc;
-    rc = finish_plan(p, a->split_tokens, a->atten_mask != nullptr);
+    rc = finish_plan(p, a->split_tokens);
     if (rc) return rc;
     *bytes = p.workspace;
     return IFA_OK;
@@ -483,7 +511,7 @@ int ifa_decode_paged(const ifa_paged_args *a, void *ws, size_t ws_bytes, ifa_str
     IfaCommon c;
     int rc = plan_paged(a, p, c);
     if (rc) return rc;
-    rc = finish_plan(p, a->split_tokens, a->atten_mask != nullptr);
+    rc = finish_plan(p, a->split_tokens);
     if (rc) return rc;
     return run(p, paged_launch(a, p), ws, ws_bytes, reinterpret_cast<hipStream_t>(stream));
 }

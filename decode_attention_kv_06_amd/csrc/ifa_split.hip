@@ -7,11 +7,11 @@
 
 namespace ifa {
 
-hipError_t launch_split(const SplitParams &p, int kv, int D, int G, bool paged, bool masked, hipStream_t s) {
+hipError_t launch_split(const SplitParams &p, int kv, int D, int G, bool paged, int extra, hipStream_t s) {
     switch (kv) {
-    case KV_F16: return launch_split_kv<KV_F16>(p, D, G, paged, masked, s);
-    case KV_BF16: return launch_split_kv<KV_BF16>(p, D, G, paged, masked, s);
-    case KV_I8: return launch_split_kv<KV_I8>(p, D, G, paged, masked, s);
+    case KV_F16: return launch_split_kv<KV_F16>(p, D, G, paged, extra, s);
+    case KV_BF16: return launch_split_kv<KV_BF16>(p, D, G, paged, extra, s);
+    case KV_I8: return launch_split_kv<KV_I8>(p, D, G, paged, extra, s);
     }
     return hipErrorInvalidValue;
 }
@@ -19,10 +19,10 @@ hipError_t launch_split(const SplitParams &p, int kv, int D, int G, bool paged, 
 // Resident waves of a kernel on the current device.  The occupancy query is
 // made once per (device, kernel) and cached: it does not change while the
 // process runs, and it would otherwise be a per-call host cost.
-int split_resident_waves(int kv, int D, int G, bool paged, bool masked) {
-    const void *f = kv == KV_F16 ? split_kernel_ptr<KV_F16>(D, G, paged, masked)
-                  : kv == KV_BF16 ? split_kernel_ptr<KV_BF16>(D, G, paged, masked)
-                                  : split_kernel_ptr<KV_I8>(D, G, paged, masked);
+int split_resident_waves(int kv, int D, int G, bool paged, int extra) {
+    const void *f = kv == KV_F16 ? split_kernel_ptr<KV_F16>(D, G, paged, extra)
+                  : kv == KV_BF16 ? split_kernel_ptr<KV_BF16>(D, G, paged, extra)
+                                  : split_kernel_ptr<KV_I8>(D, G, paged, extra);
     int dev = 0;
     if (!f || hipGetDevice(&dev) != hipSuccess) return 0;
     static std::mutex mu;

@@ -2,6 +2,6 @@
 #include "ifa_split_impl.h"
 
 namespace ifa {
-template hipError_t launch_split_kv<KV_F16>(const SplitParams &, int, int, bool, bool, hipStream_t);
-template const void *split_kernel_ptr<KV_F16>(int, int, bool, bool);
+template hipError_t launch_split_kv<KV_F16>(const SplitParams &, int, int, bool, int, hipStream_t);
+template const void *split_kernel_ptr<KV_F16>(int, int, bool, int);
 }  // namespace ifa

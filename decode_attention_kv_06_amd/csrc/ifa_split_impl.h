@@ -37,6 +37,7 @@ constexpr int kTblSlots = 256;        // staged block ids per wave (paged caches
 // this many log2 units, so p = exp2(x - m) stays below 2^kLazy (exact: the
 // same m scales both l and the accumulator).
 constexpr float kLazy = 8.0f;
+constexpr float kLog2e = 1.4426950408889634f;
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
@@ -164,12 +165,16 @@ struct Cfg {
 template <int G>
 constexpr int waves_per_eu() { return G == 1 ? 3 : 2; }
 
-template <int KV, int D, int G, bool PAGED, bool MASKED>
+// EXTRA selects the optional score terms compiled in: EX_NONE, EX_MASK
+// (attenMask), or EX_PSE (pseShift, with attenMask checked at run time).
+template <int KV, int D, int G, bool PAGED, int EXTRA>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_per_eu<G>(), 8)))
 void split_kernel(const SplitParams P) {
     using C = Cfg<KV, D, G>;
     constexpr int LPR = C::LPR, RPI = C::RPI, W = C::W, EB = C::EB, RT = C::RT, TT = C::TT;
     constexpr bool I8 = KV == KV_I8;
+    constexpr bool MASKED = EXTRA != EX_NONE;
+    constexpr bool PSE = EXTRA == EX_PSE;
     using DotK = std::integral_constant<int, I8 ? KV_F16 : KV>;
     // heads reduced by reduce-scatter (one head per lane through the softmax)
     // when a KV row fills whole DPP rows and the group has several heads
@@ -300,7 +305,27 @@ void split_kernel(const SplitParams P) {
             }
         }
         const uint8_t *mrow = nullptr;
-        if constexpr (MASKED) mrow = P.mask + (P.mask_sB ? b * P.mask_sB : 0) + (int64_t)hbase * P.mask_sH;
+        if constexpr (MASKED) {
+            if (P.mask) mrow = P.mask + (P.mask_sB ? b * P.mask_sB : 0) + (int64_t)hbase * P.mask_sH;
+        }
+        // pseShift row(s) of this lane.  Scatter path: the lane's own head, at
+        // the RT positions whose scores it holds.  Other path: every head of
+        // the group at position ts + lane (a coalesced read), fetched from the
+        // owning lane when the scores are scaled.  Heads past the group read
+        // head 0 of it; their scores are never stored.
+        constexpr int PH = PSE ? (SCATTER ? 1 : G) : 1;
+        constexpr int PR = PSE && SCATTER ? RT : 1;
+        const uint16_t *prow[PH];
+        bool pse_bf16 = false;
+        if constexpr (PSE) {
+            pse_bf16 = I8 ? P.q_bf16 != 0 : KV == KV_BF16;
+            const uint16_t *pb = reinterpret_cast<const uint16_t *>(P.pse) + (P.pse_sB ? b * P.pse_sB : 0);
+#pragma unroll
+            for (int hh = 0; hh < PH; hh++) {
+                const int hq = SCATTER ? hl : hh;
+                prow[hh] = pb + (int64_t)(hbase + (hg * G + hq < P.g ? hq : 0)) * P.pse_sH;
+            }
+        }
 
         // Rolling pipeline with one tile resident: the K rows of tile k+1 are
         // requested as soon as QK of tile k has consumed the K registers, and
@@ -309,6 +334,7 @@ void split_kernel(const SplitParams P) {
         uint32_t kr[RT][W], vr[RT][W];
         bool okr[RT];
         uint32_t mbr[MB];       // mask byte of position ts + lane (per head for per-head masks)
+        uint32_t pbr[PR][PH];   // pseShift bits: scatter path of ts + i*RPI + r, else of ts + lane
         int64_t offs[RT];       // paged: byte offsets of the tile's rows
 
         auto load_rows = [&](const char *const (&ptr)[RT], uint32_t (&dst)[RT][W]) {
@@ -355,7 +381,7 @@ void split_kernel(const SplitParams P) {
 #pragma unroll
                 for (int hh = 0; hh < MB; hh++) {
                     // shared mask: only entry 0; per-head mask: one byte per real head
-                    const bool want = lane < TT && (P.mask_mode == 2 ? hg * G + hh < P.g : hh == 0);
+                    const bool want = lane < TT && (P.mask_mode == 2 ? hg * G + hh < P.g : P.mask_mode == 1 && hh == 0);
                     uint32_t v = 0;
                     if (want) v = mrow[(int64_t)hh * P.mask_sH + tm];
                     mbr[hh] = v;
@@ -364,6 +390,19 @@ void split_kernel(const SplitParams P) {
             const char *ptr[RT];
             row_ptrs(ts, PAGED ? kb : kp, ptr);
             load_rows(ptr, kr);
+        };
+        auto issue_pse = [&](int ts) {
+            if constexpr (PSE && SCATTER) {
+#pragma unroll
+                for (int i = 0; i < RT; i++) pbr[i][0] = prow[0][min(ts + i * RPI + r, hi - 1)];
+            } else if constexpr (PSE) {
+                const int t = min(ts + lane, hi - 1);
+#pragma unroll
+                for (int hh = 0; hh < PH; hh++) pbr[0][hh] = lane < TT ? prow[hh][t] : 0u;
+            }
+        };
+        auto pse_log2 = [&](uint32_t bits) {
+            return (pse_bf16 ? bf16_to_f32(bits) : f16_to_f32(bits)) * kLog2e;
         };
         auto issue_v = [&](int ts) {
             const char *ptr[RT];
@@ -385,6 +424,7 @@ void split_kernel(const SplitParams P) {
         int ts = lo;
         issue_k(ts);
         issue_v(ts);
+        issue_pse(ts);
         while (true) {
             // QK: partial dot products of the resident K rows, then the DPP
             // reductions one step at a time across all rows and heads
@@ -487,7 +527,9 @@ void split_kernel(const SplitParams P) {
                     const int pos = i * RPI + r;
                     bool keep = ts + pos < hi && okc[i];
                     if constexpr (MASKED) keep = keep && !((mbl >> pos) & 1);
-                    x[i] = keep ? x[i] * qmul : kNegInf;
+                    float xs = x[i] * qmul;
+                    if constexpr (PSE) xs += pse_log2(pbr[i][0]);
+                    x[i] = keep ? xs : kNegInf;
                     mt = fmaxf(mt, x[i]);
                 }
                 const bool raise = mt > m1 + kLazy;
@@ -521,7 +563,9 @@ void split_kernel(const SplitParams P) {
                     for (int hh = 0; hh < G; hh++) {
                         bool keep = in;
                         if constexpr (MASKED) keep = keep && !((mbits[hh] >> pos) & 1);
-                        s[i][hh] = keep ? s[i][hh] * qmul : kNegInf;
+                        float xs = s[i][hh] * qmul;
+                        if constexpr (PSE) xs += pse_log2((uint32_t)__shfl((int)pbr[0][hh], pos));
+                        s[i][hh] = keep ? xs : kNegInf;
                     }
                 }
                 // online softmax (log2 domain) with a lazily raised maximum
@@ -556,6 +600,8 @@ void split_kernel(const SplitParams P) {
                     l[hh] += ls;
                 }
             }
+            // the next tile's bias is read while this tile's P.V runs
+            if (more) issue_pse(ts + TT);
             // P.V over pairs of row steps (two positions per dot2)
 #pragma unroll
             for (int i = 0; i < RT; i += 2) {
@@ -629,46 +675,61 @@ void split_kernel(const SplitParams P) {
     }   // segments
 }
 
-template <int KV, int D, int G, bool PAGED, bool MASKED>
+using SplitFn = void (*)(const SplitParams);
+
+template <int KV, int D, int G, bool PAGED>
+SplitFn pick_extra(int extra) {
+    return extra == EX_PSE ? split_kernel<KV, D, G, PAGED, EX_PSE>
+         : extra == EX_MASK ? split_kernel<KV, D, G, PAGED, EX_MASK>
+                            : split_kernel<KV, D, G, PAGED, EX_NONE>;
+}
+
+template <int KV, int D, int G>
+const void *ptr_pm(bool paged, int extra) {
+    return reinterpret_cast<const void *>(paged ? pick_extra<KV, D, G, true>(extra)
+                                                : pick_extra<KV, D, G, false>(extra));
+}
+
+template <int KV, int D, int G, bool PAGED, int EXTRA>
 hipError_t launch_one(const SplitParams &p, hipStream_t s) {
     const int blocks = (p.n_pieces + kWavesPerBlock - 1) / kWavesPerBlock;
-    hipLaunchKernelGGL((split_kernel<KV, D, G, PAGED, MASKED>), dim3(blocks), dim3(64 * kWavesPerBlock), 0, s, p);
+    hipLaunchKernelGGL((split_kernel<KV, D, G, PAGED, EXTRA>), dim3(blocks), dim3(64 * kWavesPerBlock), 0, s, p);
     return hipGetLastError();
 }
 
-template <int KV, int D, int G>
-hipError_t launch_pm(const SplitParams &p, bool paged, bool masked, hipStream_t s) {
-    if (paged) return masked ? launch_one<KV, D, G, true, true>(p, s) : launch_one<KV, D, G, true, false>(p, s);
-    return masked ? launch_one<KV, D, G, false, true>(p, s) : launch_one<KV, D, G, false, false>(p, s);
+template <int KV, int D, int G, bool PAGED>
+hipError_t launch_ex(const SplitParams &p, int extra, hipStream_t s) {
+    switch (extra) {
+    case EX_NONE: return launch_one<KV, D, G, PAGED, EX_NONE>(p, s);
+    case EX_MASK: return launch_one<KV, D, G, PAGED, EX_MASK>(p, s);
+    case EX_PSE: return launch_one<KV, D, G, PAGED, EX_PSE>(p, s);
+    }
+    return hipErrorInvalidValue;
 }
 
 template <int KV, int D, int G>
-const void *ptr_pm(bool paged, bool masked) {
-    void (*fp)(const SplitParams) = paged ? (masked ? split_kernel<KV, D, G, true, true>
-                                                    : split_kernel<KV, D, G, true, false>)
-                                          : (masked ? split_kernel<KV, D, G, false, true>
-                                                    : split_kernel<KV, D, G, false, false>);
-    return reinterpret_cast<const void *>(fp);
+hipError_t launch_pm(const SplitParams &p, bool paged, int extra, hipStream_t s) {
+    return paged ? launch_ex<KV, D, G, true>(p, extra, s) : launch_ex<KV, D, G, false>(p, extra, s);
 }
 
 template <int KV, int D>
-hipError_t launch_g(const SplitParams &p, int G, bool paged, bool masked, hipStream_t s) {
+hipError_t launch_g(const SplitParams &p, int G, bool paged, int extra, hipStream_t s) {
     switch (G) {
-    case 1: return launch_pm<KV, D, 1>(p, paged, masked, s);
-    case 2: return launch_pm<KV, D, 2>(p, paged, masked, s);
-    case 4: return launch_pm<KV, D, 4>(p, paged, masked, s);
-    case 8: return launch_pm<KV, D, 8>(p, paged, masked, s);
+    case 1: return launch_pm<KV, D, 1>(p, paged, extra, s);
+    case 2: return launch_pm<KV, D, 2>(p, paged, extra, s);
+    case 4: return launch_pm<KV, D, 4>(p, paged, extra, s);
+    case 8: return launch_pm<KV, D, 8>(p, paged, extra, s);
     }
     return hipErrorInvalidValue;
 }
 
 template <int KV, int D>
-const void *ptr_g(int G, bool paged, bool masked) {
+const void *ptr_g(int G, bool paged, int extra) {
     switch (G) {
-    case 1: return ptr_pm<KV, D, 1>(paged, masked);
-    case 2: return ptr_pm<KV, D, 2>(paged, masked);
-    case 4: return ptr_pm<KV, D, 4>(paged, masked);
-    case 8: return ptr_pm<KV, D, 8>(paged, masked);
+    case 1: return ptr_pm<KV, D, 1>(paged, extra);
+    case 2: return ptr_pm<KV, D, 2>(paged, extra);
+    case 4: return ptr_pm<KV, D, 4>(paged, extra);
+    case 8: return ptr_pm<KV, D, 8>(paged, extra);
     }
     return nullptr;
 }
@@ -676,25 +737,25 @@ const void *ptr_g(int G, bool paged, bool masked) {
 }  // namespace split_detail
 
 template <int KV>
-hipError_t launch_split_kv(const SplitParams &p, int D, int G, bool paged, bool masked, hipStream_t s) {
+hipError_t launch_split_kv(const SplitParams &p, int D, int G, bool paged, int extra, hipStream_t s) {
     using namespace split_detail;
     switch (D) {
-    case 64: return launch_g<KV, 64>(p, G, paged, masked, s);
-    case 128: return launch_g<KV, 128>(p, G, paged, masked, s);
-    case 256: return launch_g<KV, 256>(p, G, paged, masked, s);
-    case 512: return launch_g<KV, 512>(p, G, paged, masked, s);
+    case 64: return launch_g<KV, 64>(p, G, paged, extra, s);
+    case 128: return launch_g<KV, 128>(p, G, paged, extra, s);
+    case 256: return launch_g<KV, 256>(p, G, paged, extra, s);
+    case 512: return launch_g<KV, 512>(p, G, paged, extra, s);
     }
     return hipErrorInvalidValue;
 }
 
 template <int KV>
-const void *split_kernel_ptr(int D, int G, bool paged, bool masked) {
+const void *split_kernel_ptr(int D, int G, bool paged, int extra) {
     using namespace split_detail;
     switch (D) {
-    case 64: return ptr_g<KV, 64>(G, paged, masked);
-    case 128: return ptr_g<KV, 128>(G, paged, masked);
-    case 256: return ptr_g<KV, 256>(G, paged, masked);
-    case 512: return ptr_g<KV, 512>(G, paged, masked);
+    case 64: return ptr_g<KV, 64>(G, paged, extra);
+    case 128: return ptr_g<KV, 128>(G, paged, extra);
+    case 256: return ptr_g<KV, 256>(G, paged, extra);
+    case 512: return ptr_g<KV, 512>(G, paged, extra);
     }
     return nullptr;
 }

@@ -13,6 +13,10 @@ constexpr int kWavesPerBlock = 4;
 
 enum KvKind { KV_F16 = 0, KV_BF16 = 1, KV_I8 = 2 };
 
+// Optional score terms of a split kernel variant: none, attenMask, or
+// pseShift (with attenMask, when present, checked at run time).
+enum SplitExtra { EX_NONE = 0, EX_MASK = 1, EX_PSE = 2 };
+
 // Arguments of the split-KV decode kernel.
 //
 // Work is balanced exactly: the rows (b, kv head j, head group hg), each of
@@ -28,11 +32,13 @@ struct SplitParams {
     float *part_acc;        // [slots][G][D]  unnormalised sum p*v
     float *part_ml;         // [slots][G][2]  running max (log2 domain), sum p
     const uint8_t *mask;    // nullptr when absent
+    const void *pse;        // pseShift [pse_batch, N, 1, pse_seq], query dtype; nullptr when absent
     const int32_t *block_table;
     const void *k_scale;    // int8 only: antiquant scale, q dtype
     int64_t sB, sN, sS;     // dense element strides of (b, j, s)
     int64_t blk_stride, head_stride, row_stride;   // paged element strides
     int64_t mask_sB, mask_sH;                      // mask strides (0 = broadcast)
+    int64_t pse_sB, pse_sH;                        // pseShift strides (pse_sB 0 = broadcast)
     int64_t total;          // positions over all rows of the slice
     int64_t piece;          // positions per wave
     int32_t n_pieces;
@@ -71,16 +77,16 @@ struct CombineParams {
     int32_t maxseg[kSliceBatches];
 };
 
-hipError_t launch_split(const SplitParams &p, int kv, int D, int G, bool paged, bool masked, hipStream_t s);
+hipError_t launch_split(const SplitParams &p, int kv, int D, int G, bool paged, int extra, hipStream_t s);
 hipError_t launch_combine(const CombineParams &p, hipStream_t s);
 
 // Resident waves of the split kernel for this shape (occupancy query).
-int split_resident_waves(int kv, int D, int G, bool paged, bool masked);
+int split_resident_waves(int kv, int D, int G, bool paged, int extra);
 
 // Per-KV-dtype kernel sets (one translation unit each).
 template <int KV>
-hipError_t launch_split_kv(const SplitParams &p, int D, int G, bool paged, bool masked, hipStream_t s);
+hipError_t launch_split_kv(const SplitParams &p, int D, int G, bool paged, int extra, hipStream_t s);
 template <int KV>
-const void *split_kernel_ptr(int D, int G, bool paged, bool masked);
+const void *split_kernel_ptr(int D, int G, bool paged, int extra);
 
 }  // namespace ifa

@@ -32,7 +32,7 @@ def call(dev: dict, out: torch.Tensor, split: int = 0, workspace=None, stream=No
                                       workspace=workspace, stream=stream)
     assert isinstance(s, IfaSpec)
     common = dict(num_heads=s.N, num_key_value_heads=s.Nkv, input_layout=s.layout, scale_value=s.scale_value,
-                  actual_seq_lengths=dev["actual_seq_lengths"], atten_mask=dev["mask"],
+                  actual_seq_lengths=dev["actual_seq_lengths"], atten_mask=dev["mask"], pse_shift=dev.get("pse"),
                   antiquant_scale=dev["aq_scale"], antiquant_offset=dev["aq_offset"], antiquant_mode=dev["aq_mode"],
                   split_tokens=split, workspace=workspace, stream=stream)
     if s.paged:

@@ -335,6 +335,10 @@ def workloads() -> dict:
                                     S=32768, len_range=(4096, 32768), pad_off=(0, 64), antiquant="per_channel",
                                     scale=s128),
         "sfa_mla_bf16": SfaSpec("sfa_mla_bf16", 5),
+        # the dense GQA workload with a per-batch positional bias (pseShift) of N(0, 4)
+        "dense_pse_bf16_bsh": IfaSpec("dense_pse_bf16_bsh", 6, "bf16", "bf16", B=64, N=32, Nkv=8, D=128,
+                                      layout="BSH", S=8192, len_range=(1024, 8192), scale=s128, pse=True,
+                                      pse_scale=2.0),
     }
 
 

@@ -102,7 +102,16 @@ enum { IFA_ANTIQUANT_NONE = 0, IFA_ANTIQUANT_PER_TENSOR = 1, IFA_ANTIQUANT_PER_C
  *   per-channel (2,N_kv,1,D) (equivalently (2,N_kv,D) or (2,H)).  Required
  *   when dtype_kv is IFA_DT_I8, forbidden otherwise (README "Constraints >
  *   antiquantScale and antiquantOffset").
- * pse_shift must be NULL (positional bias is not implemented).
+ * pse_shift: device, dtype_q, shape (pse_batch, N, 1, pse_seq) contiguous,
+ *   pse_batch in {1,B} (1 = shared by every batch), pse_seq >= every position
+ *   attended; NULL for none.  pse_shift[b][h][0][s] is added to the scaled
+ *   score of query head h at cache position s, after scale_value and before
+ *   the softmax, at the position coordinate the mask uses: the physical
+ *   cache position here (IncreFlashAttention README "Formula" and
+ *   "Constraints"; the placement after the scale is this library's reading).
+ *   -inf excludes a position like a mask byte.  pse_batch and pse_seq are the
+ *   two last fields of the struct; a struct_size that stops before them means
+ *   no positional bias (pse_shift must then be NULL).
  * Envelope: 1 <= B <= 65536, 1 <= N <= 256, N % N_kv == 0,
  *   head_dim in {64, 128, 256, 512}, dtype_out == dtype_q, dtype_kv ==
  *   dtype_q or IFA_DT_I8.
@@ -136,6 +145,7 @@ typedef struct ifa_decode_args {
     int64_t split_tokens;
     void *profile_event_begin; /* optional hipEvent_t recorded right before the split kernel */
     void *profile_event_end;   /* optional hipEvent_t recorded right after it (both or neither) */
+    int64_t pse_batch, pse_seq; /* pse_shift shape (pse_batch, N, 1, pse_seq) */
 } ifa_decode_args;
 
 /*
@@ -151,7 +161,8 @@ typedef struct ifa_decode_args {
  * actual_seq_lengths: host int64[batch], required, 0 <= L_b <=
  *   max_blocks_per_seq * block_size.
  * block_size: 16..512, a multiple of 16 (fp16/bf16) or of 32 (int8).
- * atten_mask indexes the logical position; mask_seq >= max L_b.
+ * atten_mask and pse_shift index the logical position; mask_seq and
+ *   pse_seq >= max L_b.
  * Left padding is not combined with paging (IFA_ERR_PARAM_INVALID).
  */
 typedef struct ifa_paged_args {
@@ -178,6 +189,7 @@ typedef struct ifa_paged_args {
     int64_t split_tokens;
     void *profile_event_begin; /* as in ifa_decode_args */
     void *profile_event_end;
+    int64_t pse_batch, pse_seq; /* as in ifa_decode_args */
 } ifa_paged_args;
 
 /*

@@ -105,7 +105,10 @@ PADS1 = (ctypes.c_int64 * 1)(3)
     (dict(scale_value=float("nan")), 161002),
     (dict(actual_seq_lengths=ctypes.cast(BAD_LENS, ctypes.c_void_p)), 161002),
     (dict(kv_padding_size=ctypes.cast(PADS1, ctypes.c_void_p), kv_padding_size_count=3), 161002),
-    (dict(pse_shift=FAKE), 161002),
+    (dict(pse_shift=FAKE), 161002),                               # pse_batch 0
+    (dict(pse_shift=FAKE, pse_batch=3, pse_seq=64), 161002),      # pse_batch not in {1, B}
+    (dict(pse_shift=FAKE, pse_batch=2, pse_seq=63), 161002),      # shorter than the attended range
+    (dict(pse_shift=FAKE, pse_batch=1, pse_seq=64, struct_size=ctypes.sizeof(bd.IfaDecodeArgs) - 16), 161002),
     (dict(atten_mask=FAKE, dtype_mask=bd.DT_F16, mask_batch=2, mask_heads=1, mask_seq=64), 161002),
     (dict(atten_mask=FAKE, dtype_mask=bd.DT_BOOL, mask_batch=3, mask_heads=1, mask_seq=64), 161002),
     (dict(atten_mask=FAKE, dtype_mask=bd.DT_BOOL, mask_batch=2, mask_heads=4, mask_seq=64), 161002),
@@ -257,3 +260,22 @@ def test_sfa_workspace_holds_chunk_outputs_in_input_dtype():
     assert rc == 0 and n == 2 * 2 * 16 * 512 * 2 + 2 * 2 * 16 * 2 * 4
     rc, n = ws_size("sfa_decode_mla_workspace_size", sfa_args(split_hint=1))
     assert rc == 0 and n == 0
+
+
+@pytest.mark.parametrize("kw", [
+    dict(pse_shift=FAKE, pse_batch=2, pse_seq=64),
+    dict(pse_shift=FAKE, pse_batch=1, pse_seq=100),
+    dict(pse_shift=FAKE, pse_batch=1, pse_seq=64, actual_seq_lengths=ctypes.cast(LENS, ctypes.c_void_p)),
+    dict(struct_size=ctypes.sizeof(bd.IfaDecodeArgs) - 16),        # a struct without the pse dims
+])
+def test_dense_positional_bias_accepted(kw):
+    assert ws_size("ifa_decode_workspace_size", dense_args(**kw))[0] == 0
+
+
+def test_paged_positional_bias_checks():
+    assert ws_size("ifa_decode_paged_workspace_size", paged_args(pse_shift=FAKE, pse_batch=2, pse_seq=100))[0] == 0
+    # lengths (100, 64): logical positions up to 99 need a bias
+    assert ws_size("ifa_decode_paged_workspace_size", paged_args(pse_shift=FAKE, pse_batch=2, pse_seq=99))[0] \
+        == 161002
+    assert ws_size("ifa_decode_paged_workspace_size", paged_args(pse_shift=FAKE, pse_batch=4, pse_seq=100))[0] \
+        == 161002

@@ -11,7 +11,8 @@ from gpu_util import compare, run_gpu, say
 
 pytestmark = pytest.mark.gpu
 
-IFA_WORKLOADS = ["tiny_dense_f16", "dense_gqa_bf16_bsh", "paged_bf16_bs128", "int8_leftpad_f16"]
+IFA_WORKLOADS = ["tiny_dense_f16", "dense_gqa_bf16_bsh", "paged_bf16_bs128", "int8_leftpad_f16",
+                 "dense_pse_bf16_bsh"]
 
 
 @pytest.mark.parametrize("name", IFA_WORKLOADS)

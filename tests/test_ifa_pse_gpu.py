@@ -1,0 +1,97 @@
+"""pseShift (additive positional bias) on the GPU against the fp64 oracle.
+
+The bias pse[b|0, h, 0, s] is added to the scaled score of head h at cache
+position s (IncreFlashAttention README "Formula"); the kernels read it at the
+position coordinate the mask uses (physical for dense caches, logical for
+paged ones)."""
+from dataclasses import replace
+
+import pytest
+import torch
+
+from decode_attention_kv_06_amd.workloads import IfaSpec, make_ifa, workloads
+from gpu_util import compare, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+# G (heads per KV head, rounded up to 1/2/4/8) picks the kernel path: G = 1 or
+# D = 64 reduce every head in every lane, the others reduce-scatter the heads.
+@pytest.mark.parametrize("D", [64, 128, 256, 512])
+@pytest.mark.parametrize("N,Nkv", [(4, 4), (8, 4), (8, 2), (16, 2), (20, 4)])
+def test_pse_dense_head_dims_and_groups(D, N, Nkv):
+    k = D // 64 + N
+    mask = [None, "u8", "bool"][k % 3]
+    spec = IfaSpec("pse_dense", 400 + k, ["f16", "bf16"][k % 2], ["f16", "bf16"][k % 2], B=3, N=N, Nkv=Nkv, D=D,
+                   layout=["BSH", "BNSD", "BSND"][k % 3], S=333, len_range=(1, 333), mask=mask, mask_p=0.15,
+                   mask_heads=N if k % 2 else 1, pse=True, pse_batch=k % 2, pse_scale=2.0)
+    inp = make_ifa(spec)
+    out, _ = run_gpu(inp)
+    compare(inp, out)
+
+
+@pytest.mark.parametrize("split", [16, 48, 0])
+def test_pse_forced_splits(split):
+    spec = IfaSpec("pse_split", 420, "bf16", "bf16", B=2, N=16, Nkv=2, D=128, layout="BNSD", S=900,
+                   len_range=(100, 900), pse=True, pse_scale=4.0)
+    inp = make_ifa(spec)
+    out, _ = run_gpu(inp, split=split)
+    compare(inp, out)
+
+
+@pytest.mark.parametrize("layout,cache_layout", [("BNSD", 0), ("BSH", 1)])
+@pytest.mark.parametrize("bs", [16, 128])
+@pytest.mark.parametrize("pse_batch", [0, 1])
+def test_pse_paged_logical_positions(layout, cache_layout, bs, pse_batch):
+    spec = IfaSpec("pse_paged", 430 + bs, "bf16", "bf16", B=3, N=8, Nkv=2, D=128, layout=layout, S=0,
+                   len_range=(1, 6 * bs), paged=True, block_size=bs, max_blocks=6, num_blocks=40,
+                   cache_layout=cache_layout, pse=True, pse_batch=pse_batch, pse_scale=2.0)
+    inp = make_ifa(spec)
+    out, _ = run_gpu(inp)
+    compare(inp, out)
+
+
+@pytest.mark.parametrize("qdt", ["f16", "bf16"])
+def test_pse_int8_left_padding(qdt):
+    spec = IfaSpec("pse_aq", 440, qdt, "i8", B=3, N=16, Nkv=2, D=128, layout="BNSD", S=700, len_range=(1, 680),
+                   antiquant="per_channel", pad_off=(0, 20), pse=True, pse_scale=2.0)
+    inp = make_ifa(spec)
+    out, _ = run_gpu(inp)
+    compare(inp, out)
+
+
+def test_pse_minus_infinity_excludes_like_the_mask():
+    spec = IfaSpec("pse_inf", 450, "f16", "f16", B=3, N=8, Nkv=2, D=128, layout="BNSD", S=400,
+                   len_range=(50, 400), mask="bool", mask_p=0.4, mask_heads=8, pse=True)
+    inp = make_ifa(spec)
+    as_bias = dict(inp)
+    as_bias["pse"] = torch.where(inp["mask"].to(torch.bool), torch.tensor(float("-inf"), dtype=torch.float16),
+                                 inp["pse"]).contiguous()
+    as_bias["mask"] = None
+    out, _ = run_gpu(as_bias)
+    compare(as_bias, out)
+    out_m, _ = run_gpu(inp)
+    assert (out.float() - out_m.float()).abs().max().item() <= 5e-3
+
+
+def test_zero_pse_gives_the_bytes_of_no_pse_at_a_fixed_split():
+    spec = IfaSpec("pse_zero", 451, "bf16", "bf16", B=2, N=16, Nkv=2, D=128, layout="BSH", S=500,
+                   len_range=(1, 500), pse=True)
+    inp = make_ifa(spec)
+    zero = dict(inp)
+    zero["pse"] = torch.zeros_like(inp["pse"])
+    plain = dict(inp)
+    plain["pse"] = None
+    a, _ = run_gpu(zero, split=64)
+    b, _ = run_gpu(plain, split=64)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("name", ["dense_gqa_bf16_bsh", "paged_bf16_bs128"])
+def test_pse_full_size_workload_sampled_rows(name):
+    spec = replace(workloads()[name], pse=True, pse_scale=2.0)
+    inp = make_ifa(spec)
+    out, _ = run_gpu(inp)
+    n = spec.B * spec.N
+    rows = sorted(set([0, 1, n // 2, n - 1] + list(range(7, n, max(1, n // 61)))))
+    compare(inp, out, rows=rows)
