@@ -97,13 +97,13 @@ typedef double (*vfetch_fn)(const void *ctx, int64_t i, int64_t d);
 
 static void softmax_combine(const double *x, int64_t n, int64_t D, vfetch_fn vrow, const void *ctx,
                             double *w, double *out) {
-    if (n == 0) {
-        for (int64_t d = 0; d < D; d++) out[d] = 0.0;
-        return;
-    }
     double m = -INFINITY;
     for (int64_t i = 0; i < n; i++)
         if (x[i] > m) m = x[i];
+    if (n == 0 || m == -INFINITY) {      /* nothing attended (every score -inf counts as none) */
+        for (int64_t d = 0; d < D; d++) out[d] = 0.0;
+        return;
+    }
     double z = 0.0;
     for (int64_t i = 0; i < n; i++) {
         w[i] = exp(x[i] - m);

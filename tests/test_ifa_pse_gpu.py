@@ -95,3 +95,15 @@ def test_pse_full_size_workload_sampled_rows(name):
     n = spec.B * spec.N
     rows = sorted(set([0, 1, n // 2, n - 1] + list(range(7, n, max(1, n // 61)))))
     compare(inp, out, rows=rows)
+
+
+def test_pse_minus_infinity_on_a_whole_row_gives_zeros():
+    spec = IfaSpec("pse_allinf", 452, "bf16", "bf16", B=3, N=8, Nkv=2, D=128, layout="BNSD", S=300,
+                   len_range=(20, 300), pse=True)
+    inp = make_ifa(spec)
+    p = inp["pse"].clone()
+    p[1, 3] = float("-inf")
+    inp["pse"] = p
+    out, _ = run_gpu(inp)
+    assert (out[1, 3].float() == 0).all()
+    compare(inp, out)

@@ -437,3 +437,15 @@ def test_pse_shorter_than_attended_range_is_rejected():
     short["pse"] = inp["pse"][..., :20].contiguous()
     with pytest.raises(ValueError):
         oracle.ifa(short)
+
+
+def test_bias_of_minus_infinity_everywhere_is_an_empty_set():
+    spec = IfaSpec("pin", 937, "f16", "f16", B=2, N=2, Nkv=1, D=8, S=20, len_range=(5, 20), pse=True)
+    inp = make_ifa(spec)
+    allinf = dict(inp)
+    p = inp["pse"].clone()
+    p[0] = float("-inf")
+    allinf["pse"] = p
+    out = oracle.ifa(allinf)
+    assert (out[0] == 0).all() and np.isfinite(out).all()
+    np.testing.assert_allclose(out[1], oracle.ifa(inp)[1], rtol=0, atol=0)
