@@ -267,6 +267,15 @@ class SfaSpec:
     value_aliases_key: bool = False
     scale: float = 0.0                    # 0 -> float32(1/sqrt(D + DR))
     sparse_mode: int = 0
+    # breadth beyond one query row over a paged cache
+    QS: int = 1                           # query rows per batch (BSND query)
+    lq: Optional[Sequence[int]] = None    # valid query rows per batch (None: QS each)
+    pass_lq: bool = False                 # hand actual_seq_lengths_query over even when it is all QS
+    layout_q: str = "BSND"                # "BSND" | "TND" (rows packed, lq as prefix sums)
+    layout_kv: str = "PA_BSND"            # "PA_BSND" | "BSND" | "TND"
+    kv_seq: int = 0                       # KV_S of a BSND cache (0: the largest length)
+    sparse_block_size: int = 1            # positions named by one index
+    past_limit: bool = False              # also select positions past the causal limit
 
     @property
     def scale_value(self) -> float:
@@ -275,44 +284,99 @@ class SfaSpec:
 
 
 def make_sfa(spec: SfaSpec) -> dict:
+    """Host tensors for one SFA call.  Query rows are enumerated batch by batch
+    (BSND: QS per batch, padding rows included; TND: the valid rows only);
+    each row draws its own index list: distinct blocks of sparse_block_size
+    positions, from below the row's causal limit under sparse_mode 3 (below
+    the kv length with ``past_limit``), valid ones first, then -1."""
     B, QN, D, DR, bs = spec.B, spec.QN, spec.D, spec.DR, spec.block_size
+    sbs = spec.sparse_block_size
     k_id = spec.cfg_id
     out: dict = {"spec": spec}
-    out["q"] = normal_tensor(rng_for(k_id, TID_Q), (B, 1, QN, D), spec.dtype)
-    out["q_rope"] = normal_tensor(rng_for(k_id, TID_QROPE), (B, 1, QN, DR), spec.dtype)
-    out["key"] = normal_tensor(rng_for(k_id, TID_K), (spec.num_blocks, bs, 1, D), spec.dtype)
-    out["key_rope"] = normal_tensor(rng_for(k_id, TID_KROPE), (spec.num_blocks, bs, 1, DR), spec.dtype)
-    out["value"] = out["key"] if spec.value_aliases_key else normal_tensor(
-        rng_for(k_id, TID_V), (spec.num_blocks, bs, 1, D), spec.dtype)
     if spec.lkv is not None:
         lkv = np.asarray(spec.lkv, dtype=np.int64)
     else:
         lkv = rng_for(k_id, TID_LEN).integers(spec.lkv_range[0], spec.lkv_range[1], size=B, endpoint=True)
-    if int(lkv.max(initial=0)) > spec.max_blocks * bs:
-        raise ValueError("lkv exceeds the block table's reach")
-    perm = rng_for(k_id, TID_PERM).permutation(spec.num_blocks)
-    if spec.num_blocks >= B * spec.max_blocks:
-        bt = perm[: B * spec.max_blocks].reshape(B, spec.max_blocks)
+    lq = np.asarray(spec.lq if spec.lq is not None else [spec.QS] * B, dtype=np.int64)
+    if (lq < 0).any() or (spec.layout_q == "BSND" and (lq > spec.QS).any()):
+        raise ValueError("query lengths outside [0, QS]")
+    # query row -> (batch, position in the batch's query)
+    if spec.layout_q == "TND":
+        rows_b = np.repeat(np.arange(B), lq)
+        rows_s = np.concatenate([np.arange(n) for n in lq]) if B else np.zeros(0, np.int64)
     else:
-        bt = perm[np.arange(B * spec.max_blocks) % spec.num_blocks].reshape(B, spec.max_blocks)
-    out["block_table"] = torch.from_numpy(np.ascontiguousarray(bt.astype(np.int32)))
+        rows_b = np.repeat(np.arange(B), spec.QS)
+        rows_s = np.tile(np.arange(spec.QS), B)
+    R = len(rows_b)
+    qshape = (R, QN) if spec.layout_q == "TND" else (B, spec.QS, QN)
+    out["q"] = normal_tensor(rng_for(k_id, TID_Q), qshape + (D,), spec.dtype)
+    out["q_rope"] = normal_tensor(rng_for(k_id, TID_QROPE), qshape + (DR,), spec.dtype)
+
+    if spec.layout_kv == "PA_BSND":
+        if int(lkv.max(initial=0)) > spec.max_blocks * bs:
+            raise ValueError("lkv exceeds the block table's reach")
+        kshape = (spec.num_blocks, bs, 1)
+    elif spec.layout_kv == "BSND":
+        kv_seq = spec.kv_seq or int(lkv.max(initial=1))
+        if int(lkv.max(initial=0)) > kv_seq:
+            raise ValueError("lkv exceeds KV_S")
+        kshape = (B, kv_seq, 1)
+        out["kv_seq"] = kv_seq
+    else:
+        kshape = (max(1, int(lkv.sum())), 1)
+    out["key"] = normal_tensor(rng_for(k_id, TID_K), kshape + (D,), spec.dtype)
+    out["key_rope"] = normal_tensor(rng_for(k_id, TID_KROPE), kshape + (DR,), spec.dtype)
+    out["value"] = out["key"] if spec.value_aliases_key else normal_tensor(
+        rng_for(k_id, TID_V), kshape + (D,), spec.dtype)
+    if spec.layout_kv == "PA_BSND":
+        perm = rng_for(k_id, TID_PERM).permutation(spec.num_blocks)
+        if spec.num_blocks >= B * spec.max_blocks:
+            bt = perm[: B * spec.max_blocks].reshape(B, spec.max_blocks)
+        else:
+            bt = perm[np.arange(B * spec.max_blocks) % spec.num_blocks].reshape(B, spec.max_blocks)
+        out["block_table"] = torch.from_numpy(np.ascontiguousarray(bt.astype(np.int32)))
+    else:
+        out["block_table"] = None
+
+    # per query row: the domain of positions it selects from and how many blocks it takes
+    limit = lkv[rows_b].copy()
+    if spec.sparse_mode == 3 and not spec.past_limit:
+        limit = np.minimum(limit, lkv[rows_b] - lq[rows_b] + rows_s + 1)
+    limit = np.maximum(limit, 0)
+    nblk_dom = (limit + sbs - 1) // sbs
     if spec.n_valid is not None:
         nval = np.asarray(spec.n_valid, dtype=np.int64)
+        nval = np.resize(nval, R) if len(nval) != R else nval
     else:
-        tails = rng_for(k_id, TID_NVALID).integers(spec.tail_range[0], spec.tail_range[1], size=B, endpoint=True)
+        tails = rng_for(k_id, TID_NVALID).integers(spec.tail_range[0], spec.tail_range[1], size=R, endpoint=True)
         nval = spec.sparse_size - tails
-    nval = np.minimum(np.maximum(nval, 0), np.minimum(spec.sparse_size, lkv))
-    idx = np.full((B, 1, 1, spec.sparse_size), -1, dtype=np.int32)
+    nval = np.minimum(np.maximum(nval, 0), np.minimum(spec.sparse_size, nblk_dom))
+    idx = np.full((R, spec.sparse_size), -1, dtype=np.int32)
     r = rng_for(k_id, TID_IDX)
-    for b in range(B):
-        n = int(nval[b])
+    for i in range(R):
+        n = int(nval[i])
         if n:
-            sel = r.choice(int(lkv[b]), size=n, replace=False)
+            sel = r.choice(int(nblk_dom[i]), size=n, replace=False)
             if spec.sorted_indices:
                 sel = np.sort(sel)
-            idx[b, 0, 0, :n] = sel
-    out["sparse_indices"] = torch.from_numpy(idx)
-    out["actual_seq_lengths_kv"] = torch.from_numpy(lkv.astype(np.int32))
+            idx[i, :n] = sel
+    if spec.layout_q == "TND":
+        out["sparse_indices"] = torch.from_numpy(idx.reshape(R, 1, spec.sparse_size))
+    else:
+        out["sparse_indices"] = torch.from_numpy(idx.reshape(B, spec.QS, 1, spec.sparse_size))
+    if spec.layout_kv == "TND":
+        out["actual_seq_lengths_kv"] = torch.from_numpy(np.cumsum(lkv).astype(np.int32))
+    else:
+        out["actual_seq_lengths_kv"] = torch.from_numpy(lkv.astype(np.int32))
+    if spec.layout_q == "TND":
+        out["actual_seq_lengths_query"] = torch.from_numpy(np.cumsum(lq).astype(np.int32))
+    elif spec.lq is not None or spec.pass_lq:
+        out["actual_seq_lengths_query"] = torch.from_numpy(lq.astype(np.int32))
+    else:
+        out["actual_seq_lengths_query"] = None
+    out["lkv_counts"] = lkv
+    out["lq_counts"] = lq
+    out["q_rows"] = R
     out["n_valid"] = nval
     return out
 

@@ -42,7 +42,8 @@ def bind(path: str) -> ctypes.CDLL:
     lb.oracle_ifa.argtypes = [P, I, P, P, I, I, I64, I64, I64, I64, I64, D, P, P, P, I64, I64, I64,
                                     P, I64, I64, I64, I, P, P, I, P, I64, P, P, I64, I64]
     lb.oracle_ifa.restype = I
-    lb.oracle_sfa.argtypes = [P, P, P, P, P, I, P, P, P, I64, I64, I64, I64, I64, I64, I64, I64, D, P, I64, P]
+    lb.oracle_sfa.argtypes = [P, P, P, P, P, I, P, P, P, P, I, I, I64, I64, I64, I64, I64, I64, I64, I64, I64, I64,
+                              I64, I, I64, D, P, I64, P]
     lb.oracle_sfa.restype = I
     lb.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
     lb.oracle_f16_to_f64.restype = D
@@ -107,23 +108,30 @@ def ifa(inp: dict, rows=None, scale=None, use=None) -> np.ndarray:
 
 
 def sfa(inp: dict, rows=None, use=None) -> np.ndarray:
-    """Exact SFA output [B, QN, D] (or [len(rows), D]) in float64."""
+    """Exact SFA output [query rows, QN, D] (or [len(rows), D]) in float64;
+    rows are (query row) * QN + head."""
     s = inp["spec"]
     key = inp["key"].contiguous()
     value = inp["value"].contiguous()
     rows_a = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
-    n = s.B * s.QN if rows is None else len(rows_a)
+    R = inp["q_rows"]
+    n = R * s.QN if rows is None else len(rows_a)
     out = np.empty((n, s.D), dtype=np.float64)
+    bt = inp["block_table"]
+    lq = inp["actual_seq_lengths_query"]
+    lay_q = {"BSND": 0, "TND": 1}[s.layout_q]
+    lay_kv = {"PA_BSND": 0, "BSND": 1, "TND": 2}[s.layout_kv]
     rc = (use or lib()).oracle_sfa(
         _ptr(inp["q"].contiguous()), _ptr(inp["q_rope"].contiguous()), _ptr(key),
         _ptr(inp["key_rope"].contiguous()), _ptr(value), DT[key.dtype],
-        _ptr(inp["sparse_indices"].contiguous()), _ptr(inp["block_table"].contiguous()),
-        _ptr(inp["actual_seq_lengths_kv"].contiguous()), s.B, s.QN, s.D, s.DR,
-        inp["sparse_indices"].shape[-1], s.block_size, key.shape[0], inp["block_table"].shape[1],
-        float(s.scale_value), _ptr(rows_a), n, _ptr(out))
+        _ptr(inp["sparse_indices"].contiguous()), _ptr(None if bt is None else bt.contiguous()),
+        _ptr(inp["actual_seq_lengths_kv"].contiguous()), _ptr(None if lq is None else lq.contiguous()),
+        lay_q, lay_kv, s.B, s.QS, R, s.QN, s.D, s.DR, inp["sparse_indices"].shape[-1], s.block_size,
+        key.shape[0] if lay_kv == 0 else 0, bt.shape[1] if bt is not None else 0, inp.get("kv_seq", 0),
+        int(s.sparse_mode), int(s.sparse_block_size), float(s.scale_value), _ptr(rows_a), n, _ptr(out))
     if rc != 0:
         raise ValueError("oracle_sfa rejected its input (code %d)" % rc)
-    return out.reshape(s.B, s.QN, s.D) if rows is None else out
+    return out.reshape(R, s.QN, s.D) if rows is None else out
 
 
 def f16_to_f64(bits: int) -> float:

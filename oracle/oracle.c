@@ -33,11 +33,18 @@
  *       out = softmax(q [K~]^T / sqrt(d_k)) V~
  *   where the rows of K~ and V~ are the cache rows named by sparse_indices,
  *   an index t being valid when 0 <= t < actual_seq_lengths_kv[b]; each row's
- *   score uses the 512-wide part plus the 64-wide rope part.
+ *   score uses the 512-wide part plus the 64-wide rope part.  Query layouts
+ *   BSND and TND, cache layouts PA_BSND, BSND and TND, several query rows per
+ *   batch with sparse_mode 3 (rightDownCausal), and block-wise selection
+ *   (sparse_block_size > 1: an index names sparse_block_size consecutive
+ *   positions) as the parameter table describes them.
  *
  * Readings where the pages are silent: an empty attention set gives a zero
  * row; duplicate sparse indices each count; sparse_mode 3 with one query row
- * equals mode 0.
+ * equals mode 0; the causal boundary of mode 3 puts query row s (of Lq) level
+ * with KV position Lkv - Lq + s; query rows past actual_seq_lengths_query
+ * give zero rows; a position past Lkv or the causal limit inside a selected
+ * block is left out.
  *
  * Parity unpinned (conventions the pages do not fix): the GQA head map
  * h -> h / (N / N_kv) and the antiquant form (x + offset) * scale.  The tests
@@ -247,44 +254,101 @@ static double sfa_vfetch(const void *c, int64_t i, int64_t d) {
 }
 
 /*
- * MLA-absorb sparse decode, query layout BSND with Q_S = 1, KV_N = 1, cache
- * layout PA_BSND.
- *   q [B,1,QN,D], q_rope [B,1,QN,DR], key/value [nblk,bs,1,D], key_rope [nblk,bs,1,DR]
- *   sparse_indices [B,1,1,sparse_size] int32; block_table [B,max_blocks] int32;
- *   lkv [B] int32 (valid iff 0 <= t < lkv[b]).
+ * MLA-absorb sparse attention (KV_N = 1), SparseFlashAttention README,
+ * "Formula" and parameter table.
+ *
+ * Query rows.  layout_q 0 = BSND: q [B, QS, QN, D], row (b, s); lq[b] (or QS
+ * when lq is NULL) of them are valid and the rest give zero rows.  layout_q
+ * 1 = TND: q [QT, QN, D]; lq holds prefix sums, batch b owning rows
+ * [lq[b-1], lq[b]).  q_rope, sparse_indices ([rows, sparse_size]) and the
+ * output follow the same row order.
+ *
+ * Cache.  layout_kv 0 = PA_BSND: [num_blocks, block_size, 1, D], position t
+ * of batch b in row block_table[b][t / block_size] * block_size + t %
+ * block_size; lkv[b] positions.  1 = BSND: [B, KV_S, 1, D], row b * KV_S +
+ * t; lkv[b] positions (KV_S when lkv is NULL).  2 = TND: [KV_T, 1, D]; lkv
+ * holds prefix sums, batch b owning rows [lkv[b-1], lkv[b]).
+ *
+ * Selection.  Entry i of row (b, s) names block idx = sparse_indices[...][i]
+ * of sparse_block_size positions, t = idx * sparse_block_size + u; a
+ * negative idx is invalid.  A position is attended when t < limit: limit =
+ * Lkv (sparse_mode 0), or min(Lkv, Lkv - Lq + s + 1) under sparse_mode 3
+ * (the causal boundary through the bottom-right corner of the Lq x Lkv
+ * score matrix).  Each occurrence of a repeated index counts.
+ *
  *   scale is the float32 scale value widened to double.
- *   rows: list of b*QN+h rows (NULL -> all); out has nrows*D doubles.
+ *   rows: list of (query row) * QN + head (NULL -> all); out has nrows*D doubles.
  */
 int oracle_sfa(const void *q, const void *q_rope, const void *key, const void *key_rope, const void *value,
                int dtype, const int32_t *sparse_indices, const int32_t *block_table, const int32_t *lkv,
-               int64_t B, int64_t QN, int64_t D, int64_t DR, int64_t sparse_size, int64_t block_size,
-               int64_t num_blocks, int64_t max_blocks, double scale, const int64_t *rows, int64_t nrows,
-               double *out) {
-    const int64_t total = rows ? nrows : B * QN;
+               const int32_t *lq, int layout_q, int layout_kv, int64_t B, int64_t QS, int64_t q_rows,
+               int64_t QN, int64_t D, int64_t DR, int64_t sparse_size, int64_t block_size, int64_t num_blocks,
+               int64_t max_blocks, int64_t kv_seq, int sparse_mode, int64_t sparse_block_size, double scale,
+               const int64_t *rows, int64_t nrows, double *out) {
+    if (layout_q != 0 && layout_q != 1) return -3;
+    if (layout_kv < 0 || layout_kv > 2) return -3;
+    if ((layout_q == 1 && !lq) || (layout_kv != 1 && !lkv) || sparse_block_size < 1) return -3;
+    const int64_t total = rows ? nrows : q_rows * QN;
     int err = 0;
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : err)
     for (int64_t r = 0; r < total; r++) {
-        const int64_t bh = rows ? rows[r] : r;
-        const int64_t b = bh / QN, h = bh % QN;
+        const int64_t rh = rows ? rows[r] : r;
+        const int64_t qr = rh / QN, h = rh % QN;
         double *o = out + r * D;
-        double *x = (double *)malloc(sizeof(double) * (size_t)sparse_size);
-        double *w = (double *)malloc(sizeof(double) * (size_t)sparse_size);
-        int64_t *ko = (int64_t *)malloc(sizeof(int64_t) * (size_t)sparse_size);
+        /* the query row's batch, its place in the batch, and the batch's query count */
+        int64_t b, s, Lq;
+        if (layout_q == 0) {
+            b = qr / QS;
+            s = qr % QS;
+            Lq = lq ? lq[b] : QS;
+        } else {
+            b = 0;
+            while (b < B && lq[b] <= qr) b++;
+            if (b == B) { err |= 1; continue; }
+            const int64_t start = b > 0 ? lq[b - 1] : 0;
+            s = qr - start;
+            Lq = lq[b] - start;
+        }
+        int64_t kv0 = 0, Lkv;
+        if (layout_kv == 2) {
+            kv0 = b > 0 ? lkv[b - 1] : 0;
+            Lkv = lkv[b] - kv0;
+        } else {
+            Lkv = lkv ? lkv[b] : kv_seq;
+            if (layout_kv == 1) kv0 = b * kv_seq;
+        }
+        int64_t limit = Lkv;
+        if (sparse_mode == 3 && Lkv - Lq + s + 1 < limit) limit = Lkv - Lq + s + 1;
+        if (s >= Lq) limit = 0;                       /* a padding query row: zero output */
+        const int64_t cap = sparse_size * sparse_block_size;
+        double *x = (double *)malloc(sizeof(double) * (size_t)cap);
+        double *w = (double *)malloc(sizeof(double) * (size_t)cap);
+        int64_t *ko = (int64_t *)malloc(sizeof(int64_t) * (size_t)cap);
         int64_t cnt = 0;
-        for (int64_t i = 0; i < sparse_size; i++) {
-            int64_t t = sparse_indices[b * sparse_size + i];
-            if (t < 0 || t >= lkv[b]) continue;
-            int64_t blk = block_table[b * max_blocks + t / block_size];
-            if (blk < 0 || blk >= num_blocks) { err |= 1; break; }
-            int64_t row = blk * block_size + t % block_size;
-            double dot = 0.0;
-            for (int64_t d = 0; d < D; d++)
-                dot += elem(q, dtype, (b * QN + h) * D + d) * elem(key, dtype, row * D + d);
-            for (int64_t d = 0; d < DR; d++)
-                dot += elem(q_rope, dtype, (b * QN + h) * DR + d) * elem(key_rope, dtype, row * DR + d);
-            x[cnt] = scale * dot;
-            ko[cnt] = row * D;
-            cnt++;
+        for (int64_t i = 0; i < sparse_size && !err; i++) {
+            const int64_t idx = sparse_indices[qr * sparse_size + i];
+            if (idx < 0) continue;
+            for (int64_t u = 0; u < sparse_block_size; u++) {
+                const int64_t t = idx * sparse_block_size + u;
+                if (t >= limit) continue;
+                int64_t row;
+                if (layout_kv == 0) {
+                    if (t / block_size >= max_blocks) continue;      /* past the table: invalid */
+                    int64_t blk = block_table[b * max_blocks + t / block_size];
+                    if (blk < 0 || blk >= num_blocks) { err |= 1; break; }
+                    row = blk * block_size + t % block_size;
+                } else {
+                    row = kv0 + t;
+                }
+                double dot = 0.0;
+                for (int64_t d = 0; d < D; d++)
+                    dot += elem(q, dtype, (qr * QN + h) * D + d) * elem(key, dtype, row * D + d);
+                for (int64_t d = 0; d < DR; d++)
+                    dot += elem(q_rope, dtype, (qr * QN + h) * DR + d) * elem(key_rope, dtype, row * DR + d);
+                x[cnt] = scale * dot;
+                ko[cnt] = row * D;
+                cnt++;
+            }
         }
         sfa_vctx c = {value, dtype, ko};
         softmax_combine(x, cnt, D, sfa_vfetch, &c, w, o);

@@ -13,7 +13,11 @@ import torch
 
 import oracle
 from decode_attention_kv_06_amd.workloads import IfaSpec, SfaSpec, make_ifa, make_sfa
+from dataclasses import replace
+
 from test_oracle_pins import _sfa_gather_ref, _sfa_small, dense_kv_bnsd, sdpa_ref, to64
+from test_oracle_sfa_breadth import _bsnd_from_paged, paged_rows, sdpa_rows
+from test_oracle_sfa_breadth import small as _sfa_breadth
 
 MUTANTS = {
     "gqa_mapping_modulo": ("j = h / g;", "j = h % Nkv;"),
@@ -30,10 +34,19 @@ MUTANTS = {
     "value_dequant_affine_other_way": ("v = (v + of) * sc;", "v = v * sc + of;"),
     "query_head_uses_kv_head": ("dot += elem(q, q_dtype, (b * N + h) * D + d) * kv;",
                                 "dot += elem(q, q_dtype, (b * N + j) * D + d) * kv;"),
-    "sfa_rope_dropped": ("dot += elem(q_rope, dtype, (b * QN + h) * DR + d) * elem(key_rope, dtype, row * DR + d);",
+    "sfa_rope_dropped": ("dot += elem(q_rope, dtype, (qr * QN + h) * DR + d) * elem(key_rope, dtype, row * DR + d);",
                          "(void)0;"),
-    "sfa_block_table_skipped": ("int64_t row = blk * block_size + t % block_size;", "int64_t row = t;"),
-    "sfa_length_bound_inclusive": ("if (t < 0 || t >= lkv[b]) continue;", "if (t < 0 || t > lkv[b]) continue;"),
+    "sfa_block_table_skipped": ("row = blk * block_size + t % block_size;", "row = t;"),
+    "sfa_length_bound_inclusive": ("if (t >= limit) continue;", "if (t > limit) continue;"),
+    "sfa_causal_off_by_one": ("if (sparse_mode == 3 && Lkv - Lq + s + 1 < limit) limit = Lkv - Lq + s + 1;",
+                              "if (sparse_mode == 3 && Lkv - Lq + s < limit) limit = Lkv - Lq + s;"),
+    "sfa_causal_top_left": ("if (sparse_mode == 3 && Lkv - Lq + s + 1 < limit) limit = Lkv - Lq + s + 1;",
+                            "if (sparse_mode == 3 && s + 1 < limit) limit = s + 1;"),
+    "sfa_padding_rows_attend": ("if (s >= Lq) limit = 0;", "(void)0;"),
+    "sfa_block_index_not_scaled": ("const int64_t t = idx * sparse_block_size + u;", "const int64_t t = idx + u;"),
+    "sfa_tnd_query_start_ignored": ("s = qr - start;", "s = qr;"),
+    "sfa_tnd_cache_start_ignored": ("kv0 = b > 0 ? lkv[b - 1] : 0;", "kv0 = 0;"),
+    "sfa_bsnd_cache_batch_stride": ("if (layout_kv == 1) kv0 = b * kv_seq;", "if (layout_kv == 1) kv0 = b;"),
 }
 
 
@@ -81,7 +94,88 @@ def _battery(lib):
     idx[0, 0, 0, 40:] = 200                      # == lkv[0]: must be ignored
     inp["sparse_indices"] = idx
     res.append(("sfa_bound", close(oracle.sfa(inp, use=lib), _sfa_gather_ref(inp))))
+    for name, fn in (("sfa_causal", _sfa_causal), ("sfa_block_wise", _sfa_block_wise), ("sfa_tnd_q", _sfa_tnd_q),
+                     ("sfa_tnd_kv", _sfa_tnd_kv), ("sfa_bsnd_kv", _sfa_bsnd_kv)):
+        try:
+            res.append((name, fn(lib, close)))
+        except ValueError:
+            res.append((name, False))
     return res
+
+
+def _sfa_causal(lib, close):
+    lq = [4, 2]
+    spec = _sfa_breadth(QS=4, lq=lq, sparse_mode=3, sparse_size=320, past_limit=True, lkv=[37, 300])
+    inp = make_sfa(spec)
+    idx = inp["sparse_indices"]
+    idx.fill_(-1)
+    for b, L in enumerate(spec.lkv):
+        idx[b, :, 0, :L] = torch.arange(L, dtype=torch.int32)
+    out = oracle.sfa(inp, use=lib)
+    ok = True
+    for b, L in enumerate(spec.lkv):
+        mask = torch.ones(lq[b], L, dtype=torch.bool).tril(diagonal=L - lq[b])
+        ref = sdpa_rows(inp, [b * 4 + s for s in range(lq[b])], paged_rows(inp, b, torch.arange(L)), mask)
+        ok &= close(out[b * 4:b * 4 + lq[b]], ref) and bool((out[b * 4 + lq[b]:b * 4 + 4] == 0).all())
+    return ok
+
+
+def _sfa_block_wise(lib, close):
+    sbs = 4
+    spec = _sfa_breadth(QS=2, lq=[2, 1], sparse_mode=3, sparse_block_size=sbs, sparse_size=24, lkv=[197, 317],
+                        past_limit=True)
+    inp = make_sfa(spec)
+    tok = dict(inp)
+    tok["spec"] = replace(spec, sparse_block_size=1, sparse_size=24 * sbs)
+    blk = inp["sparse_indices"].long()
+    exp = (blk[..., :, None] * sbs + torch.arange(sbs)).reshape(*blk.shape[:-1], -1)
+    exp[(blk < 0)[..., :, None].expand(*blk.shape, sbs).reshape(exp.shape)] = -1
+    tok["sparse_indices"] = exp.to(torch.int32).contiguous()
+    return close(oracle.sfa(inp, use=lib), oracle.sfa(tok, use=lib))
+
+
+def _sfa_tnd_q(lib, close):
+    lq = [3, 1, 0, 2]
+    spec = _sfa_breadth(B=4, QS=3, lq=lq, sparse_mode=3, lkv=[50, 60, 70, 80], num_blocks=40, max_blocks=10)
+    bsnd = make_sfa(spec)
+    ref = oracle.sfa(bsnd, use=lib)
+    valid = [b * 3 + s for b in range(4) for s in range(lq[b])]
+    tnd = dict(bsnd)
+    tnd["spec"] = replace(spec, layout_q="TND")
+    tnd["q"] = bsnd["q"].reshape(-1, spec.QN, spec.D)[valid].contiguous()
+    tnd["q_rope"] = bsnd["q_rope"].reshape(-1, spec.QN, spec.DR)[valid].contiguous()
+    tnd["sparse_indices"] = bsnd["sparse_indices"].reshape(-1, 1, spec.sparse_size)[valid].contiguous()
+    tnd["actual_seq_lengths_query"] = torch.tensor(np.cumsum(lq), dtype=torch.int32)
+    tnd["q_rows"] = len(valid)
+    return close(oracle.sfa(tnd, use=lib), ref[valid])
+
+
+def _sfa_tnd_kv(lib, close):
+    bsnd = _bsnd_from_paged(make_sfa(_sfa_breadth(QS=2, sparse_mode=0, lkv=[200, 317])))
+    s = bsnd["spec"]
+    tnd = dict(bsnd)
+    tnd["spec"] = replace(s, layout_kv="TND")
+    for name in ("key", "key_rope", "value"):
+        tnd[name] = torch.cat([bsnd[name][b, :s.lkv[b]] for b in range(s.B)], dim=0).contiguous()
+    tnd["actual_seq_lengths_kv"] = torch.tensor(np.cumsum(s.lkv), dtype=torch.int32)
+    return close(oracle.sfa(tnd, use=lib), _sfa_gather_ref_rows(bsnd))
+
+
+def _sfa_gather_ref_rows(bsnd):
+    """SDPA per query row over its valid positions of a BSND cache (mode 0)."""
+    s = bsnd["spec"]
+    out = np.zeros((s.B * s.QS, s.QN, s.D))
+    for b in range(s.B):
+        for q in range(s.QS):
+            idx = bsnd["sparse_indices"][b, q, 0].long()
+            idx = idx[(idx >= 0) & (idx < s.lkv[b])]
+            out[b * s.QS + q] = sdpa_rows(bsnd, [b * s.QS + q], b * s.kv_seq + idx)[0]
+    return out
+
+
+def _sfa_bsnd_kv(lib, close):
+    inp = make_sfa(_sfa_breadth(QS=2, sparse_mode=0, lkv=[200, 317]))
+    return close(oracle.sfa(_bsnd_from_paged(inp), use=lib), _sfa_gather_ref_rows(_bsnd_from_paged(inp)))
 
 
 def _build(src, path):
