@@ -68,12 +68,14 @@ def algorithmic_bytes(inp) -> dict:
     from decode_attention_kv_06_amd.workloads import SfaSpec
     s = inp["spec"]
     if isinstance(s, SfaSpec):
-        nval = inp["n_valid"].astype(np.int64)
-        rows = int(nval.sum())
+        rows = sfa_attended_rows(inp)
         eb = 2
+        R = inp["q_rows"]
         kv = rows * (s.D + s.DR + s.D) * eb
-        extra = s.B * inp["sparse_indices"].shape[-1] * 4 + rows * 4 + s.B * 4
-        qo = s.B * s.QN * (s.D + s.DR) * eb + s.B * s.QN * s.D * eb
+        extra = R * inp["sparse_indices"].shape[-1] * 4 + s.B * 4 * (2 if s.layout_q == "TND" else 1)
+        if s.layout_kv == "PA_BSND":
+            extra += rows // s.sparse_block_size * 4       # one block-table entry per selected block
+        qo = R * s.QN * (s.D + s.DR) * eb + R * s.QN * s.D * eb
         return {"total": kv + extra + qo, "kv": kv, "streamed": kv + extra + qo}
     B, N, nkv, D = s.B, s.N, s.nkv, s.D
     eb = 1 if s.kv_dtype == "i8" else 2
@@ -112,13 +114,36 @@ def algorithmic_bytes(inp) -> dict:
     return {"total": kv + extra + qo, "kv": kv, "streamed": streamed + extra + qo}
 
 
+def sfa_attended_rows(inp) -> int:
+    """Cache rows the sparse call gathers: every selected position below its
+    query row's limit (the kv length, or the causal bound under mode 3)."""
+    import numpy as np
+    s = inp["spec"]
+    lkv, lq = inp["lkv_counts"], inp["lq_counts"]
+    rb, rs = inp["row_batch"], inp["row_pos"]
+    limit = lkv[rb].astype(np.int64)
+    if s.sparse_mode == 3:
+        limit = np.minimum(limit, lkv[rb] - lq[rb] + rs + 1)
+    limit[rs >= lq[rb]] = 0
+    idx = inp["sparse_indices"].numpy().reshape(len(rb), -1).astype(np.int64)
+    sbs = s.sparse_block_size
+    pos = idx[:, :, None] * sbs + np.arange(sbs)
+    ok = (idx[:, :, None] >= 0) & (pos < limit[:, None, None])
+    return int(ok.sum())
+
+
 def describe_config(inp) -> dict:
     from decode_attention_kv_06_amd.workloads import SfaSpec
     s = inp["spec"]
     if isinstance(s, SfaSpec):
-        return {"workload": s.name, "B": s.B, "Q_S": 1, "Q_N": s.QN, "KV_N": 1, "D": s.D, "Dr": s.DR,
-                "block_size": s.block_size, "sparse_size": int(inp["sparse_indices"].shape[-1]),
-                "lkv": "U[%d,%d]" % s.lkv_range, "layout": "BSND / PA_BSND", "dtype": s.dtype}
+        c = {"workload": s.name, "B": s.B, "Q_S": s.QS, "Q_N": s.QN, "KV_N": 1, "D": s.D, "Dr": s.DR,
+             "block_size": s.block_size, "sparse_size": int(inp["sparse_indices"].shape[-1]),
+             "lkv": "U[%d,%d]" % s.lkv_range, "layout": "%s / %s" % (s.layout_q, s.layout_kv), "dtype": s.dtype}
+        if s.sparse_mode:
+            c["sparse_mode"] = s.sparse_mode
+        if s.sparse_block_size > 1:
+            c["sparse_block_size"] = s.sparse_block_size
+        return c
     c = {"workload": s.name, "B": s.B, "N": s.N, "N_kv": s.nkv, "D": s.D, "Smax": inp["S"], "layout": s.layout,
          "dtype_q": s.q_dtype, "dtype_kv": s.kv_dtype}
     if s.len_range:
@@ -157,9 +182,10 @@ def build_args(d: dict, o, split: int, keep: list):
     from decode_attention_kv_06_amd.workloads import SfaSpec
     s = d["spec"]
     if isinstance(s, SfaSpec):
+        from decode_attention_kv_06_amd import harness
         a = binding.sfa_args(d["q"], d["q_rope"], d["key"], d["key_rope"], d["value"], d["sparse_indices"],
-                             d["block_table"], d["actual_seq_lengths_kv"], o, scale_value=s.scale_value,
-                             sparse_mode=s.sparse_mode, split_hint=split, keep=keep)
+                             d["block_table"], d["actual_seq_lengths_kv"], o, keep=keep,
+                             **harness.sfa_options(d, split))
         return "sfa_decode_mla", a
     if s.paged:
         a = binding.ifa_paged_args(d["q"], d["k"], d["v"], o, d["block_table"], num_heads=s.N,

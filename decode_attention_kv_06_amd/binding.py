@@ -61,7 +61,8 @@ class SfaMlaArgs(ctypes.Structure):
         ("head_dim", I64), ("rope_dim", I64), ("sparse_size", I64), ("block_size", I64), ("num_blocks", I64),
         ("max_blocks", I64), ("scale_value", ctypes.c_float), ("sparse_block_size", I64), ("sparse_mode", I64),
         ("attention_mode", I64), ("layout_query", ctypes.c_char_p), ("layout_kv", ctypes.c_char_p),
-        ("split_hint", I64), ("profile_event_begin", P), ("profile_event_end", P)]
+        ("split_hint", I64), ("profile_event_begin", P), ("profile_event_end", P), ("q_tokens", I64),
+        ("kv_tokens", I64), ("kv_seq", I64)]
 
 
 class IfaError(RuntimeError):
@@ -243,9 +244,18 @@ def ifa_decode_paged(q, key_cache, value_cache, out, block_table, *, workspace=N
 def sfa_args(query, query_rope, key, key_rope, value, sparse_indices, block_table, actual_seq_lengths_kv, out, *,
              scale_value=None, actual_seq_lengths_query=None, sparse_mode=0, sparse_block_size=1,
              attention_mode=2, layout_query="BSND", layout_kv="PA_BSND", split_hint=0, keep=None):
-    B, QS, QN, D = query.shape
+    """Fill an SfaMlaArgs.  query BSND [B, Q_S, Q_N, D] or TND [Q_T, Q_N, D] (B = the length of
+    actual_seq_lengths_query); key PA_BSND [blocks, block_size, 1, D], BSND [B, KV_S, 1, D] or
+    TND [KV_T, 1, D]."""
+    if layout_query == "TND":
+        QT, QN, D = query.shape
+        if actual_seq_lengths_query is None:
+            raise ValueError("a TND query needs actual_seq_lengths_query (prefix sums)")
+        B, QS = actual_seq_lengths_query.shape[0], 1
+    else:
+        B, QS, QN, D = query.shape
+        QT = 0
     DR = query_rope.shape[-1]
-    nblk, bs = key.shape[0], key.shape[1]
     a = SfaMlaArgs()
     a.struct_size = ctypes.sizeof(SfaMlaArgs)
     a.query, a.query_rope, a.key, a.key_rope, a.value = (_ptr(query), _ptr(query_rope), _ptr(key),
@@ -255,10 +265,17 @@ def sfa_args(query, query_rope, key, key_rope, value, sparse_indices, block_tabl
     a.actual_seq_lengths_kv = _ptr(actual_seq_lengths_kv)
     a.attention_out = _ptr(out)
     a.dtype = _DT[query.dtype]
-    a.batch, a.q_seq, a.q_heads, a.kv_heads = B, QS, QN, key.shape[2]
+    a.batch, a.q_seq, a.q_heads, a.kv_heads = B, QS, QN, key.shape[-2]
     a.head_dim, a.rope_dim = D, DR
     a.sparse_size = sparse_indices.shape[-1]
-    a.block_size, a.num_blocks, a.max_blocks = bs, nblk, block_table.shape[1]
+    if layout_kv == "PA_BSND":
+        a.block_size, a.num_blocks = key.shape[1], key.shape[0]
+        a.max_blocks = block_table.shape[1]
+    elif layout_kv == "BSND":
+        a.kv_seq = key.shape[1]
+    else:
+        a.kv_tokens = key.shape[0]
+    a.q_tokens = QT
     a.scale_value = float(scale_value if scale_value is not None else 1.0 / float(D + DR) ** 0.5)
     a.sparse_block_size, a.sparse_mode, a.attention_mode = sparse_block_size, sparse_mode, attention_mode
     lq, lk = layout_query.encode(), layout_kv.encode()
@@ -271,7 +288,7 @@ def sfa_args(query, query_rope, key, key_rope, value, sparse_indices, block_tabl
 
 def sfa_decode_mla(query, query_rope, key, key_rope, value, sparse_indices, block_table, actual_seq_lengths_kv,
                    out, *, workspace=None, stream=None, **kw) -> int:
-    """SparseFlashAttention (MLA-absorb, PA_BSND); writes `out`, returns workspace bytes used."""
+    """SparseFlashAttention (MLA-absorb); writes `out`, returns workspace bytes used."""
     keep: list = []
     a = sfa_args(query, query_rope, key, key_rope, value, sparse_indices, block_table, actual_seq_lengths_kv, out,
                  keep=keep, **kw)

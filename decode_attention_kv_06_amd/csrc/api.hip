@@ -26,7 +26,7 @@ namespace {
 
 using namespace ifa;
 
-constexpr int kAbiVersion = 2;
+constexpr int kAbiVersion = 3;
 
 bool is_float_dt(int dt) { return dt == IFA_DT_F16 || dt == IFA_DT_BF16; }
 

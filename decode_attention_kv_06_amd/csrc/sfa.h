@@ -6,27 +6,39 @@
 
 namespace ifa {
 
-// Sparse entries handled by one workgroup at most (the kernel's LDS row table).
+// Cache rows gathered by one workgroup at most (the kernel's LDS row table).
 constexpr int kSfaChunkMax = 512;
 
 // Arguments of the gather + MFMA kernel and its chunk combine.
+//
+// Query rows: BSND queries give B * QS rows (row b * QS + s), TND queries
+// their Q_T packed rows; q, q_rope, the index lists and the output all
+// follow that row order.  Cache rows: a paged cache names rows through the
+// block table; a BSND cache holds batch b at rows b * kv_seq + t, a TND
+// cache at rows lkv[b - 1] + t.
 struct SfaParams {
     const void *q, *q_rope, *key, *key_rope, *value;
-    const int32_t *idx;       // [B, sparse_size]
-    const int32_t *bt;        // [B, max_blocks]
-    const int32_t *lkv;       // [B]
-    const int32_t *lq;        // [B] or nullptr
-    void *out;                // [B, QN, 512]
-    void *part_o;             // [B, n_sc, QN, 512], input dtype: each chunk's output normalised by its own sum
-    float *part_ml;           // [B, n_sc, QN, 2]: the chunk's running max (log2 domain) and sum
+    const int32_t *idx;       // [R, sparse_size]
+    const int32_t *bt;        // [B, max_blocks] (paged cache only)
+    const int32_t *lkv;       // [B]: counts, or prefix sums (TND cache); nullptr: kv_seq each (BSND cache)
+    const int32_t *lq;        // [B]: counts (BSND query) or prefix sums (TND query); nullptr: QS each
+    void *out;                // [R, QN, 512]
+    void *part_o;             // [R, n_sc, QN, 512], input dtype: each chunk's output normalised by its own sum
+    float *part_ml;           // [R, n_sc, QN, 2]: the chunk's running max (log2 domain) and sum
     int64_t sparse_size;
-    int32_t B, QN, bs, max_blocks, num_blocks;
+    int64_t kv_seq;           // BSND cache: positions per batch
+    int64_t kv_rows;          // rows of the key tensor (bounds every cache row the kernel reads)
+    int32_t B, R, QS, QN, bs, max_blocks, num_blocks;
+    int32_t layout_q;         // 0 BSND, 1 TND
+    int32_t layout_kv;        // 0 PA_BSND, 1 BSND, 2 TND
+    int32_t sparse_mode;      // 0 all, 3 rightDownCausal
+    int32_t sbs_shift;        // log2 sparse_block_size
     uint32_t bs_magic;
     int32_t bs_shift;
     int32_t n_hb;             // blocks of 64 heads
-    int32_t n_sc;             // index chunks per batch
-    int32_t chunk;            // indices per chunk (<= 1024)
-    int32_t direct;           // one chunk per batch: write the normalised output directly
+    int32_t n_sc;             // index chunks per query row
+    int32_t chunk;            // index entries per chunk (chunk << sbs_shift <= kSfaChunkMax rows)
+    int32_t direct;           // one chunk per row: write the normalised output directly
     float score_mul;          // scale * log2(e)
 };
 

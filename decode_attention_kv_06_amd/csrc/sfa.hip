@@ -4,6 +4,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <stddef.h>
+
 #include <algorithm>
 
 #include "sfa.h"
@@ -12,25 +14,66 @@ namespace ifa {
 
 namespace {
 
-int validate(const sfa_mla_args *a) {
+// The call's shape once validated: query rows, layouts and the breadth fields
+// (zero when the caller's struct predates them).
+struct SfaShape {
+    int layout_q = 0, layout_kv = 0, sbs_shift = 0;
+    int64_t R = 0, q_tokens = 0, kv_tokens = 0, kv_seq = 0, kv_rows = 0;
+};
+
+int validate(const sfa_mla_args *a, SfaShape &sh) {
     if (!a) return IFA_ERR_PARAM_NULLPTR;
-    if (a->struct_size < sizeof(sfa_mla_args)) return IFA_ERR_PARAM_INVALID;
+    if (a->struct_size < offsetof(sfa_mla_args, q_tokens)) return IFA_ERR_PARAM_INVALID;
+    const bool breadth = a->struct_size >= sizeof(sfa_mla_args);
+    sh.q_tokens = breadth ? a->q_tokens : 0;
+    sh.kv_tokens = breadth ? a->kv_tokens : 0;
+    sh.kv_seq = breadth ? a->kv_seq : 0;
+    if (!a->layout_query || !strcmp(a->layout_query, "BSND")) sh.layout_q = 0;
+    else if (!strcmp(a->layout_query, "TND")) sh.layout_q = 1;
+    else return IFA_ERR_PARAM_INVALID;
+    if (!a->layout_kv || !strcmp(a->layout_kv, "PA_BSND")) sh.layout_kv = 0;
+    else if (!strcmp(a->layout_kv, "BSND")) sh.layout_kv = 1;
+    else if (!strcmp(a->layout_kv, "TND")) sh.layout_kv = 2;
+    else return IFA_ERR_PARAM_INVALID;
     if (!a->query || !a->query_rope || !a->key || !a->key_rope || !a->value || !a->sparse_indices ||
-        !a->block_table || !a->actual_seq_lengths_kv || !a->attention_out)
+        !a->attention_out)
         return IFA_ERR_PARAM_NULLPTR;
+    if (sh.layout_kv == 0 && !a->block_table) return IFA_ERR_PARAM_NULLPTR;
+    // README: the kv lengths are required for TND and PA_BSND caches, the
+    // query lengths (prefix sums) for TND queries
+    if (sh.layout_kv != 1 && !a->actual_seq_lengths_kv) return IFA_ERR_PARAM_NULLPTR;
+    if (sh.layout_q == 1 && !a->actual_seq_lengths_query) return IFA_ERR_PARAM_NULLPTR;
     if (a->dtype != IFA_DT_F16 && a->dtype != IFA_DT_BF16) return IFA_ERR_PARAM_INVALID;
-    if (a->layout_query && strcmp(a->layout_query, "BSND")) return IFA_ERR_PARAM_INVALID;
-    if (a->layout_kv && strcmp(a->layout_kv, "PA_BSND")) return IFA_ERR_PARAM_INVALID;
     if (a->batch < 1 || a->batch > 65536) return IFA_ERR_PARAM_INVALID;
-    if (a->q_seq != 1) return IFA_ERR_PARAM_INVALID;
+    if (sh.layout_q == 0) {
+        if (a->q_seq < 1 || a->q_seq > 65536) return IFA_ERR_PARAM_INVALID;
+        sh.R = a->batch * a->q_seq;
+    } else {
+        if (sh.q_tokens < 1) return IFA_ERR_PARAM_INVALID;
+        sh.R = sh.q_tokens;
+    }
+    if (sh.R > (1 << 24)) return IFA_ERR_PARAM_INVALID;
     if (a->kv_heads != 1) return IFA_ERR_PARAM_INVALID;                       // KV_N only 1
     if (a->head_dim != 512 || a->rope_dim != 64) return IFA_ERR_PARAM_INVALID; // Q_D = KV_D = 512, Dr = 64
     if (a->q_heads < 1 || a->q_heads > 128) return IFA_ERR_PARAM_INVALID;
     if (a->sparse_size < 1 || a->sparse_size > (1 << 24)) return IFA_ERR_PARAM_INVALID;
-    if (a->block_size < 16 || a->block_size > 1024 || a->block_size % 16) return IFA_ERR_PARAM_INVALID;
-    if (a->num_blocks < 1 || a->num_blocks * a->block_size > INT32_MAX) return IFA_ERR_PARAM_INVALID;
-    if (a->max_blocks < 1 || a->max_blocks * a->block_size > ((int64_t)1 << 31) - 1) return IFA_ERR_PARAM_INVALID;
-    if (a->sparse_block_size != 1) return IFA_ERR_PARAM_INVALID;
+    if (sh.layout_kv == 0) {
+        if (a->block_size < 16 || a->block_size > 1024 || a->block_size % 16) return IFA_ERR_PARAM_INVALID;
+        if (a->num_blocks < 1 || a->num_blocks * a->block_size > INT32_MAX) return IFA_ERR_PARAM_INVALID;
+        if (a->max_blocks < 1 || a->max_blocks * a->block_size > INT32_MAX) return IFA_ERR_PARAM_INVALID;
+        sh.kv_rows = a->num_blocks * a->block_size;
+    } else if (sh.layout_kv == 1) {
+        if (sh.kv_seq < 1 || a->batch * sh.kv_seq > INT32_MAX) return IFA_ERR_PARAM_INVALID;
+        sh.kv_rows = a->batch * sh.kv_seq;
+    } else {
+        if (sh.kv_tokens < 1 || sh.kv_tokens > INT32_MAX) return IFA_ERR_PARAM_INVALID;
+        sh.kv_rows = sh.kv_tokens;
+    }
+    // README: sparse_block_size a power of two in [1, 128], dividing block_size for a paged cache
+    const int64_t sbs = a->sparse_block_size;
+    if (sbs < 1 || sbs > 128 || (sbs & (sbs - 1))) return IFA_ERR_PARAM_INVALID;
+    if (sh.layout_kv == 0 && a->block_size % sbs) return IFA_ERR_PARAM_INVALID;
+    while ((1 << sh.sbs_shift) < sbs) sh.sbs_shift++;
     if (a->sparse_mode != 0 && a->sparse_mode != 3) return IFA_ERR_PARAM_INVALID;
     if (a->attention_mode != 2) return IFA_ERR_PARAM_INVALID;
     if (!std::isfinite(a->scale_value)) return IFA_ERR_PARAM_INVALID;
@@ -46,10 +89,11 @@ struct SfaPlan {
     size_t workspace = 0;
 };
 
-// Work split: workgroups of 64 heads x one chunk of indices, about one per
-// compute unit; chunks hold at most kSfaChunkMax indices and are a multiple
-// of the 32-row tile.
-int plan(const sfa_mla_args *a, SfaPlan &p) {
+// Work split: workgroups of 64 heads x one chunk of one query row's index
+// list, about one per compute unit; a chunk gathers at most kSfaChunkMax
+// rows (entries x sparse_block_size) and a multiple of the 32-row tile when
+// the list is long enough.
+int plan(const sfa_mla_args *a, const SfaShape &sh, SfaPlan &p) {
     p.n_hb = (int)((a->q_heads + 63) / 64);
     int n_sc;
     if (a->split_hint > 0) {
@@ -59,22 +103,25 @@ int plan(const sfa_mla_args *a, SfaPlan &p) {
         if (hipGetDevice(&dev) != hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             return IFA_ERR_RUNTIME;
-        const int64_t per = a->batch * p.n_hb;
+        const int64_t per = sh.R * p.n_hb;
         n_sc = (int)std::max<int64_t>(1, (cus + per / 2) / per);
     }
+    const int64_t gran = std::max(1, 32 >> sh.sbs_shift), cap = kSfaChunkMax >> sh.sbs_shift;
     int64_t chunk = (a->sparse_size + n_sc - 1) / n_sc;
-    chunk = (chunk + 31) / 32 * 32;
-    if (chunk > kSfaChunkMax) chunk = kSfaChunkMax;
-    n_sc = (int)((a->sparse_size + chunk - 1) / chunk);
+    chunk = (chunk + gran - 1) / gran * gran;
+    if (chunk > cap) chunk = cap;
+    const int64_t n_sc64 = (a->sparse_size + chunk - 1) / chunk;
+    if (n_sc64 > (1 << 20)) return IFA_ERR_PARAM_INVALID;
+    n_sc = (int)n_sc64;
     p.chunk = (int)chunk;
     p.n_sc = n_sc;
-    const int64_t groups = a->batch * n_sc;
+    const int64_t groups = sh.R * n_sc;
     const int64_t grid = (groups + 7) / 8 * 8 * p.n_hb;
     if (grid > INT32_MAX) return IFA_ERR_PARAM_INVALID;
     p.grid = (int)grid;
     p.workspace = 0;
     if (n_sc > 1) {
-        const size_t rows = (size_t)a->batch * n_sc * a->q_heads;
+        const size_t rows = (size_t)sh.R * n_sc * a->q_heads;
         p.workspace = part_o_bytes(rows) + (rows * 2 * sizeof(float) + 255) / 256 * 256;
     }
     return IFA_OK;
@@ -91,20 +138,22 @@ uint32_t magic_for(uint32_t d, int *shift) {
 
 int sfa_workspace_size(const sfa_mla_args *a, size_t *bytes) {
     if (!bytes) return IFA_ERR_PARAM_NULLPTR;
-    int rc = validate(a);
+    SfaShape sh;
+    int rc = validate(a, sh);
     if (rc) return rc;
     SfaPlan p;
-    rc = plan(a, p);
+    rc = plan(a, sh, p);
     if (rc) return rc;
     *bytes = p.workspace;
     return IFA_OK;
 }
 
 int sfa_run(const sfa_mla_args *a, void *ws, size_t ws_bytes, hipStream_t stream) {
-    int rc = validate(a);
+    SfaShape sh;
+    int rc = validate(a, sh);
     if (rc) return rc;
     SfaPlan pl;
-    rc = plan(a, pl);
+    rc = plan(a, sh, pl);
     if (rc) return rc;
     if (pl.workspace && !ws) return IFA_ERR_PARAM_NULLPTR;
     if (ws_bytes < pl.workspace) return IFA_ERR_PARAM_INVALID;
@@ -120,16 +169,26 @@ int sfa_run(const sfa_mla_args *a, void *ws, size_t ws_bytes, hipStream_t stream
     p.lkv = a->actual_seq_lengths_kv;
     p.lq = a->actual_seq_lengths_query;
     p.out = a->attention_out;
-    const size_t rows = (size_t)a->batch * pl.n_sc * a->q_heads;
+    const size_t rows = (size_t)sh.R * pl.n_sc * a->q_heads;
     p.part_o = ws;
     p.part_ml = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + part_o_bytes(rows));
     p.sparse_size = a->sparse_size;
+    p.kv_seq = sh.kv_seq;
+    p.kv_rows = sh.kv_rows;
     p.B = (int)a->batch;
+    p.R = (int)sh.R;
+    p.QS = sh.layout_q == 0 ? (int)a->q_seq : 1;
     p.QN = (int)a->q_heads;
-    p.bs = (int)a->block_size;
-    p.max_blocks = (int)a->max_blocks;
-    p.num_blocks = (int)a->num_blocks;
-    p.bs_magic = magic_for((uint32_t)a->block_size, &p.bs_shift);
+    p.layout_q = sh.layout_q;
+    p.layout_kv = sh.layout_kv;
+    p.sparse_mode = (int)a->sparse_mode;
+    p.sbs_shift = sh.sbs_shift;
+    if (sh.layout_kv == 0) {
+        p.bs = (int)a->block_size;
+        p.max_blocks = (int)a->max_blocks;
+        p.num_blocks = (int)a->num_blocks;
+        p.bs_magic = magic_for((uint32_t)a->block_size, &p.bs_shift);
+    }
     p.n_hb = pl.n_hb;
     p.n_sc = pl.n_sc;
     p.chunk = pl.chunk;

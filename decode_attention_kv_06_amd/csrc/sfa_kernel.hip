@@ -191,13 +191,13 @@ __global__ __launch_bounds__(256, 1) void sfa_kernel(const SfaParams P) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, l16 = lane & 15;
 
-    // workgroup -> (batch, chunk, head block); head blocks of one chunk share an XCD
+    // workgroup -> (query row, chunk, head block); head blocks of one chunk share an XCD
     const int id = blockIdx.x;
     const int x8 = id & 7, k8 = id >> 3;
     const int hb = k8 % P.n_hb;
     const int grp = (k8 / P.n_hb) * 8 + x8;
-    if (grp >= P.B * P.n_sc) return;               // whole workgroup leaves together
-    const int b = grp / P.n_sc, sc = grp - b * P.n_sc;
+    if (grp >= P.R * P.n_sc) return;               // whole workgroup leaves together
+    const int qr = grp / P.n_sc, sc = grp - qr * P.n_sc;
 
     // Head groups of 16: wave w computes the scores of group w; every wave
     // accumulates P.V for all four groups over its own 128 output columns.  A
@@ -216,43 +216,88 @@ __global__ __launch_bounds__(256, 1) void sfa_kernel(const SfaParams P) {
         u32x4 x = {0, 0, 0, 0};
         if (h_ok) {
             const char *src = ks < kD / 32
-                ? reinterpret_cast<const char *>(P.q) + (((int64_t)b * P.QN + h) * kD + 32 * ks + 8 * g) * 2
-                : reinterpret_cast<const char *>(P.q_rope) + (((int64_t)b * P.QN + h) * kDR + 32 * (ks - kD / 32) + 8 * g) * 2;
+                ? reinterpret_cast<const char *>(P.q) + (((int64_t)qr * P.QN + h) * kD + 32 * ks + 8 * g) * 2
+                : reinterpret_cast<const char *>(P.q_rope) + (((int64_t)qr * P.QN + h) * kDR + 32 * (ks - kD / 32) + 8 * g) * 2;
             x = *reinterpret_cast<const u32x4 *>(src);
         }
         qreg[ks] = __builtin_bit_cast(vec8, x);
     }
 
+    // ---------------------------------------------------- the row's batch and attended range
+    // Query row -> batch b, place s among the batch's Lq query rows; the
+    // cache rows of batch b start at kv0 and hold Lkv positions; positions
+    // t < limit are attended (limit = Lkv, or the causal bound Lkv - Lq + s + 1
+    // under sparse_mode 3; 0 for a padding query row).  Lengths are device
+    // data: every bound is clamped so no read leaves its tensor.
+    int b, s, Lq;
+    if (P.layout_q == 0) {
+        b = qr / P.QS;
+        s = qr - b * P.QS;
+        Lq = P.lq ? P.lq[b] : P.QS;
+    } else {
+        int cnt = 0;                                   // prefix sums <= qr: the batch that owns row qr
+        for (int e0 = 0; e0 < P.B; e0 += 64) {
+            const int e = e0 + lane;
+            cnt += __popcll(__ballot(e < P.B && P.lq[e] <= qr));
+        }
+        b = __builtin_amdgcn_readfirstlane(cnt);
+        const int start = b > 0 ? P.lq[b - 1] : 0;
+        s = qr - start;
+        Lq = b < P.B ? P.lq[b] - start : 0;
+        if (b >= P.B) b = P.B - 1;
+    }
+    int64_t kv0 = 0, Lkv;
+    if (P.layout_kv == 2) {
+        kv0 = b > 0 ? P.lkv[b - 1] : 0;
+        kv0 = min(max(kv0, (int64_t)0), P.kv_rows);
+        Lkv = min((int64_t)P.lkv[b] - kv0, P.kv_rows - kv0);
+    } else if (P.layout_kv == 1) {
+        kv0 = (int64_t)b * P.kv_seq;
+        Lkv = P.lkv ? min((int64_t)P.lkv[b], P.kv_seq) : P.kv_seq;
+    } else {
+        Lkv = P.lkv[b];
+    }
+    int64_t limit = Lkv;
+    if (P.sparse_mode == 3) limit = min(limit, Lkv - Lq + s + 1);
+    if (s >= Lq) limit = 0;
+    limit = max(limit, (int64_t)0);
+
     // ---------------------------------------------------- compact the chunk's valid rows
-    // Entry e = 256 k + tid (k = 0, 1); all index loads, then all block-table
-    // loads, are issued together.  Valid entries keep their order.
+    // Row slot j = 256 k + tid (k = 0, 1) is position u = j % sparse_block_size
+    // of the block named by entry j / sparse_block_size; all index loads, then
+    // all block-table loads, are issued together.  Valid rows keep their order.
     const int64_t e_begin = (int64_t)sc * P.chunk;
     const int n_entries = (int)min((int64_t)P.chunk, P.sparse_size - e_begin);
-    const int Lkv = P.lkv[b];
-    const bool q_present = P.lq == nullptr || P.lq[b] > 0;
-    const int32_t *ind = P.idx + (int64_t)b * P.sparse_size + e_begin;
+    const int n_slots = n_entries << P.sbs_shift;
+    const int32_t *ind = P.idx + (int64_t)qr * P.sparse_size + e_begin;
     const int32_t *btab = P.bt + (int64_t)b * P.max_blocks;
     constexpr int kPer = kChunkMax / 256;
     int tv[kPer];
 #pragma unroll
     for (int k = 0; k < kPer; k++) {
-        const int e = 256 * k + tid;
-        tv[k] = (e < n_entries && q_present) ? ind[e] : -1;
+        const int j = 256 * k + tid;
+        tv[k] = j < n_slots ? ind[j >> P.sbs_shift] : -1;
     }
-    uint32_t qbv[kPer];
+    int64_t pos[kPer];
+    bool valid[kPer];
     int blk[kPer];
+    uint32_t qbv[kPer];
 #pragma unroll
     for (int k = 0; k < kPer; k++) {
-        qbv[k] = div_bs((uint32_t)max(tv[k], 0), P.bs_magic, P.bs_shift);
-        // the kv length is device data: an index past the block table is left out
-        const bool look = tv[k] >= 0 && tv[k] < Lkv && qbv[k] < (uint32_t)P.max_blocks;
-        blk[k] = look ? btab[qbv[k]] : -1;
+        const int j = 256 * k + tid;
+        pos[k] = ((int64_t)tv[k] << P.sbs_shift) + (j & ((1 << P.sbs_shift) - 1));
+        valid[k] = tv[k] >= 0 && pos[k] < limit;
+        if (P.layout_kv == 0) {
+            qbv[k] = div_bs((uint32_t)(valid[k] ? pos[k] : 0), P.bs_magic, P.bs_shift);
+            // the kv length is device data: a position past the block table is left out
+            const bool look = valid[k] && qbv[k] < (uint32_t)P.max_blocks;
+            blk[k] = look ? btab[qbv[k]] : -1;
+        }
     }
-    bool valid[kPer];
     int before[kPer];
 #pragma unroll
     for (int k = 0; k < kPer; k++) {
-        valid[k] = blk[k] >= 0 && blk[k] < P.num_blocks;
+        if (P.layout_kv == 0) valid[k] = blk[k] >= 0 && blk[k] < P.num_blocks;
         const uint64_t bal = __ballot(valid[k]);
         before[k] = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
         if (lane == 0) s_cnt[k][wave] = __popcll(bal);
@@ -263,7 +308,9 @@ __global__ __launch_bounds__(256, 1) void sfa_kernel(const SfaParams P) {
     for (int k = 0; k < kPer; k++) {
         int off = nv;
         for (int w = 0; w < wave; w++) off += s_cnt[k][w];
-        if (valid[k]) s_rows[off + before[k]] = blk[k] * P.bs + (tv[k] - (int)qbv[k] * P.bs);
+        if (valid[k])
+            s_rows[off + before[k]] = P.layout_kv == 0 ? blk[k] * P.bs + ((int)pos[k] - (int)qbv[k] * P.bs)
+                                                      : (int)(kv0 + pos[k]);
         for (int w = 0; w < kWavesPerBlock; w++) nv += s_cnt[k][w];
     }
     __syncthreads();
@@ -495,7 +542,7 @@ __global__ __launch_bounds__(256, 1) void sfa_kernel(const SfaParams P) {
     // Every chunk writes its output normalised by its own sum: directly when
     // the batch has one chunk, else in the input dtype to the workspace with
     // (m, l) beside it for the combine.
-    const int64_t prow = ((int64_t)b * P.n_sc + sc) * P.QN;   // partial rows of this chunk
+    const int64_t prow = ((int64_t)qr * P.n_sc + sc) * P.QN;  // partial rows of this chunk
     if (qk_wave) {
         // l of head l16 summed over the four lane groups (m_run already agrees)
         l_run += __shfl_xor(l_run, 16);
@@ -507,7 +554,7 @@ __global__ __launch_bounds__(256, 1) void sfa_kernel(const SfaParams P) {
     }
     __syncthreads();
     void *dst = P.direct ? P.out : P.part_o;
-    const int64_t row0 = P.direct ? (int64_t)b * P.QN : prow;
+    const int64_t row0 = P.direct ? (int64_t)qr * P.QN : prow;
 #pragma unroll
     for (int hg = 0; hg < kWavesPerBlock; hg++) {
         if (hg >= n_act) continue;
@@ -523,17 +570,17 @@ __global__ __launch_bounds__(256, 1) void sfa_kernel(const SfaParams P) {
     }
 }
 
-// Merges the chunk outputs of one (b, h) row in chunk order:
+// Merges the chunk outputs of one (query row, head) in chunk order:
 // out = sum_s w_s o_s / sum_s w_s with w_s = l_s 2^(m_s - max m), and rounds.
 template <bool BF>
 __global__ __launch_bounds__(256) void sfa_combine_kernel(const SfaParams P) {
     using M = Mfma<BF>;
     const int lane = threadIdx.x & 63;
     const int row = blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (row >= P.B * P.QN) return;
-    const int b = row / P.QN, hh = row - b * P.QN;
+    if (row >= P.R * P.QN) return;
+    const int qr = row / P.QN, hh = row - qr * P.QN;
     const float2 *ml = reinterpret_cast<const float2 *>(P.part_ml);
-    auto prow = [&](int s) -> int64_t { return ((int64_t)b * P.n_sc + s) * P.QN + hh; };
+    auto prow = [&](int s) -> int64_t { return ((int64_t)qr * P.n_sc + s) * P.QN + hh; };
     float Mx = kNegInf;
     for (int s = 0; s < P.n_sc; s++) Mx = fmaxf(Mx, ml[prow(s)].x);
     float L = 0.f, o[kD / 64];
@@ -549,7 +596,7 @@ __global__ __launch_bounds__(256) void sfa_combine_kernel(const SfaParams P) {
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
-    for (int e = 0; e < kD / 64; e++) M::store(P.out, ((int64_t)b * P.QN + hh) * kD + lane + 64 * e, o[e] * inv);
+    for (int e = 0; e < kD / 64; e++) M::store(P.out, ((int64_t)qr * P.QN + hh) * kD + lane + 64 * e, o[e] * inv);
 }
 
 }  // namespace sfa_detail
@@ -566,7 +613,7 @@ hipError_t sfa_launch(const SfaParams &p, bool bf16, int grid, hipStream_t s, hi
     if (e != hipSuccess) return e;
     if (ev_end && hipEventRecord(ev_end, s) != hipSuccess) return hipErrorUnknown;
     if (!p.direct) {
-        const int rows = p.B * p.QN;
+        const int rows = p.R * p.QN;
         const int blocks = (rows + kWavesPerBlock - 1) / kWavesPerBlock;
         if (bf16)
             hipLaunchKernelGGL(sfa_combine_kernel<true>, dim3(blocks), dim3(256), 0, s, p);

@@ -22,14 +22,21 @@ def alloc_out(inp: dict) -> torch.Tensor:
     return torch.empty_like(inp["q"])
 
 
+def sfa_options(dev: dict, split: int = 0) -> dict:
+    """Keyword arguments of an SFA call beyond its tensors."""
+    s = dev["spec"]
+    return dict(scale_value=s.scale_value, sparse_mode=s.sparse_mode, sparse_block_size=s.sparse_block_size,
+                actual_seq_lengths_query=dev.get("actual_seq_lengths_query"), layout_query=s.layout_q,
+                layout_kv=s.layout_kv, split_hint=split)
+
+
 def call(dev: dict, out: torch.Tensor, split: int = 0, workspace=None, stream=None) -> int:
     """Run the entry point that `dev["spec"]` describes; returns workspace bytes."""
     s = dev["spec"]
     if isinstance(s, SfaSpec):
         return binding.sfa_decode_mla(dev["q"], dev["q_rope"], dev["key"], dev["key_rope"], dev["value"],
                                       dev["sparse_indices"], dev["block_table"], dev["actual_seq_lengths_kv"], out,
-                                      scale_value=s.scale_value, sparse_mode=s.sparse_mode, split_hint=split,
-                                      workspace=workspace, stream=stream)
+                                      workspace=workspace, stream=stream, **sfa_options(dev, split))
     assert isinstance(s, IfaSpec)
     common = dict(num_heads=s.N, num_key_value_heads=s.Nkv, input_layout=s.layout, scale_value=s.scale_value,
                   actual_seq_lengths=dev["actual_seq_lengths"], atten_mask=dev["mask"], pse_shift=dev.get("pse"),

@@ -376,6 +376,7 @@ def make_sfa(spec: SfaSpec) -> dict:
         out["actual_seq_lengths_query"] = None
     out["lkv_counts"] = lkv
     out["lq_counts"] = lq
+    out["row_batch"], out["row_pos"] = rows_b, rows_s
     out["q_rows"] = R
     out["n_valid"] = nval
     return out
@@ -399,6 +400,8 @@ def workloads() -> dict:
                                     S=32768, len_range=(4096, 32768), pad_off=(0, 64), antiquant="per_channel",
                                     scale=s128),
         "sfa_mla_bf16": SfaSpec("sfa_mla_bf16", 5),
+        # multi-token decode: C5's shapes with two query rows per batch under rightDownCausal
+        "sfa_mtp_bf16": SfaSpec("sfa_mtp_bf16", 7, QS=2, sparse_mode=3),
         # the dense GQA workload with a per-batch positional bias (pseShift) of N(0, 4)
         "dense_pse_bf16_bsh": IfaSpec("dense_pse_bf16_bsh", 6, "bf16", "bf16", B=64, N=32, Nkv=8, D=128,
                                       layout="BSH", S=8192, len_range=(1024, 8192), scale=s128, pse=True,

@@ -8,7 +8,7 @@
  *
  *   ifa_decode        IncreFlashAttention over a dense padded KV cache
  *   ifa_decode_paged  IncreFlashAttention over a paged KV cache (block table)
- *   sfa_decode_mla    SparseFlashAttention, MLA-absorb mode, paged cache
+ *   sfa_decode_mla    SparseFlashAttention, MLA-absorb mode (paged, BSND or TND cache)
  *
  * What is computed (IncreFlashAttention README "Formula"; V2 page "Formula"):
  *     attentionOut = softmax(scaleValue * query . key^T  [masked]) . value
@@ -193,29 +193,48 @@ typedef struct ifa_paged_args {
 } ifa_paged_args;
 
 /*
- * SparseFlashAttention, MLA-absorb mode (attention_mode 2), query layout
- * "BSND", cache layout "PA_BSND" (SparseFlashAttention README parameter table
- * and constraints).
+ * SparseFlashAttention, MLA-absorb mode (attention_mode 2) (SparseFlashAttention
+ * README: Formula, parameter table, constraints).
  *
- * query [B,1,Q_N,512], query_rope [B,1,Q_N,64]; key and value
- *   [num_blocks, block_size, 1, 512], key_rope [num_blocks, block_size, 1, 64];
- *   one dtype (fp16 or bf16) for all of them; value may alias key.
- * sparse_indices: device int32 [B,1,1,sparse_size]; entry t is valid when
- *   0 <= t < actual_seq_lengths_kv[b] (valid entries first, invalid last, as
- *   the README asks; every valid entry is used wherever it stands, and each
- *   occurrence of a repeated index counts).
- * block_table: device int32 [B, max_blocks]; the row of index t is
- *   block_table[b][t / block_size], t % block_size.
- * actual_seq_lengths_kv: device int32 [B], required.
- * actual_seq_lengths_query: device int32 [B] or NULL; with q_seq == 1 the
- *   only valid values are 0 (row output is zero) and 1.
- * attention_out [B,1,Q_N,512], dtype as the inputs.
- * Envelope: q_seq == 1, kv_heads == 1, head_dim == 512, rope_dim == 64,
- *   1 <= q_heads <= 128, sparse_size >= 1, block_size a multiple of 16 and
- *   <= 1024, sparse_block_size == 1, sparse_mode 0 or 3 (equal at q_seq 1),
- *   attention_mode == 2.
+ * Query (layout_query):
+ *   "BSND" (or NULL): query [B, q_seq, Q_N, 512], query_rope [B, q_seq, Q_N, 64],
+ *     sparse_indices [B, q_seq, 1, sparse_size], attention_out [B, q_seq, Q_N, 512].
+ *     actual_seq_lengths_query: device int32 [B] counts in [0, q_seq], or NULL
+ *     (q_seq each); query rows past a batch's count give zero rows.
+ *   "TND": query [q_tokens, Q_N, 512], query_rope [q_tokens, Q_N, 64],
+ *     sparse_indices [q_tokens, 1, sparse_size], attention_out [q_tokens, Q_N, 512];
+ *     actual_seq_lengths_query (required) holds the prefix sums of the batches'
+ *     row counts, so batch b owns rows [lq[b-1], lq[b]) and lq[B-1] == q_tokens.
+ * Cache (layout_kv), key and value of one shape, key_rope with 64 in place of 512:
+ *   "PA_BSND" (or NULL): [num_blocks, block_size, 1, 512] with block_table
+ *     device int32 [B, max_blocks]; position t of batch b is row t % block_size
+ *     of block block_table[b][t / block_size]; block_size a multiple of 16, at
+ *     most 1024.  actual_seq_lengths_kv: device int32 [B], required.
+ *   "BSND": [B, kv_seq, 1, 512]; block_table unused;
+ *     actual_seq_lengths_kv: device int32 [B] counts, or NULL (kv_seq each).
+ *   "TND": [kv_tokens, 1, 512]; actual_seq_lengths_kv (required) holds prefix
+ *     sums, batch b owning rows [lkv[b-1], lkv[b]).
+ *   One dtype (fp16 or bf16) for every tensor; value may alias key.
+ * Selection: entry i of a query row names block idx = sparse_indices[..][i]
+ *   of sparse_block_size consecutive positions idx * sparse_block_size + u;
+ *   a negative entry is invalid (valid entries first, invalid last, as the
+ *   README asks; every valid entry is used wherever it stands, and each
+ *   occurrence of a repeated index counts).  A position t is attended when
+ *   t < limit, limit = Lkv (sparse_mode 0) or, under sparse_mode 3
+ *   (rightDownCausal), min(Lkv, Lkv - Lq + s + 1) for query row s of Lq:
+ *   the causal boundary through the bottom-right corner (this library's
+ *   reading of the mode).  Positions past Lkv inside a block are left out;
+ *   a paged position past the block table is invalid.
+ * Envelope: kv_heads == 1, head_dim == 512, rope_dim == 64, 1 <= q_heads <=
+ *   128, 1 <= q_seq <= 65536, sparse_size >= 1, sparse_block_size a power
+ *   of two in [1, 128] (dividing block_size for a paged cache), sparse_mode
+ *   0 or 3, attention_mode == 2; cache rows (num_blocks * block_size, B *
+ *   kv_seq or kv_tokens) below 2^31.
+ * q_tokens, kv_tokens and kv_seq are the three last fields of the struct; a
+ *   struct_size that stops before them allows the BSND query and the
+ *   PA_BSND cache only.
  * split_hint: 0 lets the planner choose the number of index chunks per
- *   batch; a positive value forces it (testing and tuning).
+ *   query row; a positive value forces it (testing and tuning).
  */
 typedef struct sfa_mla_args {
     uint32_t struct_size; /* sizeof(sfa_mla_args) */
@@ -231,11 +250,14 @@ typedef struct sfa_mla_args {
     int64_t sparse_size, block_size, num_blocks, max_blocks;
     float scale_value;
     int64_t sparse_block_size, sparse_mode, attention_mode;
-    const char *layout_query; /* "BSND"; NULL means "BSND" */
-    const char *layout_kv;    /* "PA_BSND"; NULL means "PA_BSND" */
+    const char *layout_query; /* "BSND" | "TND"; NULL means "BSND" */
+    const char *layout_kv;    /* "PA_BSND" | "BSND" | "TND"; NULL means "PA_BSND" */
     int64_t split_hint;
     void *profile_event_begin; /* optional hipEvent_t pair recorded around the gather kernel */
     void *profile_event_end;
+    int64_t q_tokens;  /* Q_T of a TND query */
+    int64_t kv_tokens; /* KV_T of a TND cache */
+    int64_t kv_seq;    /* KV_S of a BSND cache */
 } sfa_mla_args;
 
 /* Phase 1: validate and return the workspace bytes the run call needs. */

@@ -119,13 +119,14 @@ def sfa(inp: dict, rows=None, use=None) -> np.ndarray:
     out = np.empty((n, s.D), dtype=np.float64)
     bt = inp["block_table"]
     lq = inp["actual_seq_lengths_query"]
+    lkv = inp["actual_seq_lengths_kv"]
     lay_q = {"BSND": 0, "TND": 1}[s.layout_q]
     lay_kv = {"PA_BSND": 0, "BSND": 1, "TND": 2}[s.layout_kv]
     rc = (use or lib()).oracle_sfa(
         _ptr(inp["q"].contiguous()), _ptr(inp["q_rope"].contiguous()), _ptr(key),
         _ptr(inp["key_rope"].contiguous()), _ptr(value), DT[key.dtype],
         _ptr(inp["sparse_indices"].contiguous()), _ptr(None if bt is None else bt.contiguous()),
-        _ptr(inp["actual_seq_lengths_kv"].contiguous()), _ptr(None if lq is None else lq.contiguous()),
+        _ptr(None if lkv is None else lkv.contiguous()), _ptr(None if lq is None else lq.contiguous()),
         lay_q, lay_kv, s.B, s.QS, R, s.QN, s.D, s.DR, inp["sparse_indices"].shape[-1], s.block_size,
         key.shape[0] if lay_kv == 0 else 0, bt.shape[1] if bt is not None else 0, inp.get("kv_seq", 0),
         int(s.sparse_mode), int(s.sparse_block_size), float(s.scale_value), _ptr(rows_a), n, _ptr(out))

@@ -21,8 +21,9 @@ def say(msg: str) -> None:
 def describe(inp) -> str:
     s = inp["spec"]
     if isinstance(s, SfaSpec):
-        return "sfa_decode_mla %s B=%d QN=%d sparse=%d bs=%d seed=%d" % (s.name, s.B, s.QN, inp["sparse_indices"]
-                                                                          .shape[-1], s.block_size, s.cfg_id)
+        return "sfa_decode_mla %s B=%d rows=%d QN=%d sparse=%d sbs=%d mode=%d %s/%s bs=%d seed=%d" % (
+            s.name, s.B, inp["q_rows"], s.QN, inp["sparse_indices"].shape[-1], s.sparse_block_size, s.sparse_mode,
+            s.layout_q, s.layout_kv, s.block_size, s.cfg_id)
     entry = "ifa_decode_paged" if s.paged else "ifa_decode"
     return "%s %s %s/%s %s B=%d N=%d Nkv=%d D=%d S=%d seed=%d" % (entry, s.name, s.q_dtype, s.kv_dtype, s.layout,
                                                                  s.B, s.N, s.nkv, s.D, inp["S"], s.cfg_id)

@@ -234,15 +234,25 @@ def test_sfa_valid_size_query():
     (dict(rope_dim=32), 161002),
     (dict(q_heads=129), 161002),
     (dict(q_heads=0), 161002),
-    (dict(q_seq=2), 161002),
+    (dict(q_seq=0), 161002),
+    (dict(q_seq=65537), 161002),
     (dict(sparse_size=0), 161002),
     (dict(block_size=24), 161002),
     (dict(block_size=1040), 161002),
-    (dict(sparse_block_size=2), 161002),
+    (dict(sparse_block_size=3), 161002),
+    (dict(sparse_block_size=256), 161002),
+    (dict(sparse_block_size=128), 161002),                 # does not divide block_size 64
     (dict(sparse_mode=1), 161002),
     (dict(attention_mode=1), 161002),
-    (dict(layout_query=b"TND"), 161002),
-    (dict(layout_kv=b"BSND"), 161002),
+    (dict(layout_query=b"TND"), 161001),                   # needs the query prefix sums
+    (dict(layout_query=b"TND", actual_seq_lengths_query=FAKE, q_tokens=0), 161002),
+    (dict(layout_query=b"BNSD"), 161002),
+    (dict(layout_kv=b"BSND"), 161002),                     # kv_seq 0
+    (dict(layout_kv=b"TND", kv_tokens=0), 161002),
+    (dict(layout_kv=b"TND", kv_tokens=10, actual_seq_lengths_kv=None), 161001),
+    (dict(layout_kv=b"PA_BNSD"), 161002),
+    (dict(layout_kv=b"BSND", kv_seq=100, struct_size=ctypes.sizeof(bd.SfaMlaArgs) - 24), 161002),
+    (dict(struct_size=ctypes.sizeof(bd.SfaMlaArgs) - 32), 161002),
     (dict(scale_value=float("inf")), 161002),
 ])
 def test_sfa_rejections(kw, code):
@@ -279,3 +289,25 @@ def test_paged_positional_bias_checks():
         == 161002
     assert ws_size("ifa_decode_paged_workspace_size", paged_args(pse_shift=FAKE, pse_batch=4, pse_seq=100))[0] \
         == 161002
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q_seq=4, sparse_mode=3),
+    dict(q_seq=4, sparse_mode=3, actual_seq_lengths_query=FAKE),
+    dict(sparse_block_size=64),
+    dict(layout_kv=b"BSND", kv_seq=100, block_table=None, actual_seq_lengths_kv=None),
+    dict(layout_kv=b"TND", kv_tokens=1000, block_table=None),
+    dict(layout_query=b"TND", actual_seq_lengths_query=FAKE, q_tokens=7),
+    dict(struct_size=ctypes.sizeof(bd.SfaMlaArgs) - 24),              # a struct without the breadth fields
+])
+def test_sfa_breadth_accepted(kw):
+    assert ws_size("sfa_decode_mla_workspace_size", sfa_args(**kw))[0] == 0
+
+
+def test_sfa_workspace_counts_query_rows_and_block_wise_chunks():
+    # 2 batches x 3 query rows = 6 rows, 2 chunks each
+    rc, n = ws_size("sfa_decode_mla_workspace_size", sfa_args(q_seq=3, split_hint=2))
+    assert rc == 0 and n == 6 * 2 * 16 * 512 * 2 + 6 * 2 * 16 * 2 * 4
+    # blocks of 64 positions: a chunk gathers at most 512 rows = 8 entries, so 100 entries take 13 chunks
+    rc, n = ws_size("sfa_decode_mla_workspace_size", sfa_args(sparse_block_size=64, split_hint=2))
+    assert rc == 0 and n == 2 * 13 * 16 * 512 * 2 + 2 * 13 * 16 * 2 * 4

@@ -1,0 +1,88 @@
+"""SparseFlashAttention breadth on the GPU against the fp64 oracle: several
+query rows per batch (rightDownCausal), block-wise selection, BSND and TND
+query and cache layouts (SparseFlashAttention README, parameter table)."""
+import pytest
+
+from decode_attention_kv_06_amd.workloads import SfaSpec, make_sfa, workloads
+from gpu_util import compare, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def small(cfg_id=500, **kw):
+    d = dict(B=3, QN=16, num_blocks=128, max_blocks=64, block_size=64, lkv_range=(300, 4096), sparse_size=300,
+             tail_range=(1, 40))
+    d.update(kw)
+    return SfaSpec("sfa_breadth", cfg_id, **d)
+
+
+@pytest.mark.parametrize("mode", [0, 3])
+@pytest.mark.parametrize("QN", [16, 128])
+def test_query_rows_per_batch(mode, QN):
+    inp = make_sfa(small(QS=4, lq=[4, 2, 0], sparse_mode=mode, QN=QN, cfg_id=501 + QN))
+    out, _ = run_gpu(inp)
+    compare(inp, out)
+
+
+def test_causal_limit_filters_indices_past_it():
+    # every row also selects positions past its causal limit: the kernel must leave them out
+    inp = make_sfa(small(QS=3, sparse_mode=3, past_limit=True, lkv=[40, 300, 2000], sparse_size=256,
+                         tail_range=(0, 8), cfg_id=510))
+    out, _ = run_gpu(inp)
+    compare(inp, out)
+
+
+@pytest.mark.parametrize("sbs", [2, 16, 64])
+@pytest.mark.parametrize("split", [0, 3])
+def test_block_wise_selection(sbs, split):
+    inp = make_sfa(small(QS=2, sparse_mode=3, sparse_block_size=sbs, sparse_size=max(8, 600 // sbs),
+                         tail_range=(0, 4), past_limit=True, cfg_id=520 + sbs))
+    out, _ = run_gpu(inp, split=split)
+    compare(inp, out)
+
+
+def test_block_wise_128_on_1024_blocks():
+    inp = make_sfa(small(sparse_block_size=128, block_size=1024, num_blocks=16, max_blocks=4,
+                         lkv_range=(1000, 4096), sparse_size=12, tail_range=(0, 3), cfg_id=530))
+    out, _ = run_gpu(inp)
+    compare(inp, out)
+
+
+@pytest.mark.parametrize("given", [True, False])
+def test_bsnd_cache(given):
+    lkv = [700, 1200, 64] if given else [1200, 1200, 1200]
+    spec = small(layout_kv="BSND", lkv=lkv, kv_seq=1200, QS=2, sparse_mode=3, cfg_id=540)
+    inp = make_sfa(spec)
+    if not given:
+        inp["actual_seq_lengths_kv"] = None          # KV_S for every batch
+    out, _ = run_gpu(inp)
+    compare(inp, out)
+
+
+def test_tnd_cache():
+    inp = make_sfa(small(layout_kv="TND", lkv=[700, 33, 1500], QS=2, sparse_mode=0, cfg_id=541))
+    out, _ = run_gpu(inp)
+    compare(inp, out)
+
+
+@pytest.mark.parametrize("layout_kv", ["PA_BSND", "TND"])
+def test_tnd_query(layout_kv):
+    inp = make_sfa(small(B=4, layout_q="TND", lq=[3, 0, 1, 4], layout_kv=layout_kv, lkv=[500, 900, 40, 3000],
+                         sparse_mode=3, cfg_id=542))
+    out, _ = run_gpu(inp)
+    compare(inp, out)
+
+
+def test_tnd_query_split_chunks():
+    inp = make_sfa(small(B=2, layout_q="TND", lq=[2, 3], sparse_mode=3, sparse_size=900, lkv=[1000, 4000],
+                         cfg_id=543))
+    out, _ = run_gpu(inp, split=4)
+    compare(inp, out)
+
+
+def test_multi_token_full_size_sampled_rows():
+    inp = make_sfa(workloads()["sfa_mtp_bf16"])
+    out, _ = run_gpu(inp)
+    n = inp["q_rows"] * inp["spec"].QN
+    rows = sorted(set([0, 1, n // 2, n - 1] + list(range(5, n, max(1, n // 97)))))
+    compare(inp, out, rows=rows)
