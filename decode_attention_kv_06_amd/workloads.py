@@ -12,6 +12,7 @@ order in which tensors are made.  Tensor ids:
     0 lengths  1 q  2 k  3 v  4 mask  5 block permutation  6 padding offsets
     7 antiquant scale  8 antiquant offset  9 q_rope  10 k_rope
     11 sparse valid counts  12 sparse indices  13 positional bias (pseShift)
+    14 per-batch cache lengths of tensor lists
 
 Normals are float32 ``standard_normal`` draws rounded to nearest-even into
 fp16/bf16; integers are uniform and inclusive.  Whole buffers are filled,
@@ -30,6 +31,7 @@ import torch
 TID_LEN, TID_Q, TID_K, TID_V, TID_MASK, TID_PERM, TID_PAD = 0, 1, 2, 3, 4, 5, 6
 TID_AQ_SCALE, TID_AQ_OFFSET, TID_QROPE, TID_KROPE, TID_NVALID, TID_IDX = 7, 8, 9, 10, 11, 12
 TID_PSE = 13
+TID_LIST = 14
 
 _TORCH_DT = {"f16": torch.float16, "bf16": torch.bfloat16, "i8": torch.int8}
 _CHUNK = 1 << 24
@@ -105,6 +107,10 @@ class IfaSpec:
     pse: bool = False
     pse_batch: int = 0           # 0 -> B, else 1
     pse_scale: float = 1.0
+    # per-batch K/V tensors (tensor lists): batch b gets its own cache of
+    # S_b = L_b + U{0..list_slack} positions (at most S), cut from the padded one
+    kv_list: bool = False
+    list_slack: int = 16
 
     @property
     def nkv(self) -> int:
@@ -231,6 +237,17 @@ def make_ifa(spec: IfaSpec) -> dict:
         out["pse"] = bias.view(pb, N, 1, ps)
     else:
         out["pse"] = None
+
+    if spec.kv_list:
+        if spec.paged or pads is not None:
+            raise ValueError("tensor lists are dense and take no left padding")
+        extra = rng_for(k_id, TID_LIST).integers(0, spec.list_slack, size=B, endpoint=True)
+        seq = np.minimum(lengths + extra, smax).astype(np.int64)
+        seq = np.maximum(seq, 1)
+        cut = (lambda t, b, n: t[b:b + 1, :, :n]) if spec.layout == "BNSD" else (lambda t, b, n: t[b:b + 1, :n])
+        out["k_list"] = [cut(out["k"], b, int(seq[b])).contiguous() for b in range(B)]
+        out["v_list"] = [cut(out["v"], b, int(seq[b])).contiguous() for b in range(B)]
+        out["list_seq"] = seq
 
     if spec.antiquant is not None:
         shp = (2,) if spec.antiquant == "per_tensor" else (2, nkv, 1, D)

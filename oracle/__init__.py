@@ -40,7 +40,7 @@ def bind(path: str) -> ctypes.CDLL:
     lb = ctypes.CDLL(path)
     P, I64, I, D = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double
     lb.oracle_ifa.argtypes = [P, I, P, P, I, I, I64, I64, I64, I64, I64, D, P, P, P, I64, I64, I64,
-                                    P, I64, I64, I64, I, P, P, I, P, I64, P, P, I64, I64]
+                                    P, I64, I64, I64, I, P, P, I, P, I64, P, P, I64, I64, P, P, P]
     lb.oracle_ifa.restype = I
     lb.oracle_sfa.argtypes = [P, P, P, P, P, I, P, P, P, P, I, I, I64, I64, I64, I64, I64, I64, I64, I64, I64, I64,
                               I64, I, I64, D, P, I64, P]
@@ -91,6 +91,13 @@ def ifa(inp: dict, rows=None, scale=None, use=None) -> np.ndarray:
     out = np.empty((n, D), dtype=np.float64)
     aqs = inp["aq_scale"].contiguous() if inp["aq_scale"] is not None else None
     aqo = inp["aq_offset"].contiguous() if inp["aq_offset"] is not None else None
+    k_list = inp.get("k_list")
+    kl = vl = seq = None
+    if k_list is not None:
+        keep = [t.contiguous() for t in k_list] + [t.contiguous() for t in inp["v_list"]]
+        kl = (ctypes.c_void_p * B)(*[t.data_ptr() for t in keep[:B]])
+        vl = (ctypes.c_void_p * B)(*[t.data_ptr() for t in keep[B:]])
+        seq = np.ascontiguousarray(inp["list_seq"], dtype=np.int64)
     pse = inp.get("pse")
     pB = pS = 0
     if pse is not None:
@@ -101,7 +108,9 @@ def ifa(inp: dict, rows=None, scale=None, use=None) -> np.ndarray:
         float(s.scale_value if scale is None else scale), _ptr(actual), _ptr(pad), _ptr(mask), mB, mN, mS,
         _ptr(bt), inp.get("max_blocks", 0) if bt is not None else 0, s.block_size if bt is not None else 0,
         inp.get("num_blocks", 0) if bt is not None else 0, s.cache_layout,
-        _ptr(aqs), _ptr(aqo), int(inp["aq_mode"]), _ptr(rows_a), n, _ptr(out), _ptr(pse), pB, pS)
+        _ptr(aqs), _ptr(aqo), int(inp["aq_mode"]), _ptr(rows_a), n, _ptr(out), _ptr(pse), pB, pS,
+        None if kl is None else ctypes.cast(kl, ctypes.c_void_p), None if vl is None else ctypes.cast(vl, ctypes.c_void_p),
+        _ptr(seq))
     if rc != 0:
         raise ValueError("oracle_ifa rejected its input (code %d)" % rc)
     return out.reshape(B, N, D) if rows is None else out

@@ -160,14 +160,21 @@ static double ifa_vfetch(const void *c, int64_t i, int64_t d) {
  *   actual: per-batch lengths or NULL (-> S).  pad: per-batch kvPaddingSize or NULL.
  *   mask: bytes [mB, mN, 1, mS], mB in {1,B}, mN in {1,N}; nonzero excludes.
  *   rows: list of b*N+h rows to evaluate (NULL -> all); out has nrows*D doubles.
+ *   k_list, v_list, list_seq (all or none): per-batch caches (the V2 page's
+ *     tensor lists, "Constraints": one tensor per batch, batch 1, shapes equal
+ *     but for S): batch b reads k_list[b] / v_list[b], a one-batch cache of
+ *     list_seq[b] positions in `layout`; lengths default to list_seq[b];
+ *     left padding is not combined with lists (reading).
  */
 int oracle_ifa(const void *q, int q_dtype, const void *k, const void *v, int kv_dtype, int layout, int64_t B,
                int64_t N, int64_t Nkv, int64_t D, int64_t S, double scale, const int64_t *actual,
                const int64_t *pad, const uint8_t *mask, int64_t mB, int64_t mN, int64_t mS,
                const int32_t *block_table, int64_t max_blocks, int64_t block_size, int64_t num_blocks,
                int cache_layout, const void *aq_scale, const void *aq_offset, int aq_mode,
-               const int64_t *rows, int64_t nrows, double *out, const void *pse, int64_t pB, int64_t pS) {
+               const int64_t *rows, int64_t nrows, double *out, const void *pse, int64_t pB, int64_t pS,
+               const void *const *k_list, const void *const *v_list, const int64_t *list_seq) {
     if (Nkv == 0) Nkv = N;
+    if (k_list && (!v_list || !list_seq || pad || block_table)) return -3;
     if (N % Nkv) return -1;
     const int64_t g = N / Nkv;
     const int paged = block_table != NULL;
@@ -179,7 +186,10 @@ int oracle_ifa(const void *q, int q_dtype, const void *k, const void *v, int kv_
         const int64_t bh = rows ? rows[r] : r;
         const int64_t b = bh / N, h = bh % N, j = h / g;
         double *o = out + r * D;
-        const int64_t L = actual ? actual[b] : S;
+        const int64_t Sb = k_list ? list_seq[b] : S;     /* positions of this batch's cache */
+        const void *kb = k_list ? k_list[b] : k, *vb = k_list ? v_list[b] : v;
+        const int64_t L = actual ? actual[b] : Sb;
+        if (L > Sb) { err |= 1; continue; }
         int64_t lo = 0, hi = L;
         if (!paged && pad && actual) {
             int64_t p = pad[b] < 0 ? 0 : pad[b];
@@ -208,6 +218,8 @@ int oracle_ifa(const void *q, int q_dtype, const void *k, const void *v, int kv_
                     off = ((blk * Nkv + j) * block_size + s % block_size) * D;
                 else
                     off = (blk * block_size + s % block_size) * Nkv * D + j * D;
+            } else if (k_list) {
+                off = layout == O_BNSD ? (j * Sb + s) * D : s * Nkv * D + j * D;
             } else if (layout == O_BNSD) {
                 off = ((b * Nkv + j) * S + s) * D;
             } else {
@@ -215,7 +227,7 @@ int oracle_ifa(const void *q, int q_dtype, const void *k, const void *v, int kv_
             }
             double dot = 0.0;
             for (int64_t d = 0; d < D; d++) {
-                double kv = elem(k, kv_dtype, off + d);
+                double kv = elem(kb, kv_dtype, off + d);
                 if (aq_mode) {
                     double sc = aq_param(aq_scale, q_dtype, aq_mode, 0, j, Nkv, D, d);
                     double of = aq_param(aq_offset, q_dtype, aq_mode, 0, j, Nkv, D, d);
@@ -231,7 +243,7 @@ int oracle_ifa(const void *q, int q_dtype, const void *k, const void *v, int kv_
             ko[cnt] = off;
             cnt++;
         }
-        ifa_vctx c = {v, kv_dtype, ko, aq_scale, aq_offset, q_dtype, aq_mode, j, Nkv, D};
+        ifa_vctx c = {vb, kv_dtype, ko, aq_scale, aq_offset, q_dtype, aq_mode, j, Nkv, D};
         softmax_combine(x, cnt, D, ifa_vfetch, &c, w, o);
         free(x);
         free(w);

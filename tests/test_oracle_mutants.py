@@ -34,6 +34,9 @@ MUTANTS = {
     "value_dequant_affine_other_way": ("v = (v + of) * sc;", "v = v * sc + of;"),
     "query_head_uses_kv_head": ("dot += elem(q, q_dtype, (b * N + h) * D + d) * kv;",
                                 "dot += elem(q, q_dtype, (b * N + j) * D + d) * kv;"),
+    "list_uses_first_tensor": ("*kb = k_list ? k_list[b] : k, *vb = k_list ? v_list[b] : v;",
+                               "*kb = k_list ? k_list[0] : k, *vb = k_list ? v_list[0] : v;"),
+    "list_bnsd_stride_of_padded_cache": ("off = layout == O_BNSD ? (j * Sb + s) * D", "off = layout == O_BNSD ? (j * S + s) * D"),
     "sfa_rope_dropped": ("dot += elem(q_rope, dtype, (qr * QN + h) * DR + d) * elem(key_rope, dtype, row * DR + d);",
                          "(void)0;"),
     "sfa_block_table_skipped": ("row = blk * block_size + t % block_size;", "row = t;"),
@@ -87,6 +90,13 @@ def _battery(lib):
         inp = make_ifa(IfaSpec("m", 935, "bf16", "bf16", B=3, N=4, Nkv=2, D=16, S=40, len_range=(1, 40),
                                pse=True, pse_batch=pb, pse_scale=2.0))
         res.append(("pse_batch%d" % pb, close(oracle.ifa(inp, use=lib), sdpa_ref(inp))))
+    for layout in ("BNSD", "BSH"):
+        inp = make_ifa(IfaSpec("m", 938, "bf16", "bf16", B=3, N=4, Nkv=2, D=16, layout=layout, S=50,
+                               len_range=(1, 40), kv_list=True))
+        try:
+            res.append(("kv_list_" + layout, close(oracle.ifa(inp, use=lib), sdpa_ref(inp))))
+        except ValueError:
+            res.append(("kv_list_" + layout, False))
     inp = make_sfa(_sfa_small())
     res.append(("sfa", close(oracle.sfa(inp, use=lib), _sfa_gather_ref(inp))))
     inp = make_sfa(_sfa_small(n_valid=[40, 50]))

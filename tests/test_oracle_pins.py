@@ -449,3 +449,44 @@ def test_bias_of_minus_infinity_everywhere_is_an_empty_set():
     out = oracle.ifa(allinf)
     assert (out[0] == 0).all() and np.isfinite(out).all()
     np.testing.assert_allclose(out[1], oracle.ifa(inp)[1], rtol=0, atol=0)
+
+
+# ------------------------------------------------------- per-batch lists ----
+@pytest.mark.parametrize("layout", ["BSH", "BNSD", "BSND"])
+def test_kv_lists_equal_the_padded_cache(layout):
+    spec = IfaSpec("pin", 940, "bf16", "bf16", B=3, N=4, Nkv=2, D=16, layout=layout, S=50, len_range=(1, 40),
+                   kv_list=True, mask="u8", mask_p=0.2, pse=True)
+    inp = make_ifa(spec)
+    assert [t.shape[1 if layout != "BNSD" else 2] for t in inp["k_list"]] == list(inp["list_seq"])
+    padded = dict(inp)
+    padded["k_list"] = None
+    np.testing.assert_allclose(oracle.ifa(inp), oracle.ifa(padded), rtol=0, atol=0)
+    np.testing.assert_allclose(oracle.ifa(inp), sdpa_ref(inp), rtol=0, atol=1e-12)
+
+
+def test_kv_lists_without_lengths_use_each_tensors_length():
+    spec = IfaSpec("pin", 941, "f16", "f16", B=3, N=2, Nkv=1, D=8, layout="BNSD", S=30, len_range=(5, 20),
+                   kv_list=True, list_slack=6)
+    inp = make_ifa(spec)
+    nolen = dict(inp)
+    nolen["actual_seq_lengths"] = None
+    withseq = dict(inp)
+    withseq["actual_seq_lengths"] = np.asarray(inp["list_seq"], dtype=np.int64)
+    np.testing.assert_allclose(oracle.ifa(nolen), oracle.ifa(withseq), rtol=0, atol=0)
+    # and differs from the lengths-only answer whenever some tensor is longer than its length
+    assert (inp["list_seq"] > inp["lengths_drawn"]).any()
+    assert not np.allclose(oracle.ifa(nolen), oracle.ifa(inp))
+
+
+def test_kv_lists_with_left_padding_or_too_long_lengths_are_rejected():
+    spec = IfaSpec("pin", 942, "f16", "f16", B=2, N=2, Nkv=1, D=8, layout="BNSD", S=30, len_range=(5, 20),
+                   kv_list=True)
+    inp = make_ifa(spec)
+    bad = dict(inp)
+    bad["actual_seq_lengths"] = np.asarray(inp["list_seq"], dtype=np.int64) + 1
+    with pytest.raises(ValueError):
+        oracle.ifa(bad)
+    padded = dict(inp)
+    padded["kv_padding_size"] = np.asarray([1, 1], dtype=np.int64)
+    with pytest.raises(ValueError):
+        oracle.ifa(padded)
