@@ -196,7 +196,9 @@ def build_args(d: dict, o, split: int, keep: list):
                                    antiquant_mode=d["aq_mode"], kv_cache_layout=s.cache_layout,
                                    split_tokens=split, keep=keep)
         return "ifa_decode_paged", a
-    a = binding.ifa_decode_args(d["q"], d["k"], d["v"], o, num_heads=s.N, num_key_value_heads=s.Nkv,
+    lists = d.get("k_list") is not None
+    a = binding.ifa_decode_args(d["q"], None if lists else d["k"], None if lists else d["v"], o, num_heads=s.N,
+                                num_key_value_heads=s.Nkv, key_list=d.get("k_list"), value_list=d.get("v_list"),
                                 input_layout=s.layout, scale_value=s.scale_value,
                                 actual_seq_lengths=d["actual_seq_lengths"],
                                 kv_padding_size=d["kv_padding_size"], atten_mask=d["mask"],

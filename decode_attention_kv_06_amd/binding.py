@@ -38,7 +38,7 @@ class IfaDecodeArgs(ctypes.Structure):
         ("kv_padding_size_count", I64), ("atten_mask", P), ("dtype_mask", I32), ("mask_batch", I64),
         ("mask_heads", I64), ("mask_seq", I64), ("pse_shift", P), ("antiquant_scale", P), ("antiquant_offset", P),
         ("antiquant_mode", I32), ("split_tokens", I64), ("profile_event_begin", P), ("profile_event_end", P),
-        ("pse_batch", I64), ("pse_seq", I64)]
+        ("pse_batch", I64), ("pse_seq", I64), ("key_list", P), ("value_list", P), ("kv_list_seq_len", P)]
 
 
 class IfaPagedArgs(ctypes.Structure):
@@ -154,30 +154,54 @@ def _pse_fields(pse, q, num_heads):
     return pse, pse.shape[0], pse.shape[3]
 
 
+def _kv_lists(key_list, value_list, input_layout, device):
+    """Device pointer arrays and host lengths of per-batch K/V tensors (batch 1 each)."""
+    if len(key_list) != len(value_list):
+        raise ValueError("key and value lists differ in length")
+    for t in list(key_list) + list(value_list):
+        if not t.is_contiguous() or t.shape[0] != 1:
+            raise ValueError("list tensors must be contiguous, of batch 1")
+    seq_axis = 2 if input_layout == "BNSD" else 1
+    kp = torch.tensor([t.data_ptr() for t in key_list], dtype=torch.int64, device=device)
+    vp = torch.tensor([t.data_ptr() for t in value_list], dtype=torch.int64, device=device)
+    seq = np.ascontiguousarray([t.shape[seq_axis] for t in key_list], dtype=np.int64)
+    return kp, vp, seq
+
+
 def ifa_decode_args(q, k, v, out, *, num_heads, num_key_value_heads=0, input_layout="BSH", scale_value=None,
                     actual_seq_lengths=None, kv_padding_size=None, atten_mask=None, pse_shift=None,
-                    antiquant_scale=None, antiquant_offset=None, antiquant_mode=0, split_tokens=0, keep=None):
-    """Fill an IfaDecodeArgs from tensors; `keep` collects host arrays that must outlive the call."""
+                    antiquant_scale=None, antiquant_offset=None, antiquant_mode=0, split_tokens=0, keep=None,
+                    key_list=None, value_list=None):
+    """Fill an IfaDecodeArgs from tensors; `keep` collects arrays that must outlive the call.
+    With key_list / value_list (per-batch tensors of batch 1), k and v must be None."""
     N = int(num_heads)
+    kref = k if key_list is None else key_list[0]
     if input_layout == "BSH":
-        B, H, S = q.shape[0], q.shape[2], k.shape[1]
+        B, H, S = q.shape[0], q.shape[2], kref.shape[1]
         D = H // N
     elif input_layout == "BNSD":
-        B, D, S = q.shape[0], q.shape[3], k.shape[2]
+        B, D, S = q.shape[0], q.shape[3], kref.shape[2]
     elif input_layout == "BSND":
-        B, D, S = q.shape[0], q.shape[3], k.shape[1]
+        B, D, S = q.shape[0], q.shape[3], kref.shape[1]
     else:
         B, D, S = q.shape[0], 0, 0
+    lists = None
+    if key_list is not None:
+        lists = _kv_lists(key_list, value_list, input_layout, q.device)
+        S = 0
     lens = _host_i64(actual_seq_lengths)
     pads = _host_i64(kv_padding_size)
     mask, dmask, mB, mN, mS = _mask_fields(atten_mask)
     pse, pB, pS = _pse_fields(pse_shift, q, N)
     if keep is not None:
-        keep.extend([lens, pads, input_layout.encode()])
+        keep.extend([lens, pads, input_layout.encode(), lists])
     a = IfaDecodeArgs()
     a.struct_size = ctypes.sizeof(IfaDecodeArgs)
     a.query, a.key, a.value, a.attention_out = _ptr(q), _ptr(k), _ptr(v), _ptr(out)
-    a.dtype_q, a.dtype_kv, a.dtype_out = _DT[q.dtype], _DT[k.dtype], _DT[out.dtype]
+    a.dtype_q, a.dtype_kv, a.dtype_out = _DT[q.dtype], _DT[kref.dtype], _DT[out.dtype]
+    if lists is not None:
+        a.key_list, a.value_list = lists[0].data_ptr(), lists[1].data_ptr()
+        a.kv_list_seq_len = lists[2].ctypes.data
     a.input_layout = input_layout.encode()
     a.batch, a.num_heads, a.num_key_value_heads, a.head_dim, a.kv_seq_len = B, N, int(num_key_value_heads), D, S
     a.scale_value = float(scale_value if scale_value is not None else 1.0 / float(D) ** 0.5)

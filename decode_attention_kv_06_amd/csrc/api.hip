@@ -26,7 +26,7 @@ namespace {
 
 using namespace ifa;
 
-constexpr int kAbiVersion = 3;
+constexpr int kAbiVersion = 4;
 
 bool is_float_dt(int dt) { return dt == IFA_DT_F16 || dt == IFA_DT_BF16; }
 
@@ -55,7 +55,8 @@ struct IfaPlan {
     int kv = 0, D = 0, G = 0, n_hg = 0, g = 0, N = 0, Nkv = 0, B = 0;
     bool paged = false;
     int extra = EX_NONE;                 // split kernel variant (mask / positional bias)
-    std::vector<Window> win;             // per batch
+    std::vector<Window> win;
+    std::vector<int64_t> list_seq;       // per-batch caches: positions of each tensor             // per batch
     std::vector<SlicePlan> slices;
     int64_t total_slots = 0;
     size_t workspace = 0;
@@ -176,7 +177,7 @@ int kv_kind(int dkv) { return dkv == IFA_DT_F16 ? KV_F16 : dkv == IFA_DT_BF16 ? 
 int plan_dense(const ifa_decode_args *a, IfaPlan &p, IfaCommon &c) {
     if (!a) return IFA_ERR_PARAM_NULLPTR;
     if (a->struct_size < offsetof(ifa_decode_args, pse_batch)) return IFA_ERR_PARAM_INVALID;
-    const bool has_pse_dims = a->struct_size >= sizeof(ifa_decode_args);
+    const bool has_pse_dims = a->struct_size >= offsetof(ifa_decode_args, key_list);
     if (a->pse_shift && !has_pse_dims) return IFA_ERR_PARAM_INVALID;
     int rc = check_common(a->query, a->attention_out, a->dtype_q, a->dtype_kv, a->dtype_out, a->input_layout,
                           a->batch, a->num_heads, a->num_key_value_heads, a->head_dim, a->scale_value, a->atten_mask,
@@ -184,9 +185,21 @@ int plan_dense(const ifa_decode_args *a, IfaPlan &p, IfaCommon &c) {
                           has_pse_dims ? a->pse_batch : 0, a->antiquant_scale, a->antiquant_offset,
                           a->antiquant_mode, a->split_tokens, &c);
     if (rc) return rc;
-    if (!a->key || !a->value) return IFA_ERR_PARAM_NULLPTR;
-    const int64_t S = a->kv_seq_len;
-    if (S < 1 || S > (int64_t)1 << 30) return IFA_ERR_PARAM_INVALID;
+    // per-batch caches (tensor lists), from ABI version 4 on
+    const bool has_lists = a->struct_size >= sizeof(ifa_decode_args);
+    const bool lists = has_lists && (a->key_list || a->value_list || a->kv_list_seq_len);
+    if (lists) {
+        if (!a->key_list || !a->value_list || !a->kv_list_seq_len) return IFA_ERR_PARAM_NULLPTR;
+        if (a->key || a->value || a->kv_padding_size || a->batch > 256) return IFA_ERR_PARAM_INVALID;
+        p.list_seq.assign(a->kv_list_seq_len, a->kv_list_seq_len + a->batch);
+        for (int64_t sb : p.list_seq)
+            if (sb < 1 || sb > (int64_t)1 << 30) return IFA_ERR_PARAM_INVALID;
+    } else {
+        if (!a->key || !a->value) return IFA_ERR_PARAM_NULLPTR;
+        p.list_seq.clear();
+    }
+    const int64_t S = lists ? 0 : a->kv_seq_len;
+    if (!lists && (S < 1 || S > (int64_t)1 << 30)) return IFA_ERR_PARAM_INVALID;
     if (a->kv_padding_size && a->kv_padding_size_count != 1 && a->kv_padding_size_count != a->batch)
         return IFA_ERR_PARAM_INVALID;
     p.B = (int)a->batch;
@@ -199,10 +212,11 @@ int plan_dense(const ifa_decode_args *a, IfaPlan &p, IfaCommon &c) {
     p.win.resize(p.B);
     int64_t max_hi = 0;
     for (int b = 0; b < p.B; b++) {
-        int64_t L = S, lo = 0, hi = S;
+        const int64_t Sb = lists ? p.list_seq[b] : S;
+        int64_t L = Sb, lo = 0, hi = Sb;
         if (a->actual_seq_lengths) {
             L = a->actual_seq_lengths[b];
-            if (L < 0 || L > S) return IFA_ERR_PARAM_INVALID;
+            if (L < 0 || L > Sb) return IFA_ERR_PARAM_INVALID;
             lo = 0;
             hi = L;
             if (a->kv_padding_size) {
@@ -289,6 +303,9 @@ struct Launch {
     int max_blocks, block_size, num_blocks;
     const void *aqs, *aqo;
     int aq_mode;
+    const void *const *k_list;
+    const void *const *v_list;
+    int list_bnsd;
     bool q_bf16;
     double scale;
     hipEvent_t ev_begin, ev_end;
@@ -312,6 +329,9 @@ int run(const IfaPlan &p, const Launch &L, void *ws, size_t ws_bytes, hipStream_
     sp.pse_sH = L.pse_sH;
     sp.block_table = L.block_table;
     sp.k_scale = L.aqs;
+    sp.k_list = L.k_list;
+    sp.v_list = L.v_list;
+    sp.list_bnsd = L.list_bnsd;
     sp.sB = L.sB;
     sp.sN = L.sN;
     sp.sS = L.sS;
@@ -362,6 +382,7 @@ int run(const IfaPlan &p, const Launch &L, void *ws, size_t ws_bytes, hipStream_
             sp.len[i] = cp.len[i] = p.win[s.b0 + i].hi - p.win[s.b0 + i].lo;
             sp.sbase[i] = cp.sbase[i] = s.sbase[i];
             sp.maxseg[i] = cp.maxseg[i] = s.maxseg[i];
+            sp.list_seq[i] = p.list_seq.empty() ? 0 : (int32_t)p.list_seq[s.b0 + i];
         }
         sp.pre[s.nb] = cp.pre[s.nb] = s.pre[s.nb];
         sp.part_acc = part_acc + s.slot_base * p.G * p.D;
@@ -385,6 +406,11 @@ Launch dense_launch(const ifa_decode_args *a, const IfaPlan &p, const IfaCommon 
     L.v = a->value;
     L.out = a->attention_out;
     const int64_t S = a->kv_seq_len, D = p.D, Nkv = p.Nkv;
+    if (!p.list_seq.empty()) {   // per-batch tensors: batch 0 of each; BNSD head stride from its S
+        L.k_list = a->key_list;
+        L.v_list = a->value_list;
+        L.list_bnsd = c.layout == 1;
+    }
     if (c.layout == 1) {         // BNSD: [B, Nkv, S, D]
         L.sB = Nkv * S * D;
         L.sN = S * D;

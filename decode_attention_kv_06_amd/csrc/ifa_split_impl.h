@@ -278,9 +278,18 @@ void split_kernel(const SplitParams P) {
         int64_t sS_b = 0;
         if constexpr (!PAGED) {
             sS_b = P.sS * EB;
-            const int64_t base = (b * P.sB + (int64_t)j * P.sN) * EB + lane_byte + (int64_t)(lo + r) * sS_b;
-            kp = kb + base;
-            vp_ = vb + base;
+            // per-batch caches (tensor lists): batch b's own tensor, batch index 0
+            const char *kb_ = kb, *vb_ = vb;
+            int64_t boff = b * P.sB, sN = P.sN;
+            if (P.k_list) {
+                kb_ = reinterpret_cast<const char *const *>(P.k_list)[b];
+                vb_ = reinterpret_cast<const char *const *>(P.v_list)[b];
+                boff = 0;
+                if (P.list_bnsd) sN = (int64_t)P.list_seq[bl] * P.sS;
+            }
+            const int64_t base = (boff + (int64_t)j * sN) * EB + lane_byte + (int64_t)(lo + r) * sS_b;
+            kp = kb_ + base;
+            vp_ = vb_ + base;
         }
         const int lim = hi - 1 - lo - r;     // last valid row index relative to row lo + r
         // Paged: the block ids of the segment are staged into this wave's LDS

@@ -35,6 +35,8 @@ struct SplitParams {
     const void *pse;        // pseShift [pse_batch, N, 1, pse_seq], query dtype; nullptr when absent
     const int32_t *block_table;
     const void *k_scale;    // int8 only: antiquant scale, q dtype
+    const void *const *k_list;   // per-batch caches: device array of B device pointers, or nullptr
+    const void *const *v_list;
     int64_t sB, sN, sS;     // dense element strides of (b, j, s)
     int64_t blk_stride, head_stride, row_stride;   // paged element strides
     int64_t mask_sB, mask_sH;                      // mask strides (0 = broadcast)
@@ -49,6 +51,7 @@ struct SplitParams {
     int32_t mask_mode;      // 0 none, 1 shared by the heads, 2 per head
     int32_t aq_mode;        // int8: 1 per-tensor, 2 per-channel
     int32_t q_bf16;         // int8 kernels: query dtype is bf16
+    int32_t list_bnsd;      // per-batch BNSD caches: the head stride is list_seq[b] * sS
     float score_mul;        // scale * log2(e)
     int32_t nb;             // batches in this slice
     int32_t b0;             // first batch of the slice
@@ -57,6 +60,7 @@ struct SplitParams {
     int32_t len[kSliceBatches];       // window length of each batch
     int32_t sbase[kSliceBatches];     // first partial slot of each batch
     int32_t maxseg[kSliceBatches];    // slots reserved per row of each batch
+    int32_t list_seq[kSliceBatches];  // per-batch caches: positions of each batch's tensor
 };
 
 // Arguments of the split-combine kernel: one wave per (b, h) row.

@@ -14,7 +14,12 @@ from .workloads import IfaSpec, SfaSpec
 def to_device(inp: dict, device: str = "cuda") -> dict:
     out = {}
     for key, val in inp.items():
-        out[key] = val.to(device) if isinstance(val, torch.Tensor) else val
+        if isinstance(val, torch.Tensor):
+            out[key] = val.to(device)
+        elif isinstance(val, list) and val and isinstance(val[0], torch.Tensor):
+            out[key] = [t.to(device) for t in val]
+        else:
+            out[key] = val
     return out
 
 
@@ -45,4 +50,7 @@ def call(dev: dict, out: torch.Tensor, split: int = 0, workspace=None, stream=No
     if s.paged:
         return binding.ifa_decode_paged(dev["q"], dev["k"], dev["v"], out, dev["block_table"],
                                         kv_cache_layout=s.cache_layout, **common)
+    if dev.get("k_list") is not None:
+        return binding.ifa_decode(dev["q"], None, None, out, kv_padding_size=dev["kv_padding_size"],
+                                  key_list=dev["k_list"], value_list=dev["v_list"], **common)
     return binding.ifa_decode(dev["q"], dev["k"], dev["v"], out, kv_padding_size=dev["kv_padding_size"], **common)

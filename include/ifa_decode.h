@@ -115,6 +115,16 @@ enum { IFA_ANTIQUANT_NONE = 0, IFA_ANTIQUANT_PER_TENSOR = 1, IFA_ANTIQUANT_PER_C
  * Envelope: 1 <= B <= 65536, 1 <= N <= 256, N % N_kv == 0,
  *   head_dim in {64, 128, 256, 512}, dtype_out == dtype_q, dtype_kv ==
  *   dtype_q or IFA_DT_I8.
+ * key_list / value_list / kv_list_seq_len (all three, or none): the tensor
+ *   lists of the V2 page ("Constraints", non-contiguous case): batch b reads
+ *   its own key and value tensors, each of batch 1, kv_list_seq_len[b]
+ *   positions and otherwise the shape of one batch of key/value in
+ *   input_layout; key and value must then be NULL and kv_seq_len is not
+ *   used.  The two pointer arrays live in device memory (caller-owned, read
+ *   by the kernels); 1 <= batch <= 256 (V2 page); actual_seq_lengths, when
+ *   given, must not exceed a batch's kv_list_seq_len; kv_padding_size must
+ *   be NULL (left padding is defined on one padded buffer).  These three are
+ *   the last fields of the struct (ABI version 4).
  * split_tokens: 0 lets the planner choose how many KV positions one work
  *   item covers; a positive multiple of 16 forces it (testing and tuning).
  * profile_event_begin / _end: NULL, or two hipEvent_t the call records on
@@ -146,6 +156,9 @@ typedef struct ifa_decode_args {
     void *profile_event_begin; /* optional hipEvent_t recorded right before the split kernel */
     void *profile_event_end;   /* optional hipEvent_t recorded right after it (both or neither) */
     int64_t pse_batch, pse_seq; /* pse_shift shape (pse_batch, N, 1, pse_seq) */
+    const void *const *key_list;    /* per-batch caches: device array of `batch` device pointers */
+    const void *const *value_list;
+    const int64_t *kv_list_seq_len; /* host int64[batch]: positions of each list tensor */
 } ifa_decode_args;
 
 /*

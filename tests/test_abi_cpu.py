@@ -108,7 +108,7 @@ PADS1 = (ctypes.c_int64 * 1)(3)
     (dict(pse_shift=FAKE), 161002),                               # pse_batch 0
     (dict(pse_shift=FAKE, pse_batch=3, pse_seq=64), 161002),      # pse_batch not in {1, B}
     (dict(pse_shift=FAKE, pse_batch=2, pse_seq=63), 161002),      # shorter than the attended range
-    (dict(pse_shift=FAKE, pse_batch=1, pse_seq=64, struct_size=ctypes.sizeof(bd.IfaDecodeArgs) - 16), 161002),
+    (dict(pse_shift=FAKE, pse_batch=1, pse_seq=64, struct_size=bd.IfaDecodeArgs.pse_batch.offset), 161002),
     (dict(atten_mask=FAKE, dtype_mask=bd.DT_F16, mask_batch=2, mask_heads=1, mask_seq=64), 161002),
     (dict(atten_mask=FAKE, dtype_mask=bd.DT_BOOL, mask_batch=3, mask_heads=1, mask_seq=64), 161002),
     (dict(atten_mask=FAKE, dtype_mask=bd.DT_BOOL, mask_batch=2, mask_heads=4, mask_seq=64), 161002),
@@ -276,7 +276,8 @@ def test_sfa_workspace_holds_chunk_outputs_in_input_dtype():
     dict(pse_shift=FAKE, pse_batch=2, pse_seq=64),
     dict(pse_shift=FAKE, pse_batch=1, pse_seq=100),
     dict(pse_shift=FAKE, pse_batch=1, pse_seq=64, actual_seq_lengths=ctypes.cast(LENS, ctypes.c_void_p)),
-    dict(struct_size=ctypes.sizeof(bd.IfaDecodeArgs) - 16),        # a struct without the pse dims
+    dict(struct_size=bd.IfaDecodeArgs.pse_batch.offset),           # a struct without the pse dims
+    dict(pse_shift=FAKE, pse_batch=2, pse_seq=64, struct_size=bd.IfaDecodeArgs.key_list.offset),  # no lists
 ])
 def test_dense_positional_bias_accepted(kw):
     assert ws_size("ifa_decode_workspace_size", dense_args(**kw))[0] == 0
@@ -311,3 +312,34 @@ def test_sfa_workspace_counts_query_rows_and_block_wise_chunks():
     # blocks of 64 positions: a chunk gathers at most 512 rows = 8 entries, so 100 entries take 13 chunks
     rc, n = ws_size("sfa_decode_mla_workspace_size", sfa_args(sparse_block_size=64, split_hint=2))
     assert rc == 0 and n == 2 * 13 * 16 * 512 * 2 + 2 * 13 * 16 * 2 * 4
+
+
+SEQ2 = (ctypes.c_int64 * 2)(64, 40)
+SEQ_SHORT = (ctypes.c_int64 * 2)(9, 64)
+
+
+def list_args(**kw):
+    base = dict(key=None, value=None, key_list=FAKE, value_list=FAKE,
+                kv_list_seq_len=ctypes.cast(SEQ2, ctypes.c_void_p), kv_seq_len=0)
+    base.update(kw)
+    return dense_args(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(), 0),
+    (dict(actual_seq_lengths=ctypes.cast(LENS, ctypes.c_void_p), kv_list_seq_len=ctypes.cast(SEQ_SHORT,
+                                                                                             ctypes.c_void_p)), 161002),
+    (dict(value_list=None), 161001),
+    (dict(kv_list_seq_len=None), 161001),
+    (dict(key=FAKE), 161002),                                   # a contiguous key beside the lists
+    (dict(kv_padding_size=ctypes.cast(PADS1, ctypes.c_void_p), kv_padding_size_count=1), 161002),
+    (dict(struct_size=bd.IfaDecodeArgs.key_list.offset), 161001),  # lists invisible: key is NULL
+])
+def test_dense_kv_lists_validation(kw, code):
+    assert ws_size("ifa_decode_workspace_size", list_args(**kw))[0] == code
+
+
+def test_dense_kv_lists_batch_limit():
+    seq = (ctypes.c_int64 * 257)(*([64] * 257))
+    a = list_args(batch=257, kv_list_seq_len=ctypes.cast(seq, ctypes.c_void_p))
+    assert ws_size("ifa_decode_workspace_size", a)[0] == 161002

@@ -1,0 +1,51 @@
+"""Per-batch K/V tensor lists (the aclnnIncreFlashAttentionV2 page's
+non-contiguous case) on the GPU against the fp64 oracle, and against the
+padded cache the lists are cut from."""
+import pytest
+import torch
+
+from decode_attention_kv_06_amd.workloads import IfaSpec, make_ifa
+from gpu_util import compare, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("layout", ["BSH", "BNSD", "BSND"])
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_lists_match_oracle_and_padded_cache_bytes(layout, dt):
+    spec = IfaSpec("kv_list", 600, dt, dt, B=5, N=16, Nkv=4, D=128, layout=layout, S=900, len_range=(1, 800),
+                   kv_list=True, list_slack=100)
+    inp = make_ifa(spec)
+    out, _ = run_gpu(inp)
+    compare(inp, out)
+    padded = dict(inp)
+    padded["k_list"] = None
+    ref, _ = run_gpu(padded)
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+
+
+@pytest.mark.parametrize("D", [64, 256, 512])
+def test_lists_without_lengths_use_each_tensors_positions(D):
+    spec = IfaSpec("kv_list_nolen", 601, "bf16", "bf16", B=3, N=8, Nkv=2, D=D, layout="BNSD", S=500,
+                   len_range=(1, 400), kv_list=True, list_slack=90, no_lengths=True)
+    inp = make_ifa(spec)
+    out, _ = run_gpu(inp)
+    compare(inp, out)
+
+
+def test_lists_with_mask_bias_and_int8():
+    spec = IfaSpec("kv_list_aq", 602, "f16", "i8", B=4, N=16, Nkv=2, D=128, layout="BSH", S=1200,
+                   len_range=(1, 1100), kv_list=True, antiquant="per_channel", mask="u8", mask_p=0.2,
+                   pse=True, pse_scale=2.0)
+    inp = make_ifa(spec)
+    out, _ = run_gpu(inp)
+    compare(inp, out)
+
+
+def test_lists_over_two_launch_slices():
+    # more than 128 batches: the per-batch table travels in two launches
+    spec = IfaSpec("kv_list_many", 603, "bf16", "bf16", B=200, N=8, Nkv=8, D=64, layout="BNSD", S=300,
+                   len_range=(1, 280), kv_list=True, list_slack=20)
+    inp = make_ifa(spec)
+    out, _ = run_gpu(inp)
+    compare(inp, out)
