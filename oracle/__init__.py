@@ -23,7 +23,7 @@ _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-DT = {torch.float16: 1, torch.bfloat16: 2, torch.int8: 3}
+DT = {torch.float16: 1, torch.bfloat16: 2, torch.int8: 3, torch.float32: 6}
 LAYOUT = {"BSH": 0, "BNSD": 1, "BSND": 2}
 
 
@@ -42,6 +42,8 @@ def bind(path: str) -> ctypes.CDLL:
     lb.oracle_ifa.argtypes = [P, I, P, P, I, I, I64, I64, I64, I64, I64, D, P, P, P, I64, I64, I64,
                                     P, I64, I64, I64, I, P, P, I, P, I64, P, P, I64, I64, P, P, P]
     lb.oracle_ifa.restype = I
+    lb.oracle_quant_int8.argtypes = [P, I64, I64, P, P, I, P, P]
+    lb.oracle_quant_int8.restype = I
     lb.oracle_sfa.argtypes = [P, P, P, P, P, I, P, P, P, P, I, I, I64, I64, I64, I64, I64, I64, I64, I64, I64, I64,
                               I64, I, I64, D, P, I64, P]
     lb.oracle_sfa.restype = I
@@ -142,6 +144,21 @@ def sfa(inp: dict, rows=None, use=None) -> np.ndarray:
     if rc != 0:
         raise ValueError("oracle_sfa rejected its input (code %d)" % rc)
     return out.reshape(R, s.QN, s.D) if rows is None else out
+
+
+def quant_int8(o: np.ndarray, scale: torch.Tensor, offset=None, use=None):
+    """int8 codes of the exact output `o` ([..., N*D] order) under quantScale2 /
+    quantOffset2 (1 or N*D values, fp32 or bf16); returns (codes, value before rounding)."""
+    o = np.ascontiguousarray(o, dtype=np.float64)
+    sc = scale.contiguous().reshape(-1)
+    off = None if offset is None else offset.contiguous().reshape(-1)
+    codes = np.empty(o.shape, dtype=np.int8)
+    pre = np.empty(o.shape, dtype=np.float64)
+    rc = (use or lib()).oracle_quant_int8(_ptr(o), o.size, sc.numel(), _ptr(sc), _ptr(off), DT[sc.dtype],
+                                          _ptr(codes), _ptr(pre))
+    if rc != 0:
+        raise ValueError("oracle_quant_int8 rejected its input (code %d)" % rc)
+    return codes, pre
 
 
 def f16_to_f64(bits: int) -> float:

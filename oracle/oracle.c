@@ -62,7 +62,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { O_F16 = 1, O_BF16 = 2, O_I8 = 3 };
+enum { O_F16 = 1, O_BF16 = 2, O_I8 = 3, O_F32 = 6 };
 enum { O_BSH = 0, O_BNSD = 1, O_BSND = 2 };
 
 /* IEEE-754 binary16 -> double, written from the format's definition:
@@ -91,6 +91,7 @@ double oracle_bf16_to_f64(uint16_t b) {
 
 static double elem(const void *base, int dtype, int64_t i) {
     switch (dtype) {
+    case O_F32: return (double)((const float *)base)[i];
     case O_F16: return oracle_f16_to_f64(((const uint16_t *)base)[i]);
     case O_BF16: return oracle_bf16_to_f64(((const uint16_t *)base)[i]);
     case O_I8: return (double)((const int8_t *)base)[i];
@@ -369,4 +370,33 @@ int oracle_sfa(const void *q, const void *q_rope, const void *key, const void *k
         free(ko);
     }
     return err ? -2 : 0;
+}
+
+/* ------------------------------------------------------- output int8 ---- */
+
+/*
+ * Post-quantisation of the attention output into int8 (IncreFlashAttention
+ * README "Constraints": quantScale2 required, quantOffset2 optional, per-tensor
+ * or per-channel, fp32 or bf16).  The pages give no formula; the reading taken
+ * is y = o * scale + offset on the exact output, rounded to the nearest
+ * integer with ties to even, then saturated to [-128, 127].
+ *   o: n doubles, channel of element i = i % C (C = 1 per-tensor, N*D
+ *   per-channel over the output's heads); qs / qo: C values of q_dtype
+ *   (qo may be NULL); out: n codes; pre (may be NULL): the value y before
+ *   rounding, so a test can see how close it came to a rounding boundary.
+ */
+int oracle_quant_int8(const double *o, int64_t n, int64_t C, const void *qs, const void *qo, int q_dtype,
+                      int8_t *out, double *pre) {
+    if (C < 1) return -1;
+    for (int64_t i = 0; i < n; i++) {
+        const int64_t c = i % C;
+        double y = o[i] * elem(qs, q_dtype, c);
+        if (qo) y += elem(qo, q_dtype, c);
+        if (pre) pre[i] = y;
+        double r = nearbyint(y);                /* the default rounding mode: to nearest, ties to even */
+        if (r > 127.0) r = 127.0;
+        if (r < -128.0) r = -128.0;
+        out[i] = (int8_t)r;
+    }
+    return 0;
 }

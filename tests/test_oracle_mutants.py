@@ -37,6 +37,11 @@ MUTANTS = {
     "list_uses_first_tensor": ("*kb = k_list ? k_list[b] : k, *vb = k_list ? v_list[b] : v;",
                                "*kb = k_list ? k_list[0] : k, *vb = k_list ? v_list[0] : v;"),
     "list_bnsd_stride_of_padded_cache": ("off = layout == O_BNSD ? (j * Sb + s) * D", "off = layout == O_BNSD ? (j * S + s) * D"),
+    "quant_ties_away_from_zero": ("double r = nearbyint(y);", "double r = round(y);"),
+    "quant_symmetric_clamp": ("if (r < -128.0) r = -128.0;", "if (r < -127.0) r = -127.0;"),
+    "quant_offset_before_scale": ("double y = o[i] * elem(qs, q_dtype, c);\n        if (qo) y += elem(qo, q_dtype, c);",
+                                  "double y = o[i];\n        if (qo) y += elem(qo, q_dtype, c);\n        y *= elem(qs, q_dtype, c);"),
+    "quant_one_channel": ("const int64_t c = i % C;", "const int64_t c = 0;"),
     "sfa_rope_dropped": ("dot += elem(q_rope, dtype, (qr * QN + h) * DR + d) * elem(key_rope, dtype, row * DR + d);",
                          "(void)0;"),
     "sfa_block_table_skipped": ("row = blk * block_size + t % block_size;", "row = t;"),
@@ -104,6 +109,7 @@ def _battery(lib):
     idx[0, 0, 0, 40:] = 200                      # == lkv[0]: must be ignored
     inp["sparse_indices"] = idx
     res.append(("sfa_bound", close(oracle.sfa(inp, use=lib), _sfa_gather_ref(inp))))
+    res.append(("quant", _quant_checks(lib)))
     for name, fn in (("sfa_causal", _sfa_causal), ("sfa_block_wise", _sfa_block_wise), ("sfa_tnd_q", _sfa_tnd_q),
                      ("sfa_tnd_kv", _sfa_tnd_kv), ("sfa_bsnd_kv", _sfa_bsnd_kv)):
         try:
@@ -111,6 +117,20 @@ def _battery(lib):
         except ValueError:
             res.append((name, False))
     return res
+
+
+def _quant_checks(lib):
+    o = np.array([0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 126.5, 127.6, -128.5, -1000.0, 1000.0, 0.0])
+    codes, _ = oracle.quant_int8(o, torch.tensor([1.0]), use=lib)
+    ok = codes.tolist() == [0, 2, 2, 0, -2, -2, 126, 127, -128, -128, 127, 0]
+    codes, _ = oracle.quant_int8(np.array([0.25, -0.75, 0.1]), torch.tensor([4.0]), torch.tensor([0.5]), use=lib)
+    ok &= codes.tolist() == [2, -2, 1]
+    sc = torch.zeros(12)
+    sc[6] = 7.0
+    codes, _ = oracle.quant_int8(np.ones((2, 12)), sc, use=lib)
+    want = np.zeros((2, 12), dtype=np.int8)
+    want[:, 6] = 7
+    return ok and bool((codes == want).all())
 
 
 def _sfa_causal(lib, close):

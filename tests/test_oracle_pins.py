@@ -490,3 +490,33 @@ def test_kv_lists_with_left_padding_or_too_long_lengths_are_rejected():
     padded["kv_padding_size"] = np.asarray([1, 1], dtype=np.int64)
     with pytest.raises(ValueError):
         oracle.ifa(padded)
+
+
+# ------------------------------------------------------- output int8 ----
+def test_quant_ties_go_to_even_and_codes_saturate():
+    o = np.array([0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 0.49999999, 126.5, 127.6, -128.5, -1000.0, 1000.0, 0.0])
+    codes, pre = oracle.quant_int8(o, torch.tensor([1.0], dtype=torch.float32))
+    assert codes.tolist() == [0, 2, 2, 0, -2, -2, 0, 126, 127, -128, -128, 127, 0]
+    assert (pre == o).all()
+
+
+def test_quant_scale_then_offset():
+    o = np.array([0.25, -0.75, 0.1])
+    codes, pre = oracle.quant_int8(o, torch.tensor([4.0]), torch.tensor([0.5]))
+    # 0.25*4+0.5 = 1.5 -> 2; -0.75*4+0.5 = -2.5 -> -2; 0.1*4+0.5 = 0.9 -> 1
+    assert codes.tolist() == [2, -2, 1]
+    np.testing.assert_allclose(pre, [1.5, -2.5, 0.9], rtol=0, atol=1e-15)
+
+
+def test_quant_per_channel_indexes_the_output_channel():
+    N, D = 3, 4
+    o = np.ones((2, N * D))
+    sc = torch.zeros(N * D, dtype=torch.bfloat16)
+    sc[1 * D + 2] = 7.0                  # head 1, column 2
+    off = torch.zeros(N * D, dtype=torch.bfloat16)
+    off[2 * D + 0] = -3.0                # head 2, column 0
+    codes, _ = oracle.quant_int8(o, sc, off)
+    want = np.zeros((2, N * D), dtype=np.int8)
+    want[:, 1 * D + 2] = 7
+    want[:, 2 * D + 0] = -3
+    assert (codes == want).all()
