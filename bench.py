@@ -194,7 +194,8 @@ def build_args(d: dict, o, split: int, keep: list):
                                    pse_shift=d.get("pse"),
                                    antiquant_scale=d["aq_scale"], antiquant_offset=d["aq_offset"],
                                    antiquant_mode=d["aq_mode"], kv_cache_layout=s.cache_layout,
-                                   split_tokens=split, keep=keep)
+                                   split_tokens=split, keep=keep, quant_scale2=d.get("quant_scale2"),
+                                   quant_offset2=d.get("quant_offset2"))
         return "ifa_decode_paged", a
     lists = d.get("k_list") is not None
     a = binding.ifa_decode_args(d["q"], None if lists else d["k"], None if lists else d["v"], o, num_heads=s.N,
@@ -204,7 +205,8 @@ def build_args(d: dict, o, split: int, keep: list):
                                 kv_padding_size=d["kv_padding_size"], atten_mask=d["mask"],
                                 pse_shift=d.get("pse"),
                                 antiquant_scale=d["aq_scale"], antiquant_offset=d["aq_offset"],
-                                antiquant_mode=d["aq_mode"], split_tokens=split, keep=keep)
+                                antiquant_mode=d["aq_mode"], split_tokens=split, keep=keep,
+                                quant_scale2=d.get("quant_scale2"), quant_offset2=d.get("quant_offset2"))
     return "ifa_decode", a
 
 def main() -> int:

@@ -22,8 +22,9 @@ IFA_ERR_PARAM_NULLPTR = 161001
 IFA_ERR_PARAM_INVALID = 161002
 IFA_ERR_RUNTIME = 361001
 
-DT_F16, DT_BF16, DT_I8, DT_U8, DT_BOOL = 1, 2, 3, 4, 5
-_DT = {torch.float16: DT_F16, torch.bfloat16: DT_BF16, torch.int8: DT_I8, torch.uint8: DT_U8, torch.bool: DT_BOOL}
+DT_F16, DT_BF16, DT_I8, DT_U8, DT_BOOL, DT_F32 = 1, 2, 3, 4, 5, 6
+_DT = {torch.float16: DT_F16, torch.bfloat16: DT_BF16, torch.int8: DT_I8, torch.uint8: DT_U8, torch.bool: DT_BOOL,
+       torch.float32: DT_F32}
 
 P = ctypes.c_void_p
 I32, I64, U32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32
@@ -38,7 +39,8 @@ class IfaDecodeArgs(ctypes.Structure):
         ("kv_padding_size_count", I64), ("atten_mask", P), ("dtype_mask", I32), ("mask_batch", I64),
         ("mask_heads", I64), ("mask_seq", I64), ("pse_shift", P), ("antiquant_scale", P), ("antiquant_offset", P),
         ("antiquant_mode", I32), ("split_tokens", I64), ("profile_event_begin", P), ("profile_event_end", P),
-        ("pse_batch", I64), ("pse_seq", I64), ("key_list", P), ("value_list", P), ("kv_list_seq_len", P)]
+        ("pse_batch", I64), ("pse_seq", I64), ("key_list", P), ("value_list", P), ("kv_list_seq_len", P),
+        ("quant_scale2", P), ("quant_offset2", P), ("quant_count", I64), ("dtype_quant", I32)]
 
 
 class IfaPagedArgs(ctypes.Structure):
@@ -50,7 +52,8 @@ class IfaPagedArgs(ctypes.Structure):
         ("mask_batch", I64), ("mask_heads", I64), ("mask_seq", I64), ("pse_shift", P), ("antiquant_scale", P),
         ("antiquant_offset", P), ("antiquant_mode", I32), ("block_table", P), ("max_blocks_per_seq", I64),
         ("block_size", I64), ("num_blocks", I64), ("kv_cache_layout", I32), ("split_tokens", I64),
-        ("profile_event_begin", P), ("profile_event_end", P), ("pse_batch", I64), ("pse_seq", I64)]
+        ("profile_event_begin", P), ("profile_event_end", P), ("pse_batch", I64), ("pse_seq", I64),
+        ("quant_scale2", P), ("quant_offset2", P), ("quant_count", I64), ("dtype_quant", I32)]
 
 
 class SfaMlaArgs(ctypes.Structure):
@@ -168,10 +171,23 @@ def _kv_lists(key_list, value_list, input_layout, device):
     return kp, vp, seq
 
 
+def _set_quant(a, quant_scale2, quant_offset2):
+    """int8 output: quantScale2 (required) and quantOffset2 (optional), 1 or N*D values, fp32 or bf16."""
+    if quant_scale2 is None:
+        if quant_offset2 is not None:
+            raise ValueError("quant_offset2 without quant_scale2")
+        return
+    if quant_offset2 is not None and (quant_offset2.dtype != quant_scale2.dtype or
+                                      quant_offset2.numel() != quant_scale2.numel()):
+        raise ValueError("quant_offset2 must match quant_scale2 in dtype and size")
+    a.quant_scale2, a.quant_offset2 = _ptr(quant_scale2), _ptr(quant_offset2)
+    a.quant_count, a.dtype_quant = quant_scale2.numel(), _DT[quant_scale2.dtype]
+
+
 def ifa_decode_args(q, k, v, out, *, num_heads, num_key_value_heads=0, input_layout="BSH", scale_value=None,
                     actual_seq_lengths=None, kv_padding_size=None, atten_mask=None, pse_shift=None,
                     antiquant_scale=None, antiquant_offset=None, antiquant_mode=0, split_tokens=0, keep=None,
-                    key_list=None, value_list=None):
+                    key_list=None, value_list=None, quant_scale2=None, quant_offset2=None):
     """Fill an IfaDecodeArgs from tensors; `keep` collects arrays that must outlive the call.
     With key_list / value_list (per-batch tensors of batch 1), k and v must be None."""
     N = int(num_heads)
@@ -202,6 +218,7 @@ def ifa_decode_args(q, k, v, out, *, num_heads, num_key_value_heads=0, input_lay
     if lists is not None:
         a.key_list, a.value_list = lists[0].data_ptr(), lists[1].data_ptr()
         a.kv_list_seq_len = lists[2].ctypes.data
+    _set_quant(a, quant_scale2, quant_offset2)
     a.input_layout = input_layout.encode()
     a.batch, a.num_heads, a.num_key_value_heads, a.head_dim, a.kv_seq_len = B, N, int(num_key_value_heads), D, S
     a.scale_value = float(scale_value if scale_value is not None else 1.0 / float(D) ** 0.5)
@@ -226,7 +243,7 @@ def ifa_decode(q, k, v, out, *, workspace=None, stream=None, **kw) -> int:
 def ifa_paged_args(q, key_cache, value_cache, out, block_table, *, num_heads, num_key_value_heads=0,
                    input_layout="BNSD", scale_value=None, actual_seq_lengths=None, atten_mask=None,
                    pse_shift=None, antiquant_scale=None, antiquant_offset=None, antiquant_mode=0, kv_cache_layout=0,
-                   split_tokens=0, keep=None):
+                   split_tokens=0, keep=None, quant_scale2=None, quant_offset2=None):
     N = int(num_heads)
     nkv = int(num_key_value_heads) or N
     if kv_cache_layout == 0:
@@ -255,6 +272,7 @@ def ifa_paged_args(q, key_cache, value_cache, out, block_table, *, num_heads, nu
     a.max_blocks_per_seq = block_table.shape[1]
     a.block_size, a.num_blocks, a.kv_cache_layout = bs, nblk, int(kv_cache_layout)
     a.split_tokens = int(split_tokens)
+    _set_quant(a, quant_scale2, quant_offset2)
     return a
 
 

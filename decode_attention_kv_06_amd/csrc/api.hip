@@ -26,7 +26,7 @@ namespace {
 
 using namespace ifa;
 
-constexpr int kAbiVersion = 4;
+constexpr int kAbiVersion = 5;
 
 bool is_float_dt(int dt) { return dt == IFA_DT_F16 || dt == IFA_DT_BF16; }
 
@@ -143,12 +143,27 @@ struct IfaCommon {
     int64_t Nkv = 0;
 };
 
+// Output quantisation fields (int8 output); zero when the caller's struct predates them.
+struct QuantArgs {
+    const void *scale = nullptr, *offset = nullptr;
+    int64_t count = 0;
+    int dtype = 0;
+};
+
+int check_quant(int dq, int dout, int64_t N, int64_t D, const QuantArgs &qa) {
+    if (dout != IFA_DT_I8) return qa.scale || qa.offset ? IFA_ERR_PARAM_INVALID : IFA_OK;
+    if (!qa.scale) return IFA_ERR_PARAM_NULLPTR;                     // README: quantScale2 required
+    if (qa.dtype != IFA_DT_F32 && !(qa.dtype == IFA_DT_BF16 && dq == IFA_DT_BF16)) return IFA_ERR_PARAM_INVALID;
+    if (qa.count != 1 && qa.count != N * D) return IFA_ERR_PARAM_INVALID;
+    return IFA_OK;
+}
+
 int check_common(const void *q, const void *out, int dq, int dkv, int dout, const char *layout, int64_t B, int64_t N,
                  int64_t Nkv_in, int64_t D, double scale, const void *mask, int dmask, int64_t mB, int64_t mN,
                  const void *pse, int64_t pse_b, const void *aqs, const void *aqo, int aq_mode,
                  int64_t split_tokens, IfaCommon *c) {
     if (!q || !out) return IFA_ERR_PARAM_NULLPTR;
-    if (!is_float_dt(dq) || dout != dq) return IFA_ERR_PARAM_INVALID;
+    if (!is_float_dt(dq) || (dout != dq && dout != IFA_DT_I8)) return IFA_ERR_PARAM_INVALID;
     if (dkv != dq && dkv != IFA_DT_I8) return IFA_ERR_PARAM_INVALID;
     if (parse_layout(layout, &c->layout) != IFA_OK) return IFA_ERR_PARAM_INVALID;
     if (B < 1 || B > 65536 || N < 1 || N > 256) return IFA_ERR_PARAM_INVALID;
@@ -174,6 +189,28 @@ int check_common(const void *q, const void *out, int dq, int dkv, int dout, cons
 
 int kv_kind(int dkv) { return dkv == IFA_DT_F16 ? KV_F16 : dkv == IFA_DT_BF16 ? KV_BF16 : KV_I8; }
 
+QuantArgs dense_quant(const ifa_decode_args *a) {
+    QuantArgs q;
+    if (a->struct_size >= sizeof(ifa_decode_args)) {
+        q.scale = a->quant_scale2;
+        q.offset = a->quant_offset2;
+        q.count = a->quant_count;
+        q.dtype = a->dtype_quant;
+    }
+    return q;
+}
+
+QuantArgs paged_quant(const ifa_paged_args *a) {
+    QuantArgs q;
+    if (a->struct_size >= sizeof(ifa_paged_args)) {
+        q.scale = a->quant_scale2;
+        q.offset = a->quant_offset2;
+        q.count = a->quant_count;
+        q.dtype = a->dtype_quant;
+    }
+    return q;
+}
+
 int plan_dense(const ifa_decode_args *a, IfaPlan &p, IfaCommon &c) {
     if (!a) return IFA_ERR_PARAM_NULLPTR;
     if (a->struct_size < offsetof(ifa_decode_args, pse_batch)) return IFA_ERR_PARAM_INVALID;
@@ -186,7 +223,7 @@ int plan_dense(const ifa_decode_args *a, IfaPlan &p, IfaCommon &c) {
                           a->antiquant_mode, a->split_tokens, &c);
     if (rc) return rc;
     // per-batch caches (tensor lists), from ABI version 4 on
-    const bool has_lists = a->struct_size >= sizeof(ifa_decode_args);
+    const bool has_lists = a->struct_size >= offsetof(ifa_decode_args, quant_scale2);
     const bool lists = has_lists && (a->key_list || a->value_list || a->kv_list_seq_len);
     if (lists) {
         if (!a->key_list || !a->value_list || !a->kv_list_seq_len) return IFA_ERR_PARAM_NULLPTR;
@@ -198,6 +235,8 @@ int plan_dense(const ifa_decode_args *a, IfaPlan &p, IfaCommon &c) {
         if (!a->key || !a->value) return IFA_ERR_PARAM_NULLPTR;
         p.list_seq.clear();
     }
+    rc = check_quant(a->dtype_q, a->dtype_out, a->num_heads, a->head_dim, dense_quant(a));
+    if (rc) return rc;
     const int64_t S = lists ? 0 : a->kv_seq_len;
     if (!lists && (S < 1 || S > (int64_t)1 << 30)) return IFA_ERR_PARAM_INVALID;
     if (a->kv_padding_size && a->kv_padding_size_count != 1 && a->kv_padding_size_count != a->batch)
@@ -239,7 +278,7 @@ int plan_dense(const ifa_decode_args *a, IfaPlan &p, IfaCommon &c) {
 int plan_paged(const ifa_paged_args *a, IfaPlan &p, IfaCommon &c) {
     if (!a) return IFA_ERR_PARAM_NULLPTR;
     if (a->struct_size < offsetof(ifa_paged_args, pse_batch)) return IFA_ERR_PARAM_INVALID;
-    const bool has_pse_dims = a->struct_size >= sizeof(ifa_paged_args);
+    const bool has_pse_dims = a->struct_size >= offsetof(ifa_paged_args, quant_scale2);
     if (a->pse_shift && !has_pse_dims) return IFA_ERR_PARAM_INVALID;
     int rc = check_common(a->query, a->attention_out, a->dtype_q, a->dtype_kv, a->dtype_out, a->input_layout,
                           a->batch, a->num_heads, a->num_key_value_heads, a->head_dim, a->scale_value, a->atten_mask,
@@ -248,6 +287,8 @@ int plan_paged(const ifa_paged_args *a, IfaPlan &p, IfaCommon &c) {
                           a->antiquant_mode, a->split_tokens, &c);
     if (rc) return rc;
     if (!a->key_cache || !a->value_cache || !a->block_table || !a->actual_seq_lengths) return IFA_ERR_PARAM_NULLPTR;
+    rc = check_quant(a->dtype_q, a->dtype_out, a->num_heads, a->head_dim, paged_quant(a));
+    if (rc) return rc;
     const int64_t bs = a->block_size;
     const int align = a->dtype_kv == IFA_DT_I8 ? 32 : 16;
     if (bs < 16 || bs > 512 || bs % align) return IFA_ERR_PARAM_INVALID;
@@ -306,6 +347,8 @@ struct Launch {
     const void *const *k_list;
     const void *const *v_list;
     int list_bnsd;
+    QuantArgs quant;
+    bool out_i8;
     bool q_bf16;
     double scale;
     hipEvent_t ev_begin, ev_end;
@@ -366,6 +409,11 @@ int run(const IfaPlan &p, const Launch &L, void *ws, size_t ws_bytes, hipStream_
     cp.D = p.D;
     cp.out_bf16 = L.q_bf16;
     cp.aq_mode = L.aq_mode;
+    cp.out_i8 = L.out_i8;
+    cp.q_scale2 = L.quant.scale;
+    cp.q_offset2 = L.quant.offset;
+    cp.q2_bf16 = L.quant.dtype == IFA_DT_BF16;
+    cp.q2_per_channel = L.quant.count > 1;
 
     const bool timed = L.ev_begin && L.ev_end;
     if (timed && hipEventRecord(L.ev_begin, stream) != hipSuccess) return IFA_ERR_RUNTIME;
@@ -436,6 +484,8 @@ Launch dense_launch(const ifa_decode_args *a, const IfaPlan &p, const IfaCommon 
     L.aq_mode = a->dtype_kv == IFA_DT_I8 ? a->antiquant_mode : 0;
     L.q_bf16 = a->dtype_q == IFA_DT_BF16;
     L.scale = a->scale_value;
+    L.out_i8 = a->dtype_out == IFA_DT_I8;
+    L.quant = dense_quant(a);
     L.ev_begin = reinterpret_cast<hipEvent_t>(a->profile_event_begin);
     L.ev_end = reinterpret_cast<hipEvent_t>(a->profile_event_end);
     return L;
@@ -477,6 +527,8 @@ Launch paged_launch(const ifa_paged_args *a, const IfaPlan &p) {
     L.aq_mode = a->dtype_kv == IFA_DT_I8 ? a->antiquant_mode : 0;
     L.q_bf16 = a->dtype_q == IFA_DT_BF16;
     L.scale = a->scale_value;
+    L.out_i8 = a->dtype_out == IFA_DT_I8;
+    L.quant = paged_quant(a);
     L.ev_begin = reinterpret_cast<hipEvent_t>(a->profile_event_begin);
     L.ev_end = reinterpret_cast<hipEvent_t>(a->profile_event_end);
     return L;

@@ -1,7 +1,7 @@
 // Split-combine kernel: merges the partial softmax states of one (b, h) row
 // in a fixed order (deterministic: same inputs, same bits), divides by the
 // softmax denominator, applies the V antiquant epilogue and rounds the fp32
-// result to nearest-even into the query dtype.
+// result to nearest-even into the query dtype, or quantises it to int8.
 //
 //   M = max_i m_i,  out = sum_i 2^(m_i - M) acc_i / sum_i 2^(m_i - M) l_i
 //
@@ -17,6 +17,11 @@ namespace {
 __device__ __forceinline__ float ld_param(const void *p, int64_t i, bool bf16) {
     const uint32_t bits = reinterpret_cast<const uint16_t *>(p)[i];
     return bf16 ? __builtin_bit_cast(float, bits << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+}
+
+__device__ __forceinline__ float ld_q2(const void *p, int64_t i, int bf16) {
+    if (bf16) return __builtin_bit_cast(float, (uint32_t)reinterpret_cast<const uint16_t *>(p)[i] << 16);
+    return reinterpret_cast<const float *>(p)[i];
 }
 
 // Maximum over the 64 lanes: DPP within each 16-lane row, then the four row
@@ -135,10 +140,18 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineParams P) {
             }
         }
         const int64_t oi = (b * P.N + h) * D + d;
-        if (bf)
+        if (P.out_i8) {
+            // int8 output: y = res * s + t on the fp32 result, ties to even, saturated
+            const int64_t ci = P.q2_per_channel ? (int64_t)h * D + d : 0;
+            const float qs = ld_q2(P.q_scale2, ci, P.q2_bf16);
+            const float qo = P.q_offset2 ? ld_q2(P.q_offset2, ci, P.q2_bf16) : 0.f;
+            const float y = fminf(fmaxf(__builtin_rintf(fmaf(res, qs, qo)), -128.f), 127.f);
+            reinterpret_cast<int8_t *>(P.out)[oi] = (int8_t)(int)y;
+        } else if (bf) {
             reinterpret_cast<__bf16 *>(P.out)[oi] = (__bf16)res;
-        else
+        } else {
             reinterpret_cast<_Float16 *>(P.out)[oi] = (_Float16)res;
+        }
     }
 }
 

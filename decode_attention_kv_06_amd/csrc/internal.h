@@ -74,6 +74,10 @@ struct CombineParams {
     int32_t N, Nkv, g, G, n_hg, D;
     int32_t out_bf16;
     int32_t aq_mode;
+    int32_t out_i8;         // int8 output: quantise with (q_scale2, q_offset2)
+    int32_t q2_bf16;        // quant parameters are bf16 (else fp32)
+    int32_t q2_per_channel; // one parameter per output channel h * D + d (else one for all)
+    const void *q_scale2, *q_offset2;
     int32_t nb, b0;
     int64_t pre[kSliceBatches + 1];
     int32_t len[kSliceBatches];

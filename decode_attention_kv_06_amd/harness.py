@@ -24,6 +24,8 @@ def to_device(inp: dict, device: str = "cuda") -> dict:
 
 
 def alloc_out(inp: dict) -> torch.Tensor:
+    if inp.get("quant_scale2") is not None:
+        return torch.empty(inp["q"].shape, dtype=torch.int8, device=inp["q"].device)
     return torch.empty_like(inp["q"])
 
 
@@ -46,6 +48,7 @@ def call(dev: dict, out: torch.Tensor, split: int = 0, workspace=None, stream=No
     common = dict(num_heads=s.N, num_key_value_heads=s.Nkv, input_layout=s.layout, scale_value=s.scale_value,
                   actual_seq_lengths=dev["actual_seq_lengths"], atten_mask=dev["mask"], pse_shift=dev.get("pse"),
                   antiquant_scale=dev["aq_scale"], antiquant_offset=dev["aq_offset"], antiquant_mode=dev["aq_mode"],
+                  quant_scale2=dev.get("quant_scale2"), quant_offset2=dev.get("quant_offset2"),
                   split_tokens=split, workspace=workspace, stream=stream)
     if s.paged:
         return binding.ifa_decode_paged(dev["q"], dev["k"], dev["v"], out, dev["block_table"],

@@ -12,7 +12,7 @@ order in which tensors are made.  Tensor ids:
     0 lengths  1 q  2 k  3 v  4 mask  5 block permutation  6 padding offsets
     7 antiquant scale  8 antiquant offset  9 q_rope  10 k_rope
     11 sparse valid counts  12 sparse indices  13 positional bias (pseShift)
-    14 per-batch cache lengths of tensor lists
+    14 per-batch cache lengths of tensor lists  15 output quant scale  16 output quant offset
 
 Normals are float32 ``standard_normal`` draws rounded to nearest-even into
 fp16/bf16; integers are uniform and inclusive.  Whole buffers are filled,
@@ -32,8 +32,9 @@ TID_LEN, TID_Q, TID_K, TID_V, TID_MASK, TID_PERM, TID_PAD = 0, 1, 2, 3, 4, 5, 6
 TID_AQ_SCALE, TID_AQ_OFFSET, TID_QROPE, TID_KROPE, TID_NVALID, TID_IDX = 7, 8, 9, 10, 11, 12
 TID_PSE = 13
 TID_LIST = 14
+TID_QSCALE2, TID_QOFFSET2 = 15, 16
 
-_TORCH_DT = {"f16": torch.float16, "bf16": torch.bfloat16, "i8": torch.int8}
+_TORCH_DT = {"f16": torch.float16, "bf16": torch.bfloat16, "i8": torch.int8, "f32": torch.float32}
 _CHUNK = 1 << 24
 
 
@@ -111,6 +112,12 @@ class IfaSpec:
     # S_b = L_b + U{0..list_slack} positions (at most S), cut from the padded one
     kv_list: bool = False
     list_slack: int = 16
+    # int8 output (post-quantisation): quantScale2 ~ U[qs_range], quantOffset2 ~ U[qo_range]
+    out_int8: Optional[str] = None       # None | "per_tensor" | "per_channel"
+    quant_dtype: str = "f32"             # "f32" | "bf16"
+    quant_offset: bool = True
+    qs_range: tuple = (100.0, 400.0)
+    qo_range: tuple = (-8.0, 8.0)
 
     @property
     def nkv(self) -> int:
@@ -248,6 +255,15 @@ def make_ifa(spec: IfaSpec) -> dict:
         out["k_list"] = [cut(out["k"], b, int(seq[b])).contiguous() for b in range(B)]
         out["v_list"] = [cut(out["v"], b, int(seq[b])).contiguous() for b in range(B)]
         out["list_seq"] = seq
+
+    if spec.out_int8 is not None:
+        n = 1 if spec.out_int8 == "per_tensor" else N * D
+        qdt = "f32" if spec.quant_dtype == "f32" else "bf16"
+        out["quant_scale2"] = uniform_tensor(rng_for(k_id, TID_QSCALE2), (n,), *spec.qs_range, qdt)
+        out["quant_offset2"] = (uniform_tensor(rng_for(k_id, TID_QOFFSET2), (n,), *spec.qo_range, qdt)
+                                if spec.quant_offset else None)
+    else:
+        out["quant_scale2"] = out["quant_offset2"] = None
 
     if spec.antiquant is not None:
         shp = (2,) if spec.antiquant == "per_tensor" else (2, nkv, 1, D)

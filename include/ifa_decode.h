@@ -76,7 +76,8 @@ enum {
     IFA_DT_BF16 = 2, /* bfloat16 */
     IFA_DT_I8 = 3,   /* int8 (KV cache with antiquant; or mask) */
     IFA_DT_U8 = 4,   /* uint8 (mask) */
-    IFA_DT_BOOL = 5  /* one byte per element, 0 or 1 (mask) */
+    IFA_DT_BOOL = 5, /* one byte per element, 0 or 1 (mask) */
+    IFA_DT_F32 = 6   /* IEEE binary32 (output quantisation parameters) */
 };
 
 enum { IFA_ANTIQUANT_NONE = 0, IFA_ANTIQUANT_PER_TENSOR = 1, IFA_ANTIQUANT_PER_CHANNEL = 2 };
@@ -113,8 +114,16 @@ enum { IFA_ANTIQUANT_NONE = 0, IFA_ANTIQUANT_PER_TENSOR = 1, IFA_ANTIQUANT_PER_C
  *   two last fields of the struct; a struct_size that stops before them means
  *   no positional bias (pse_shift must then be NULL).
  * Envelope: 1 <= B <= 65536, 1 <= N <= 256, N % N_kv == 0,
- *   head_dim in {64, 128, 256, 512}, dtype_out == dtype_q, dtype_kv ==
- *   dtype_q or IFA_DT_I8.
+ *   head_dim in {64, 128, 256, 512}, dtype_out == dtype_q or IFA_DT_I8,
+ *   dtype_kv == dtype_q or IFA_DT_I8.
+ * Int8 output (dtype_out IFA_DT_I8; README "Constraints": quantScale2
+ *   required, quantOffset2 optional, per-tensor or per-channel, fp32, or bf16
+ *   with bf16 inputs): each output element o of head h, column d becomes
+ *   clamp(round_half_even(o * s[c] + t[c]), -128, 127), c = 0 per-tensor or
+ *   h * head_dim + d per-channel, o being the fp32 result before any
+ *   rounding (the formula, the rounding and the saturation are this
+ *   library's reading: the pages give none).  The quant fields are the last
+ *   of each struct (ABI version 5) and must be NULL/0 for a float output.
  * key_list / value_list / kv_list_seq_len (all three, or none): the tensor
  *   lists of the V2 page ("Constraints", non-contiguous case): batch b reads
  *   its own key and value tensors, each of batch 1, kv_list_seq_len[b]
@@ -159,6 +168,10 @@ typedef struct ifa_decode_args {
     const void *const *key_list;    /* per-batch caches: device array of `batch` device pointers */
     const void *const *value_list;
     const int64_t *kv_list_seq_len; /* host int64[batch]: positions of each list tensor */
+    const void *quant_scale2;       /* int8 output: quantScale2, device, quant_count values */
+    const void *quant_offset2;      /* int8 output: quantOffset2 or NULL, same dtype and count */
+    int64_t quant_count;            /* 1 (per-tensor) or num_heads * head_dim (per-channel) */
+    int32_t dtype_quant;            /* IFA_DT_F32, or IFA_DT_BF16 with bf16 inputs */
 } ifa_decode_args;
 
 /*
@@ -203,6 +216,10 @@ typedef struct ifa_paged_args {
     void *profile_event_begin; /* as in ifa_decode_args */
     void *profile_event_end;
     int64_t pse_batch, pse_seq; /* as in ifa_decode_args */
+    const void *quant_scale2;   /* int8 output, as in ifa_decode_args */
+    const void *quant_offset2;
+    int64_t quant_count;
+    int32_t dtype_quant;
 } ifa_paged_args;
 
 /*

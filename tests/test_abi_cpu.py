@@ -343,3 +343,26 @@ def test_dense_kv_lists_batch_limit():
     seq = (ctypes.c_int64 * 257)(*([64] * 257))
     a = list_args(batch=257, kv_list_seq_len=ctypes.cast(seq, ctypes.c_void_p))
     assert ws_size("ifa_decode_workspace_size", a)[0] == 161002
+
+
+# ---------------------------------------------------------------- int8 output
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype_out=bd.DT_I8, quant_scale2=FAKE, quant_count=1, dtype_quant=bd.DT_F32), 0),
+    (dict(dtype_out=bd.DT_I8, quant_scale2=FAKE, quant_offset2=FAKE, quant_count=8 * 128, dtype_quant=bd.DT_BF16), 0),
+    (dict(dtype_out=bd.DT_I8), 161001),                                             # quantScale2 required
+    (dict(dtype_out=bd.DT_I8, quant_scale2=FAKE, quant_count=2 * 128, dtype_quant=bd.DT_F32), 161002),
+    (dict(dtype_out=bd.DT_I8, quant_scale2=FAKE, quant_count=1, dtype_quant=bd.DT_F16), 161002),
+    (dict(dtype_q=bd.DT_F16, dtype_kv=bd.DT_F16, dtype_out=bd.DT_I8, quant_scale2=FAKE, quant_count=1,
+          dtype_quant=bd.DT_BF16), 161002),                                         # bf16 only with bf16 inputs
+    (dict(quant_scale2=FAKE, quant_count=1, dtype_quant=bd.DT_F32), 161002),        # float output takes none
+    (dict(dtype_out=bd.DT_I8, quant_scale2=FAKE, quant_count=1, dtype_quant=bd.DT_F32,
+          struct_size=bd.IfaDecodeArgs.quant_scale2.offset), 161001),               # fields invisible
+])
+def test_dense_int8_output_validation(kw, code):
+    assert ws_size("ifa_decode_workspace_size", dense_args(**kw))[0] == code
+
+
+def test_paged_int8_output_validation():
+    ok = paged_args(dtype_out=bd.DT_I8, quant_scale2=FAKE, quant_count=4 * 64, dtype_quant=bd.DT_F32)
+    assert ws_size("ifa_decode_paged_workspace_size", ok)[0] == 0
+    assert ws_size("ifa_decode_paged_workspace_size", paged_args(dtype_out=bd.DT_I8))[0] == 161001
