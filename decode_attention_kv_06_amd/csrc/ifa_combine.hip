@@ -68,7 +68,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineParams P) {
     }
     // partial state i of this head lives at row (slot0 + i) * G + hh
     auto prow = [&](int i) -> int64_t { return (slot0 + i) * P.G + hh; };
-    const float2 *ml = reinterpret_cast<const float2 *>(P.part_ml);
+    // (m, l) pairs read as 64-bit words through a global pointer (no flat loads)
+    typedef __attribute__((address_space(1))) const uint64_t gu64;
+    gu64 *mlw = (gu64 *)P.part_ml;
+    auto ml = [&](int64_t r) { return __builtin_bit_cast(float2, (uint64_t)mlw[r]); };
 
     // (m, l) of up to 64 splits in one load round, lane i holding split i
     const bool bf = P.out_bf16 != 0;
@@ -92,19 +95,19 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineParams P) {
         }
     };
     float2 ml0 = make_float2(-__builtin_huge_valf(), 0.f);
-    if (lane < nch) ml0 = ml[prow(lane)];
+    if (lane < nch) ml0 = ml(prow(lane));
     if (nch > 0) load_acc(0, nch);
     M = ml0.x;
     for (int i0 = 64; i0 < nch; i0 += 64) {
         const int i = i0 + lane;
-        if (i < nch) M = fmaxf(M, ml[prow(i)].x);
+        if (i < nch) M = fmaxf(M, ml(prow(i)).x);
     }
     M = wave_max(M);
     for (int i0 = 0; i0 < nch; i0 += 64) {
         const int cnt = min(64, nch - i0);
         float w = 0.f, lw = 0.f;
         if (lane < cnt) {
-            const float2 mv = i0 == 0 ? ml0 : ml[prow(i0 + lane)];
+            const float2 mv = i0 == 0 ? ml0 : ml(prow(i0 + lane));
             w = __builtin_amdgcn_exp2f(mv.x - M);
             lw = w * mv.y;
         }
