@@ -341,10 +341,17 @@ void split_kernel(const SplitParams P) {
         // Rolling pipeline with one tile resident: the K rows of tile k+1 are
         // requested as soon as QK of tile k has consumed the K registers, and
         // its V rows as soon as PV of tile k has consumed the V registers.
+        // With a mask, the mask bytes run one tile further ahead, so the rows
+        // every head of the group excludes are never read: their registers
+        // keep the previous tile's (finite) values, and their p is 0.
         constexpr int MB = MASKED ? G : 1;
         uint32_t kr[RT][W], vr[RT][W];
+#pragma unroll
+        for (int i = 0; i < RT; i++)
+#pragma unroll
+            for (int w = 0; w < W; w++) kr[i][w] = vr[i][w] = 0u;
         bool okr[RT];
-        uint32_t mbr[MB];       // mask byte of position ts + lane (per head for per-head masks)
+        uint32_t mbr[MB];       // mask byte of position ts + lane (per head for per-head masks), one tile ahead
         uint32_t pbr[PR][PH];   // pseShift bits: scatter path of ts + i*RPI + r, else of ts + lane
         int64_t offs[RT];       // paged: byte offsets of the tile's rows
 
@@ -356,9 +363,12 @@ void split_kernel(const SplitParams P) {
         // per SIMD) are the exception: there the flat loads, waited for all at
         // once, measured 4-6 % faster on BSH caches and no slower on BNSD ones.
         constexpr bool kFlatRows = !PAGED && EXTRA == EX_NONE && !I8 && (G == 2 || G == 4);
-        auto load_rows = [&](const char *const (&ptr)[RT], uint32_t (&dst)[RT][W]) {
+        auto load_rows = [&](const char *const (&ptr)[RT], uint32_t (&dst)[RT][W], uint64_t skip) {
 #pragma unroll
             for (int i = 0; i < RT; i++) {
+                if constexpr (MASKED) {
+                    if ((skip >> (i * RPI + r)) & 1) continue;     // excluded for every head: not read
+                }
                 if constexpr (W == 4) {
                     const u32x4 x = kFlatRows ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(ptr[i]))
                                               : __builtin_nontemporal_load((const gu32x4 *)ptr[i]);
@@ -383,7 +393,7 @@ void split_kernel(const SplitParams P) {
                 for (int i = 0; i < RT; i++) ptr[i] = base + offs[i];
             }
         };
-        auto issue_k = [&](int ts) {
+        auto issue_k = [&](int ts, uint64_t skip) {
             if constexpr (PAGED) {
 #pragma unroll
                 for (int i = 0; i < RT; i++) {
@@ -400,6 +410,12 @@ void split_kernel(const SplitParams P) {
                     offs[i] = okr[i] ? (int64_t)(uint32_t)blk * blk_b + (head_b + rr * row_b) + lane_byte : 0;
                 }
             }
+            const char *ptr[RT];
+            row_ptrs(ts, PAGED ? kb : kp, ptr);
+            load_rows(ptr, kr, skip);
+        };
+        // mask bytes of the tile at ts: position ts + lane, lanes < TT
+        auto load_mask = [&](int ts) {
             if constexpr (MASKED) {
                 const int tm = min(ts + lane, hi - 1);
 #pragma unroll
@@ -411,9 +427,28 @@ void split_kernel(const SplitParams P) {
                     mbr[hh] = v;
                 }
             }
-            const char *ptr[RT];
-            row_ptrs(ts, PAGED ? kb : kp, ptr);
-            load_rows(ptr, kr);
+        };
+        // the loaded mask bytes as per-head bitmaps (bit = position in the tile),
+        // and the positions that every real head of the group excludes
+        auto mask_bits = [&](uint64_t (&bits)[MB]) -> uint64_t {
+            uint64_t all = 0;
+            if constexpr (MASKED) {
+                if (P.mask_mode == 1) {
+                    bits[0] = __ballot(mbr[0] != 0);
+#pragma unroll
+                    for (int hh = 1; hh < MB; hh++) bits[hh] = bits[0];
+                    all = bits[0];
+                } else {
+                    all = ~0ull;
+#pragma unroll
+                    for (int hh = 0; hh < MB; hh++) {
+                        bits[hh] = __ballot(mbr[hh] != 0);
+                        if (hg * G + hh < P.g) all &= bits[hh];
+                    }
+                    if (P.mask_mode == 0) all = 0;
+                }
+            }
+            return all;
         };
         auto issue_pse = [&](int ts) {
             if constexpr (PSE && SCATTER) {
@@ -428,10 +463,10 @@ void split_kernel(const SplitParams P) {
         auto pse_log2 = [&](uint32_t bits) {
             return (pse_bf16 ? bf16_to_f32(bits) : f16_to_f32(bits)) * kLog2e;
         };
-        auto issue_v = [&](int ts) {
+        auto issue_v = [&](int ts, uint64_t skip) {
             const char *ptr[RT];
             row_ptrs(ts, PAGED ? vb : vp_, ptr);
-            load_rows(ptr, vr);
+            load_rows(ptr, vr, skip);
         };
 
         float m[G], l[G], acc[G][8];
@@ -446,8 +481,19 @@ void split_kernel(const SplitParams P) {
 
         // -------------------------------------------------- main loop
         int ts = lo;
-        issue_k(ts);
-        issue_v(ts);
+        uint64_t mcur[MB], mnext[MB];     // per-head mask bitmaps of this tile and the next
+        uint64_t skip_cur = 0, skip_next = 0;
+#pragma unroll
+        for (int hh = 0; hh < MB; hh++) mcur[hh] = mnext[hh] = 0;
+        if constexpr (MASKED) {
+            load_mask(ts);
+            skip_cur = mask_bits(mcur);
+        }
+        issue_k(ts, skip_cur);
+        if constexpr (MASKED) {
+            if (ts + TT < hi) load_mask(ts + TT);
+        }
+        issue_v(ts, skip_cur);
         issue_pse(ts);
         while (true) {
             // QK: partial dot products of the resident K rows, then the DPP
@@ -519,22 +565,20 @@ void split_kernel(const SplitParams P) {
             // validity bitmaps of the tile, taken before the next tile's
             // loads reuse the registers
             uint64_t mbits[MB];
-            if constexpr (MASKED) {
-                if (P.mask_mode == 1) {
-                    mbits[0] = __ballot(mbr[0] != 0);
 #pragma unroll
-                    for (int hh = 1; hh < MB; hh++) mbits[hh] = mbits[0];
-                } else {
-#pragma unroll
-                    for (int hh = 0; hh < MB; hh++) mbits[hh] = __ballot(mbr[hh] != 0);
-                }
-            }
+            for (int hh = 0; hh < MB; hh++) mbits[hh] = mcur[hh];
             bool okc[RT];
 #pragma unroll
             for (int i = 0; i < RT; i++) okc[i] = PAGED ? okr[i] : true;
 
             const bool more = ts + TT < hi;
-            if (more) issue_k(ts + TT);
+            if (more) {
+                if constexpr (MASKED) {
+                    skip_next = mask_bits(mnext);          // the mask loaded one tile ago
+                    if (ts + 2 * TT < hi) load_mask(ts + 2 * TT);
+                }
+                issue_k(ts + TT, skip_next);
+            }
 
             if constexpr (SCATTER) {
                 // this lane's head: mask bitmap, scale, online softmax, then
@@ -656,7 +700,9 @@ void split_kernel(const SplitParams P) {
                 }
             }
             if (!more) break;
-            issue_v(ts + TT);
+            issue_v(ts + TT, skip_next);
+#pragma unroll
+            for (int hh = 0; hh < MB; hh++) mcur[hh] = mnext[hh];
             ts += TT;
         }
 
