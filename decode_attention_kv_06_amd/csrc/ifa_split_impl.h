@@ -56,32 +56,38 @@ template <int N>
 __device__ __forceinline__ float row_bcast(float x) { return dpp<0x150 + N>(x); }
 
 // Reduce-scatter of G per-lane partial sums over the 16 lanes of a DPP row.
-// Each level pairs lanes differing in one lane bit (row mirror: bit 3, half
-// mirror: bit 2, quad xor 2: bit 1) and halves the heads a lane keeps: the
-// lane with the bit set keeps the upper half and sends the lower half.  After
-// log2(G) levels lane c holds one head, head_of_lane(c); the remaining in-row
-// levels (and the cross-row ones for rows longer than 16 lanes) are plain.
-template <int CTRL, int BIT, int N>
-__device__ __forceinline__ void scatter_level(float (&v)[8], int lane) {
-    const bool up = (lane >> BIT) & 1;
+// Each level pairs every lane with the lane a DPP pattern names (row mirror:
+// lane bits 0-3 flipped; half mirror: bits 0-2; quad swap: bit 1), adds the
+// partner's upper half of the remaining registers to its own lower half, and
+// so halves the heads a lane keeps.  No lane-dependent select is needed: the
+// lanes hold their heads in a lane-dependent order, register p of lane l
+// holding head p ^ head_code(l), with the code's bits (top first) b3, b2^b3,
+// b1^b2 of the lane number.  Each pattern flips exactly the code bit of its
+// level, so a lane's partner always holds the lane's kept heads in the
+// registers it sends.  After log2(G) levels lane l holds head head_code(l);
+// the remaining in-row levels (and the cross-row ones for rows longer than
+// 16 lanes) are plain sums, which leave the code unchanged.
+template <int G>
+__host__ __device__ constexpr int head_code(int lane) {
+    const int b1 = (lane >> 1) & 1, b2 = (lane >> 2) & 1, b3 = (lane >> 3) & 1;
+    return G == 2 ? b3 : G == 4 ? (b3 << 1) | (b2 ^ b3) : G == 8 ? (b3 << 2) | ((b2 ^ b3) << 1) | (b1 ^ b2) : 0;
+}
+template <int CTRL, int N>
+__device__ __forceinline__ void scatter_level(float (&v)[8]) {
 #pragma unroll
-    for (int j = 0; j < N / 2; j++) {
-        const float keep = up ? v[j + N / 2] : v[j];
-        const float send = up ? v[j] : v[j + N / 2];
-        v[j] = keep + dpp<CTRL>(send);
-    }
+    for (int j = 0; j < N / 2; j++) v[j] += dpp<CTRL>(v[j + N / 2]);
 }
 template <int G, int LPR>
-__device__ __forceinline__ float scatter_reduce(const float (&s)[G], int lane) {
+__device__ __forceinline__ float scatter_reduce(const float (&s)[G]) {
     static_assert(G == 2 || G == 4 || G == 8, "head group");
     static_assert(LPR >= 16, "whole DPP rows");
     float v[8];
 #pragma unroll
     for (int h = 0; h < G; h++) v[h] = s[h];
-    scatter_level<0x140, 3, G>(v, lane);
-    if constexpr (G >= 4) scatter_level<0x141, 2, G / 2>(v, lane);
+    scatter_level<0x140, G>(v);
+    if constexpr (G >= 4) scatter_level<0x141, G / 2>(v);
     else v[0] += dpp<0x141>(v[0]);
-    if constexpr (G >= 8) scatter_level<0x4E, 1, G / 4>(v, lane);
+    if constexpr (G >= 8) scatter_level<0x4E, G / 4>(v);
     else v[0] += dpp<0x4E>(v[0]);
     v[0] += dpp<0xB1>(v[0]);
     if constexpr (LPR >= 32) v[0] += swz_xor16(v[0]);
@@ -89,16 +95,15 @@ __device__ __forceinline__ float scatter_reduce(const float (&s)[G], int lane) {
     return v[0];
 }
 template <int G>
-__device__ __forceinline__ int head_of_lane(int lane) {
-    int h = ((lane >> 3) & 1) * (G / 2);
-    if constexpr (G >= 4) h += ((lane >> 2) & 1) * (G / 4);
-    if constexpr (G >= 8) h += (lane >> 1) & 1;
-    return h;
-}
-// the lane of a DPP row that holds head H after scatter_reduce
+__device__ __forceinline__ int head_of_lane(int lane) { return head_code<G>(lane); }
+// a lane of a DPP row that holds head H after scatter_reduce (lane bit 0 clear)
 template <int G, int H>
 constexpr int lane_of_head() {
-    return ((H / (G / 2)) & 1) * 8 + (G >= 4 ? ((H / (G >= 4 ? G / 4 : 1)) & 1) * 4 : 0) + (G >= 8 ? (H & 1) * 2 : 0);
+    constexpr int b3 = G == 2 ? H : G == 4 ? H >> 1 : H >> 2;
+    constexpr int b2 = G == 4 ? (H & 1) ^ b3 : G == 8 ? ((H >> 1) & 1) ^ b3 : 0;
+    constexpr int b1 = G == 8 ? (H & 1) ^ b2 : 0;
+    static_assert(head_code<G>(8 * b3 + 4 * b2 + 2 * b1) == H, "head code inverse");
+    return 8 * b3 + 4 * b2 + 2 * b1;
 }
 // every head's value from the lanes that hold them
 template <int G, int H = 0>
@@ -222,13 +227,16 @@ void split_kernel(const SplitParams P) {
 
         // ------------------------------------------------------ query
         const int hbase = j * P.g + hg * G;
+        // register hh of the query holds head hh ^ hl on the scatter path (the
+        // lane-dependent order its reduce-scatter needs), head hh otherwise
         uint32_t qv[G][4];
         float qmul = P.score_mul;
         if constexpr (!I8) {
 #pragma unroll
             for (int hh = 0; hh < G; hh++) {
-                const bool ok = hg * G + hh < P.g;
-                const int64_t off = ((b * P.N + hbase + (ok ? hh : 0)) * D + 8 * c) * 2;
+                const int hq = SCATTER ? hh ^ hl : hh;
+                const bool ok = hg * G + hq < P.g;
+                const int64_t off = ((b * P.N + hbase + (ok ? hq : 0)) * D + 8 * c) * 2;
                 u32x4 x = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(P.q) + off);
 #pragma unroll
                 for (int w = 0; w < 4; w++) qv[hh][w] = ok ? x[w] : 0u;
@@ -242,8 +250,9 @@ void split_kernel(const SplitParams P) {
             float amax = 0.f;
 #pragma unroll
             for (int hh = 0; hh < G; hh++) {
-                const bool ok = hg * G + hh < P.g;
-                const int64_t off = ((b * P.N + hbase + (ok ? hh : 0)) * D + 8 * c) * 2;
+                const int hq = SCATTER ? hh ^ hl : hh;
+                const bool ok = hg * G + hq < P.g;
+                const int64_t off = ((b * P.N + hbase + (ok ? hq : 0)) * D + 8 * c) * 2;
                 const u32x4 x = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(P.q) + off);
 #pragma unroll
                 for (int e = 0; e < 8; e++) {
@@ -523,7 +532,7 @@ void split_kernel(const SplitParams P) {
             float x[RT];        // scatter path: this lane's head, per row step
             if constexpr (SCATTER) {
 #pragma unroll
-                for (int i = 0; i < RT; i++) x[i] = scatter_reduce<G, LPR>(s[i], lane);
+                for (int i = 0; i < RT; i++) x[i] = scatter_reduce<G, LPR>(s[i]);
             }
             if constexpr (!SCATTER && LPR >= 2) {
 #pragma unroll
