@@ -121,6 +121,20 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c, std::inte
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c, false);
 }
 
+// The first product of a dot-product chain, written as the three-operand
+// form with an inline 0 accumulator: the compiler otherwise picks the
+// two-operand accumulate form and spends a v_mov per chain to zero it.
+__device__ __forceinline__ float dot2_first(uint32_t a, uint32_t b, std::integral_constant<int, KV_BF16>) {
+    float r;
+    asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+__device__ __forceinline__ float dot2_first(uint32_t a, uint32_t b, std::integral_constant<int, KV_F16>) {
+    float r;
+    asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
 __device__ __forceinline__ uint32_t pack_p(float a, float b, std::integral_constant<int, KV_BF16>) {
     bf16x2 r;
     r[0] = (__bf16)a;
@@ -523,7 +537,7 @@ void split_kernel(const SplitParams P) {
                 }
 #pragma unroll
                 for (int hh = 0; hh < G; hh++) {
-                    float a = dot2(qv[hh][0], kk[0], 0.f, DotK{});
+                    float a = dot2_first(qv[hh][0], kk[0], DotK{});
 #pragma unroll
                     for (int w = 1; w < 4; w++) a = dot2(qv[hh][w], kk[w], a, DotK{});
                     s[i][hh] = a;
