@@ -768,10 +768,291 @@ void split_kernel(const SplitParams P) {
     }   // segments
 }
 
+// int8 cache, D = 128, head groups of 8, dense, no mask or bias: the
+// query-key products run on the matrix cores.  The query, scaled by K's
+// antiquant scale and a power of two to |q'| < 2^14 and rounded to an
+// integer, is split into q' = 128 a + b with a in [-128, 127], b in [0, 127];
+// two v_mfma_i32_16x16x64_i8 products per 64 dimensions (a and b parts
+// against the raw int8 keys) give the exact integer score 128 A + B of 16
+// rows x 16 heads (8 real) per tile, with no byte widening of K at all.
+// Lane (n, g) of the result holds row n of heads 4g .. 4g+3: the online
+// softmax runs there (a 16-lane reduction per head for the tile maximum),
+// and each row's p values move to the lanes that hold its V row with
+// ds_bpermute, as fp16 pairs of heads.  P.V is the vector path's.
+__device__ __forceinline__ int bperm(int src_lane, int v) { return __builtin_amdgcn_ds_bpermute(src_lane * 4, v); }
+
+template <int KV>   // KV_I8 only (a template so each translation unit may include it)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8)))
+void split_kernel_i8m(const SplitParams P) {
+    constexpr int D = 128, G = 8, RT = 4, RPI = 4, LPR = 16, TT = 16, KS = D / 64;
+    typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(1))) i32x4 gi32x4;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wave_id = blockIdx.x * kWavesPerBlock + wave;
+    if (wave_id >= P.n_pieces) return;
+    const int r = lane / LPR, c = lane % LPR;      // V rows: row group r, 8-byte chunk c
+    const int n = lane & 15, grp = lane >> 4;       // matrix layout: tile row n, k slice / head group
+    const char *kb = reinterpret_cast<const char *>(P.k);
+    const char *vb = reinterpret_cast<const char *>(P.v);
+
+    const int64_t f1 = min(P.total, (int64_t)(wave_id + 1) * P.piece);
+    for (int64_t f = (int64_t)wave_id * P.piece; f < f1;) {
+        int cnt = 0;
+        for (int e0 = 0; e0 < P.nb; e0 += 64) {
+            const int e = e0 + lane;
+            cnt += __popcll(__ballot(e < P.nb && P.pre[e] <= f));
+        }
+        const int bl = __builtin_amdgcn_readfirstlane(cnt - 1);
+        const int len = P.len[bl];
+        const int64_t within = f - P.pre[bl];
+        const int rj = (int)(within / len);
+        const int t0 = (int)(within - (int64_t)rj * len);
+        const int nseg = (int)min((int64_t)(len - t0), f1 - f);
+        const int j = rj / P.n_hg, hg = rj - j * P.n_hg;
+        const int lo = P.lo[bl] + t0;
+        const int hi = lo + nseg;
+        const int64_t b = P.b0 + bl;
+        const int64_t row_start = P.pre[bl] + (int64_t)rj * len;
+        const int64_t slot = P.sbase[bl] + (int64_t)rj * P.maxseg[bl] + (wave_id - row_start / P.piece);
+        const int hbase = j * P.g + hg * G;
+
+        // ------------------------------------------------ query (matrix A operand)
+        // lane (n, grp): head n (real when n < 8 and inside the group), dims 64 ks + 16 grp + e
+        const bool hok = n < G && hg * G + n < P.g;
+        float qf[KS][16];
+        float amax = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++) {
+            const int d0 = 64 * ks + 16 * grp;
+            const char *qp = reinterpret_cast<const char *>(P.q) + ((b * P.N + hbase + (hok ? n : 0)) * D + d0) * 2;
+            const u32x4 x0 = *reinterpret_cast<const u32x4 *>(qp), x1 = *reinterpret_cast<const u32x4 *>(qp + 16);
+            u32x4 s0 = {0, 0, 0, 0}, s1 = {0, 0, 0, 0};
+            if (P.aq_mode == 2) {
+                const char *sp = reinterpret_cast<const char *>(P.k_scale) + ((int64_t)j * D + d0) * 2;
+                s0 = *reinterpret_cast<const u32x4 *>(sp);
+                s1 = *reinterpret_cast<const u32x4 *>(sp + 16);
+            }
+            const uint32_t s_all = reinterpret_cast<const uint16_t *>(P.k_scale)[0];
+#pragma unroll
+            for (int e = 0; e < 16; e++) {
+                const uint32_t qw = e < 8 ? x0[e >> 1] : x1[(e - 8) >> 1];
+                const uint32_t sw = e < 8 ? s0[e >> 1] : s1[(e - 8) >> 1];
+                const uint32_t qbits = (qw >> (16 * (e & 1))) & 0xFFFF;
+                const uint32_t sbits = P.aq_mode == 2 ? (sw >> (16 * (e & 1))) & 0xFFFF : s_all;
+                const float qe = P.q_bf16 ? bf16_to_f32(qbits) : f16_to_f32(qbits);
+                const float se = P.q_bf16 ? bf16_to_f32(sbits) : f16_to_f32(sbits);
+                qf[ks][e] = hok ? qe * se : 0.f;
+                amax = fmaxf(amax, fabsf(qf[ks][e]));
+            }
+        }
+        for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+        int ex = 0;
+        if (amax > 0.f) (void)frexpf(amax, &ex);        // amax < 2^ex
+        const float up = ldexpf(1.f, 14 - ex);
+        const float qmul = P.score_mul * ldexpf(1.f, ex - 14);
+        i32x4 qa[KS], qb[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++)
+#pragma unroll
+            for (int w = 0; w < 4; w++) {
+                uint32_t wa = 0, wb = 0;
+#pragma unroll
+                for (int e4 = 0; e4 < 4; e4++) {
+                    int qi = (int)__builtin_rintf(qf[ks][4 * w + e4] * up);
+                    qi = min(max(qi, -16383), 16383);
+                    const int a = qi >> 7;                   // floor(qi / 128), in [-128, 127]
+                    const int bb = qi - (a << 7);            // in [0, 127]
+                    wa |= (uint32_t)(a & 0xFF) << (8 * e4);
+                    wb |= (uint32_t)bb << (8 * e4);
+                }
+                qa[ks][w] = (int32_t)wa;
+                qb[ks][w] = (int32_t)wb;
+            }
+
+        // ------------------------------------------------ addressing (dense, or per-batch tensors)
+        const int64_t sS_b = P.sS;                     // int8: element stride = byte stride
+        const char *kb_ = kb, *vb_ = vb;
+        int64_t boff = b * P.sB, sN = P.sN;
+        if (P.k_list) {
+            kb_ = reinterpret_cast<const char *const *>(P.k_list)[b];
+            vb_ = reinterpret_cast<const char *const *>(P.v_list)[b];
+            boff = 0;
+            if (P.list_bnsd) sN = (int64_t)P.list_seq[bl] * P.sS;
+        }
+        const char *kp = kb_ + boff + (int64_t)j * sN + 16 * grp;            // + row * sS_b + 64 ks
+        const char *vp_ = vb_ + boff + (int64_t)j * sN + 8 * c + (int64_t)(lo + r) * sS_b;
+        const int lim = hi - 1 - lo - r;
+        i32x4 kt[KS];
+        uint32_t vr[RT][2];
+#pragma unroll
+        for (int i = 0; i < RT; i++) vr[i][0] = vr[i][1] = 0u;
+        auto issue_k = [&](int ts) {
+            const char *rowp = kp + (int64_t)min(ts + n, hi - 1) * sS_b;
+#pragma unroll
+            for (int ks = 0; ks < KS; ks++) kt[ks] = __builtin_nontemporal_load((const gi32x4 *)(rowp + 64 * ks));
+        };
+        auto issue_v = [&](int ts) {
+#pragma unroll
+            for (int i = 0; i < RT; i++) {
+                const u32x2 x = __builtin_nontemporal_load(
+                    (const gu32x2 *)(vp_ + (int64_t)min(ts - lo + i * RPI, lim) * sS_b));
+                vr[i][0] = x[0];
+                vr[i][1] = x[1];
+            }
+        };
+
+        float m4[4], l4[4], acc[G][8];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            m4[i] = kMaxInit;
+            l4[i] = 0.f;
+        }
+#pragma unroll
+        for (int hh = 0; hh < G; hh++)
+#pragma unroll
+            for (int e = 0; e < 8; e++) acc[hh][e] = 0.f;
+
+        int ts = lo;
+        issue_k(ts);
+        issue_v(ts);
+        while (true) {
+            i32x4 ca = {0, 0, 0, 0}, cb = {0, 0, 0, 0};
+#pragma unroll
+            for (int ks = 0; ks < KS; ks++) {
+                ca = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[ks], kt[ks], ca, 0, 0, 0);
+                cb = __builtin_amdgcn_mfma_i32_16x16x64_i8(qb[ks], kt[ks], cb, 0, 0, 0);
+            }
+            const bool more = ts + TT < hi;
+            if (more) issue_k(ts + TT);
+
+            // scores of heads 4 grp + i at tile row n; the tile maximum per head
+            const bool keep = ts + n < hi;
+            float x[4], mt[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                x[i] = keep ? (float)(ca[i] * 128 + cb[i]) * qmul : kNegInf;
+                float v = fmaxf(x[i], dpp<0xB1>(x[i]));
+                v = fmaxf(v, dpp<0x4E>(v));
+                v = fmaxf(v, dpp<0x141>(v));
+                mt[i] = fmaxf(v, dpp<0x140>(v));
+            }
+            bool raise = false;
+#pragma unroll
+            for (int i = 0; i < 4; i++) raise |= mt[i] > m4[i] + kLazy;
+            if (__builtin_amdgcn_ballot_w64(raise)) {
+                float alpha[4];
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const float mn = mt[i] > m4[i] + kLazy ? mt[i] : m4[i];
+                    alpha[i] = __builtin_amdgcn_exp2f(m4[i] - mn);
+                    m4[i] = mn;
+                    l4[i] *= alpha[i];
+                }
+                // head h's factor sits in lane 16 (h / 4), value h % 4
+#pragma unroll
+                for (int hh = 0; hh < G; hh++) {
+                    const float ah = __builtin_bit_cast(
+                        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha[hh & 3]), 16 * (hh >> 2)));
+#pragma unroll
+                    for (int e = 0; e < 8; e++) acc[hh][e] *= ah;
+                }
+            }
+            float p[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                p[i] = __builtin_amdgcn_exp2f(x[i] - m4[i]);
+                l4[i] += p[i];
+            }
+            // this row's p as fp16 pairs of heads, to the lanes holding V rows
+            // i*4 + r: heads 0-3 come from lane i*4 + r, heads 4-7 from lane i*4 + r + 16
+            const int p01 = (int)pack_p(p[0], p[1], std::integral_constant<int, KV_F16>{});
+            const int p23 = (int)pack_p(p[2], p[3], std::integral_constant<int, KV_F16>{});
+            uint32_t ph[RT][4];
+#pragma unroll
+            for (int i = 0; i < RT; i++) {
+                const int src = i * RPI + r;
+                ph[i][0] = (uint32_t)bperm(src, p01);
+                ph[i][1] = (uint32_t)bperm(src, p23);
+                ph[i][2] = (uint32_t)bperm(src + 16, p01);
+                ph[i][3] = (uint32_t)bperm(src + 16, p23);
+            }
+#pragma unroll
+            for (int i = 0; i < RT; i += 2) {
+                uint32_t vp[8];
+#pragma unroll
+                for (int w = 0; w < 2; w++) {
+                    const uint32_t a = vr[i][w] ^ 0x80808080u, bq = vr[i + 1][w] ^ 0x80808080u;
+                    const uint32_t x01 = __builtin_amdgcn_perm(bq, a, 0x05010400u);
+                    const uint32_t x23 = __builtin_amdgcn_perm(bq, a, 0x07030602u);
+                    vp[4 * w + 0] = i8pair_to_f16x2(__builtin_amdgcn_perm(kF16Hi, x01, 0x04010400u));
+                    vp[4 * w + 1] = i8pair_to_f16x2(__builtin_amdgcn_perm(kF16Hi, x01, 0x04030402u));
+                    vp[4 * w + 2] = i8pair_to_f16x2(__builtin_amdgcn_perm(kF16Hi, x23, 0x04010400u));
+                    vp[4 * w + 3] = i8pair_to_f16x2(__builtin_amdgcn_perm(kF16Hi, x23, 0x04030402u));
+                }
+#pragma unroll
+                for (int hh = 0; hh < G; hh++) {
+                    // {p of row i, p of row i + 1} for head hh
+                    const uint32_t pp = __builtin_amdgcn_perm(ph[i + 1][hh >> 1], ph[i][hh >> 1],
+                                                              (hh & 1) ? 0x07060302u : 0x05040100u);
+#pragma unroll
+                    for (int e = 0; e < 8; e++)
+                        acc[hh][e] = dot2(pp, vp[e], acc[hh][e], std::integral_constant<int, KV_F16>{});
+                }
+            }
+            if (!more) break;
+            issue_v(ts + TT);
+            ts += TT;
+        }
+
+        // per-head state in the V layout: m uniform, l summed over the 16 rows
+        // and counted once (row group 0), so the row-group merge below adds the
+        // accumulators only
+        float m[G], l[G];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            float v = l4[i] + dpp<0xB1>(l4[i]);
+            v += dpp<0x4E>(v);
+            v += dpp<0x141>(v);
+            l4[i] = v + dpp<0x140>(v);
+        }
+#pragma unroll
+        for (int hh = 0; hh < G; hh++) {
+            m[hh] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m4[hh & 3]), 16 * (hh >> 2)));
+            const float lt = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l4[hh & 3]), 16 * (hh >> 2)));
+            l[hh] = r == 0 ? lt : 0.f;
+        }
+#pragma unroll
+        for (int off = LPR; off < 64; off <<= 1) {
+#pragma unroll
+            for (int hh = 0; hh < G; hh++) {
+                l[hh] += __shfl_xor(l[hh], off);
+#pragma unroll
+                for (int e = 0; e < 8; e++) acc[hh][e] += __shfl_xor(acc[hh][e], off);
+            }
+        }
+        if (r == 0) {
+#pragma unroll
+            for (int hh = 0; hh < G; hh++) {
+                if (hg * G + hh >= P.g) break;
+                const int64_t row = slot * G + hh;
+                float4 *dst = reinterpret_cast<float4 *>(P.part_acc + row * D + 8 * c);
+                dst[0] = make_float4(acc[hh][0], acc[hh][1], acc[hh][2], acc[hh][3]);
+                dst[1] = make_float4(acc[hh][4], acc[hh][5], acc[hh][6], acc[hh][7]);
+                if (c == 0) *reinterpret_cast<float2 *>(P.part_ml + row * 2) = make_float2(m[hh], l[hh]);
+            }
+        }
+        f += nseg;
+    }   // segments
+}
+
 using SplitFn = void (*)(const SplitParams);
 
 template <int KV, int D, int G, bool PAGED>
 SplitFn pick_extra(int extra) {
+    if constexpr (KV == KV_I8 && D == 128 && G == 8 && !PAGED) {
+        if (extra == EX_NONE) return split_kernel_i8m<KV_I8>;
+    }
     return extra == EX_PSE ? split_kernel<KV, D, G, PAGED, EX_PSE>
          : extra == EX_MASK ? split_kernel<KV, D, G, PAGED, EX_MASK>
                             : split_kernel<KV, D, G, PAGED, EX_NONE>;
@@ -786,7 +1067,10 @@ const void *ptr_pm(bool paged, int extra) {
 template <int KV, int D, int G, bool PAGED, int EXTRA>
 hipError_t launch_one(const SplitParams &p, hipStream_t s) {
     const int blocks = (p.n_pieces + kWavesPerBlock - 1) / kWavesPerBlock;
-    hipLaunchKernelGGL((split_kernel<KV, D, G, PAGED, EXTRA>), dim3(blocks), dim3(64 * kWavesPerBlock), 0, s, p);
+    if constexpr (KV == KV_I8 && D == 128 && G == 8 && !PAGED && EXTRA == EX_NONE)
+        hipLaunchKernelGGL(split_kernel_i8m<KV_I8>, dim3(blocks), dim3(64 * kWavesPerBlock), 0, s, p);
+    else
+        hipLaunchKernelGGL((split_kernel<KV, D, G, PAGED, EXTRA>), dim3(blocks), dim3(64 * kWavesPerBlock), 0, s, p);
     return hipGetLastError();
 }
 
