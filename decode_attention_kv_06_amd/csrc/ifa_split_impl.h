@@ -776,17 +776,26 @@ void split_kernel(const SplitParams P) {
 // against the raw int8 keys) give the exact integer score 128 A + B of 16
 // rows x 16 heads (8 real) per tile, with no byte widening of K at all.
 // Lane (n, g) of the result holds row n of heads 4g .. 4g+3: the online
-// softmax runs there (a 16-lane reduction per head for the tile maximum),
-// and each row's p values move to the lanes that hold its V row with
-// ds_bpermute, as fp16 pairs of heads.  P.V is the vector path's.
+// softmax runs there (a 16-lane reduction per head for the tile maximum).
+// P.V runs on the matrix cores too: P and the tile's V rows, widened to
+// fp16, are staged in the wave's LDS, and V is read back transposed as the
+// operand of one v_mfma_f32_16x16x16_f16 per 16 output columns.
 __device__ __forceinline__ int bperm(int src_lane, int v) { return __builtin_amdgcn_ds_bpermute(src_lane * 4, v); }
 
 template <int KV>   // KV_I8 only (a template so each translation unit may include it)
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void split_kernel_i8m(const SplitParams P) {
     constexpr int D = 128, G = 8, RT = 4, RPI = 4, LPR = 16, TT = 16, KS = D / 64;
+    // fp16 V tile rows at a 288-byte pitch: the transposed reads of a 16-lane
+    // group (4 rows x 32 bytes) then fall in distinct banks
+    constexpr int kVtPitch = 2 * D + 32;
     typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(1))) i32x4 gi32x4;
+    typedef float floatx4 __attribute__((ext_vector_type(4)));
+    typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+    typedef short shortx4 __attribute__((ext_vector_type(4)));
+    __shared__ __attribute__((aligned(16))) char s_vt[kWavesPerBlock][16 * kVtPitch];
+    __shared__ __attribute__((aligned(16))) char s_pp[kWavesPerBlock][16 * 32];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wave_id = blockIdx.x * kWavesPerBlock + wave;
@@ -902,16 +911,15 @@ void split_kernel_i8m(const SplitParams P) {
             }
         };
 
-        float m4[4], l4[4], acc[G][8];
+        float m4[4], l4[4];
+        floatx4 oacc[D / 16];        // O[4 grp + i][16 blk + n]
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             m4[i] = kMaxInit;
             l4[i] = 0.f;
         }
 #pragma unroll
-        for (int hh = 0; hh < G; hh++)
-#pragma unroll
-            for (int e = 0; e < 8; e++) acc[hh][e] = 0.f;
+        for (int blk = 0; blk < D / 16; blk++) oacc[blk] = floatx4{0.f, 0.f, 0.f, 0.f};
 
         int ts = lo;
         issue_k(ts);
@@ -949,14 +957,10 @@ void split_kernel_i8m(const SplitParams P) {
                     m4[i] = mn;
                     l4[i] *= alpha[i];
                 }
-                // head h's factor sits in lane 16 (h / 4), value h % 4
 #pragma unroll
-                for (int hh = 0; hh < G; hh++) {
-                    const float ah = __builtin_bit_cast(
-                        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha[hh & 3]), 16 * (hh >> 2)));
+                for (int blk = 0; blk < D / 16; blk++)
 #pragma unroll
-                    for (int e = 0; e < 8; e++) acc[hh][e] *= ah;
-                }
+                    for (int i = 0; i < 4; i++) oacc[blk][i] *= alpha[i];
             }
             float p[4];
 #pragma unroll
@@ -964,51 +968,46 @@ void split_kernel_i8m(const SplitParams P) {
                 p[i] = __builtin_amdgcn_exp2f(x[i] - m4[i]);
                 l4[i] += p[i];
             }
-            // this row's p as fp16 pairs of heads, to the lanes holding V rows
-            // i*4 + r: heads 0-3 come from lane i*4 + r, heads 4-7 from lane i*4 + r + 16
-            const int p01 = (int)pack_p(p[0], p[1], std::integral_constant<int, KV_F16>{});
-            const int p23 = (int)pack_p(p[2], p[3], std::integral_constant<int, KV_F16>{});
-            uint32_t ph[RT][4];
+            // P.V on the matrix cores: P (16 heads x 16 rows) and the tile's V
+            // rows, widened to fp16, go through this wave's LDS; V is read back
+            // transposed (ds_read_b64_tr_b16) as the B operand of eight
+            // v_mfma_f32_16x16x16_f16, one per 16-column block.
+            char *pw = s_pp[wave];
+            char *vw = s_vt[wave];
+#pragma unroll
+            for (int i = 0; i < 4; i++) *reinterpret_cast<_Float16 *>(pw + (4 * grp + i) * 32 + 2 * n) = (_Float16)p[i];
 #pragma unroll
             for (int i = 0; i < RT; i++) {
-                const int src = i * RPI + r;
-                ph[i][0] = (uint32_t)bperm(src, p01);
-                ph[i][1] = (uint32_t)bperm(src, p23);
-                ph[i][2] = (uint32_t)bperm(src + 16, p01);
-                ph[i][3] = (uint32_t)bperm(src + 16, p23);
+                const uint32_t w0 = vr[i][0] ^ 0x80808080u, w1 = vr[i][1] ^ 0x80808080u;
+                u32x4 h;
+                h[0] = i8pair_to_f16x2(__builtin_amdgcn_perm(kF16Hi, w0, 0x04010400u));
+                h[1] = i8pair_to_f16x2(__builtin_amdgcn_perm(kF16Hi, w0, 0x04030402u));
+                h[2] = i8pair_to_f16x2(__builtin_amdgcn_perm(kF16Hi, w1, 0x04010400u));
+                h[3] = i8pair_to_f16x2(__builtin_amdgcn_perm(kF16Hi, w1, 0x04030402u));
+                *reinterpret_cast<u32x4 *>(vw + (i * RPI + r) * kVtPitch + 16 * c) = h;
             }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            // A: lane (h = n, g = grp) holds P[h][rows 4g .. 4g+3]
+            const f16x4 pa = *reinterpret_cast<const f16x4 *>(pw + n * 32 + 8 * grp);
+            // B: lane j of 16-lane group g points at row 4g + j/4, columns 4(j%4) .. +3 of a block
+            const char *vt0 = vw + (4 * grp + (n >> 2)) * kVtPitch + 8 * (n & 3);
 #pragma unroll
-            for (int i = 0; i < RT; i += 2) {
-                uint32_t vp[8];
-#pragma unroll
-                for (int w = 0; w < 2; w++) {
-                    const uint32_t a = vr[i][w] ^ 0x80808080u, bq = vr[i + 1][w] ^ 0x80808080u;
-                    const uint32_t x01 = __builtin_amdgcn_perm(bq, a, 0x05010400u);
-                    const uint32_t x23 = __builtin_amdgcn_perm(bq, a, 0x07030602u);
-                    vp[4 * w + 0] = i8pair_to_f16x2(__builtin_amdgcn_perm(kF16Hi, x01, 0x04010400u));
-                    vp[4 * w + 1] = i8pair_to_f16x2(__builtin_amdgcn_perm(kF16Hi, x01, 0x04030402u));
-                    vp[4 * w + 2] = i8pair_to_f16x2(__builtin_amdgcn_perm(kF16Hi, x23, 0x04010400u));
-                    vp[4 * w + 3] = i8pair_to_f16x2(__builtin_amdgcn_perm(kF16Hi, x23, 0x04030402u));
-                }
-#pragma unroll
-                for (int hh = 0; hh < G; hh++) {
-                    // {p of row i, p of row i + 1} for head hh
-                    const uint32_t pp = __builtin_amdgcn_perm(ph[i + 1][hh >> 1], ph[i][hh >> 1],
-                                                              (hh & 1) ? 0x07060302u : 0x05040100u);
-#pragma unroll
-                    for (int e = 0; e < 8; e++)
-                        acc[hh][e] = dot2(pp, vp[e], acc[hh][e], std::integral_constant<int, KV_F16>{});
-                }
+            for (int blk = 0; blk < D / 16; blk++) {
+                const f16x4 bv = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) shortx4 *)(vt0 + 32 * blk)));
+                oacc[blk] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, bv, oacc[blk], 0, 0, 0);
             }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             if (!more) break;
             issue_v(ts + TT);
             ts += TT;
         }
 
-        // per-head state in the V layout: m uniform, l summed over the 16 rows
-        // and counted once (row group 0), so the row-group merge below adds the
-        // accumulators only
-        float m[G], l[G];
+        // l summed over the tile rows (the 16 lanes of a head group); m is uniform there
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             float v = l4[i] + dpp<0xB1>(l4[i]);
@@ -1016,30 +1015,16 @@ void split_kernel_i8m(const SplitParams P) {
             v += dpp<0x141>(v);
             l4[i] = v + dpp<0x140>(v);
         }
+        // lane (n, grp < 2) holds O[4 grp + i][16 blk + n]
+        if (grp < 2) {
 #pragma unroll
-        for (int hh = 0; hh < G; hh++) {
-            m[hh] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m4[hh & 3]), 16 * (hh >> 2)));
-            const float lt = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l4[hh & 3]), 16 * (hh >> 2)));
-            l[hh] = r == 0 ? lt : 0.f;
-        }
-#pragma unroll
-        for (int off = LPR; off < 64; off <<= 1) {
-#pragma unroll
-            for (int hh = 0; hh < G; hh++) {
-                l[hh] += __shfl_xor(l[hh], off);
-#pragma unroll
-                for (int e = 0; e < 8; e++) acc[hh][e] += __shfl_xor(acc[hh][e], off);
-            }
-        }
-        if (r == 0) {
-#pragma unroll
-            for (int hh = 0; hh < G; hh++) {
+            for (int i = 0; i < 4; i++) {
+                const int hh = 4 * grp + i;
                 if (hg * G + hh >= P.g) break;
                 const int64_t row = slot * G + hh;
-                float4 *dst = reinterpret_cast<float4 *>(P.part_acc + row * D + 8 * c);
-                dst[0] = make_float4(acc[hh][0], acc[hh][1], acc[hh][2], acc[hh][3]);
-                dst[1] = make_float4(acc[hh][4], acc[hh][5], acc[hh][6], acc[hh][7]);
-                if (c == 0) *reinterpret_cast<float2 *>(P.part_ml + row * 2) = make_float2(m[hh], l[hh]);
+#pragma unroll
+                for (int blk = 0; blk < D / 16; blk++) P.part_acc[row * D + 16 * blk + n] = oacc[blk][i];
+                if (n == 0) *reinterpret_cast<float2 *>(P.part_ml + row * 2) = make_float2(m4[i], l4[i]);
             }
         }
         f += nseg;
