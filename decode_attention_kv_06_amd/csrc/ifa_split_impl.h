@@ -46,6 +46,18 @@ __device__ __forceinline__ float dpp(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
 }
 
+// A wave-uniform pointer, declared so (scalar registers).
+__device__ __forceinline__ const char *uniform_ptr(const char *p) {
+    const uint64_t v = (uint64_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<const char *>(((uint64_t)hi << 32) | lo);
+}
+
+template <int CTRL>
+__device__ __forceinline__ int dppi(int x) {
+    return __builtin_amdgcn_mov_dpp(x, CTRL, 0xF, 0xF, true);
+}
+
 __device__ __forceinline__ float swz_xor16(float x) {
     // ds_swizzle bit mode: and 0x1f, or 0, xor 0x10 (within 32-lane halves).
     return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F));
@@ -776,12 +788,12 @@ void split_kernel(const SplitParams P) {
 // against the raw int8 keys) give the exact integer score 128 A + B of 16
 // rows x 16 heads (8 real) per tile, with no byte widening of K at all.
 // Lane (n, g) of the result holds row n of heads 4g .. 4g+3: the online
-// softmax runs there (a 16-lane reduction per head for the tile maximum).
-// P.V runs on the matrix cores too: P and the tile's V rows, widened to
-// fp16, are staged in the wave's LDS, and V is read back transposed as the
-// operand of one v_mfma_f32_16x16x16_f16 per 16 output columns.
-__device__ __forceinline__ int bperm(int src_lane, int v) { return __builtin_amdgcn_ds_bpermute(src_lane * 4, v); }
-
+// softmax runs there, with the tile maximum per head taken over the integer
+// scores (a 16-lane DPP reduction).  P.V runs on the matrix cores too: P and
+// the tile's V rows, widened to fp16, are staged in the wave's LDS and read
+// back transposed as the operands of one v_mfma_f32_16x16x16_f16 per 16
+// output columns.  K and V tiles are loaded two tiles ahead, from scalar row
+// bases with fixed per-lane offsets.
 template <int KV>   // KV_I8 only (a template so each translation unit may include it)
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void split_kernel_i8m(const SplitParams P) {
@@ -858,8 +870,9 @@ void split_kernel_i8m(const SplitParams P) {
         for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
         int ex = 0;
         if (amax > 0.f) (void)frexpf(amax, &ex);        // amax < 2^ex
-        const float up = ldexpf(1.f, 14 - ex);
-        const float qmul = P.score_mul * ldexpf(1.f, ex - 14);
+        // the sign of the score factor goes into q, so the factor is positive
+        const float up = P.score_mul < 0.f ? -ldexpf(1.f, 14 - ex) : ldexpf(1.f, 14 - ex);
+        const float qmul = fabsf(P.score_mul) * ldexpf(1.f, ex - 14);
         i32x4 qa[KS], qb[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ks++)
@@ -889,23 +902,37 @@ void split_kernel_i8m(const SplitParams P) {
             boff = 0;
             if (P.list_bnsd) sN = (int64_t)P.list_seq[bl] * P.sS;
         }
-        const char *kp = kb_ + boff + (int64_t)j * sN + 16 * grp;            // + row * sS_b + 64 ks
-        const char *vp_ = vb_ + boff + (int64_t)j * sN + 8 * c + (int64_t)(lo + r) * sS_b;
-        const int lim = hi - 1 - lo - r;
-        i32x4 kt[KS];
-        uint32_t vr[RT][2];
+        // wave-uniform row bases (scalar registers) plus fixed 32-bit lane
+        // offsets: every load is a saddr + voffset global load
+        const char *kbase = uniform_ptr(kb_ + boff + (int64_t)j * sN);
+        const char *vbase = uniform_ptr(vb_ + boff + (int64_t)j * sN);
+        const uint32_t sSu = (uint32_t)sS_b;
+        const uint32_t koff = (uint32_t)n * sSu + 16u * grp;
+        uint32_t voff[RT];
 #pragma unroll
-        for (int i = 0; i < RT; i++) vr[i][0] = vr[i][1] = 0u;
-        auto issue_k = [&](int ts) {
-            const char *rowp = kp + (int64_t)min(ts + n, hi - 1) * sS_b;
+        for (int i = 0; i < RT; i++) voff[i] = (uint32_t)(i * RPI + r) * sSu + 8u * c;
+        // K and V tiles run two deep: buffers A and B alternate, so a tile's
+        // registers are reloaded only once its products are issued
+        i32x4 kA[KS], kB[KS];
+        uint32_t vA[RT][2], vB[RT][2];
 #pragma unroll
-            for (int ks = 0; ks < KS; ks++) kt[ks] = __builtin_nontemporal_load((const gi32x4 *)(rowp + 64 * ks));
+        for (int i = 0; i < RT; i++) vA[i][0] = vA[i][1] = vB[i][0] = vB[i][1] = 0u;
+        // a tile that runs past hi re-reads its last row in the lanes beyond it
+        auto issue_k = [&](i32x4 (&kt)[KS], int ts) {
+            const char *tb = kbase + (int64_t)ts * sS_b;
+            uint32_t o = koff;
+            if (ts + TT > hi) o = min((uint32_t)n, (uint32_t)(hi - 1 - ts)) * sSu + 16u * grp;
+#pragma unroll
+            for (int ks = 0; ks < KS; ks++) kt[ks] = __builtin_nontemporal_load((const gi32x4 *)(tb + o + 64 * ks));
         };
-        auto issue_v = [&](int ts) {
+        auto issue_v = [&](uint32_t (&vr)[RT][2], int ts) {
+            const char *tb = vbase + (int64_t)ts * sS_b;
+            const bool part = ts + TT > hi;
 #pragma unroll
             for (int i = 0; i < RT; i++) {
-                const u32x2 x = __builtin_nontemporal_load(
-                    (const gu32x2 *)(vp_ + (int64_t)min(ts - lo + i * RPI, lim) * sS_b));
+                uint32_t o = voff[i];
+                if (part) o = min((uint32_t)(i * RPI + r), (uint32_t)(hi - 1 - ts)) * sSu + 8u * c;
+                const u32x2 x = __builtin_nontemporal_load((const gu32x2 *)(tb + o));
                 vr[i][0] = x[0];
                 vr[i][1] = x[1];
             }
@@ -922,28 +949,36 @@ void split_kernel_i8m(const SplitParams P) {
         for (int blk = 0; blk < D / 16; blk++) oacc[blk] = floatx4{0.f, 0.f, 0.f, 0.f};
 
         int ts = lo;
-        issue_k(ts);
-        issue_v(ts);
-        while (true) {
+        char *pw = s_pp[wave];
+        char *vw = s_vt[wave];
+        // one tile: products with K in kt, V in vr; both are refilled with the
+        // tile two ahead.  Returns whether another tile follows.
+        auto tile = [&](i32x4 (&kt)[KS], uint32_t (&vr)[RT][2]) -> bool {
             i32x4 ca = {0, 0, 0, 0}, cb = {0, 0, 0, 0};
 #pragma unroll
             for (int ks = 0; ks < KS; ks++) {
                 ca = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[ks], kt[ks], ca, 0, 0, 0);
                 cb = __builtin_amdgcn_mfma_i32_16x16x64_i8(qb[ks], kt[ks], cb, 0, 0, 0);
             }
-            const bool more = ts + TT < hi;
-            if (more) issue_k(ts + TT);
+            const bool more = ts + TT < hi, more2 = ts + 2 * TT < hi;
+            if (more2) issue_k(kt, ts + 2 * TT);
 
             // scores of heads 4 grp + i at tile row n; the tile maximum per head
             const bool keep = ts + n < hi;
             float x[4], mt[4];
+            // the maximum is taken over the integer scores (the scale factor
+            // is positive, so it commutes with the rounding of the products);
+            // row 0 of a tile is always inside the window
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-                x[i] = keep ? (float)(ca[i] * 128 + cb[i]) * qmul : kNegInf;
-                float v = fmaxf(x[i], dpp<0xB1>(x[i]));
-                v = fmaxf(v, dpp<0x4E>(v));
-                v = fmaxf(v, dpp<0x141>(v));
-                mt[i] = fmaxf(v, dpp<0x140>(v));
+                const int si = ca[i] * 128 + cb[i];
+                x[i] = keep ? (float)si * qmul : kNegInf;
+                int v = keep ? si : (-2147483647 - 1);
+                v = max(v, dppi<0xB1>(v));
+                v = max(v, dppi<0x4E>(v));
+                v = max(v, dppi<0x141>(v));
+                v = max(v, dppi<0x140>(v));
+                mt[i] = (float)v * qmul;
             }
             bool raise = false;
 #pragma unroll
@@ -968,14 +1003,11 @@ void split_kernel_i8m(const SplitParams P) {
                 p[i] = __builtin_amdgcn_exp2f(x[i] - m4[i]);
                 l4[i] += p[i];
             }
-            // P.V on the matrix cores: P (16 heads x 16 rows) and the tile's V
-            // rows, widened to fp16, go through this wave's LDS; V is read back
-            // transposed (ds_read_b64_tr_b16) as the B operand of eight
-            // v_mfma_f32_16x16x16_f16, one per 16-column block.
-            char *pw = s_pp[wave];
-            char *vw = s_vt[wave];
-#pragma unroll
-            for (int i = 0; i < 4; i++) *reinterpret_cast<_Float16 *>(pw + (4 * grp + i) * 32 + 2 * n) = (_Float16)p[i];
+            // P stored row-major by tile row (16 heads per row): one 8-byte write per lane
+            {
+                f16x4 ph = {(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
+                *reinterpret_cast<f16x4 *>(pw + n * 32 + 8 * grp) = ph;
+            }
 #pragma unroll
             for (int i = 0; i < RT; i++) {
                 const uint32_t w0 = vr[i][0] ^ 0x80808080u, w1 = vr[i][1] ^ 0x80808080u;
@@ -986,12 +1018,13 @@ void split_kernel_i8m(const SplitParams P) {
                 h[3] = i8pair_to_f16x2(__builtin_amdgcn_perm(kF16Hi, w1, 0x04030402u));
                 *reinterpret_cast<u32x4 *>(vw + (i * RPI + r) * kVtPitch + 16 * c) = h;
             }
+            if (more2) issue_v(vr, ts + 2 * TT);
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            // A: lane (h = n, g = grp) holds P[h][rows 4g .. 4g+3]
-            const f16x4 pa = *reinterpret_cast<const f16x4 *>(pw + n * 32 + 8 * grp);
-            // B: lane j of 16-lane group g points at row 4g + j/4, columns 4(j%4) .. +3 of a block
+            // A: lane (h = n, g = grp) takes P[rows 4g .. 4g+3][head h], a transposed read
+            const f16x4 pa = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) shortx4 *)(pw + (4 * grp + (n >> 2)) * 32 + 8 * (n & 3))));
             const char *vt0 = vw + (4 * grp + (n >> 2)) * kVtPitch + 8 * (n & 3);
 #pragma unroll
             for (int blk = 0; blk < D / 16; blk++) {
@@ -1002,9 +1035,16 @@ void split_kernel_i8m(const SplitParams P) {
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            if (!more) break;
-            issue_v(ts + TT);
             ts += TT;
+            return more;
+        };
+        issue_k(kA, ts);
+        issue_v(vA, ts);
+        if (ts + TT < hi) {
+            issue_k(kB, ts + TT);
+            issue_v(vB, ts + TT);
+        }
+        while (tile(kA, vA) && tile(kB, vB)) {
         }
 
         // l summed over the tile rows (the 16 lanes of a head group); m is uniform there

@@ -108,6 +108,17 @@ def test_int8_antiquant(qdt, mode):
     compare(inp, out)
 
 
+@pytest.mark.parametrize("kv", ["i8", "f16"])
+def test_negative_scale(kv):
+    """A negative scale reverses the score order; for int8 keys with head groups of 8 the
+    matrix-core kernel folds the sign into q and takes the tile maximum over integers."""
+    spec = IfaSpec("neg_scale", 318, "f16", kv, B=3, N=16, Nkv=2, D=128, layout="BNSD", S=700,
+                   len_range=(1, 700), scale=-0.3, antiquant="per_channel" if kv == "i8" else None)
+    inp = make_ifa(spec)
+    out, _ = run_gpu(inp)
+    compare(inp, out)
+
+
 @pytest.mark.parametrize("layout,cache_layout", [("BNSD", 0), ("BNSD", 1), ("BSH", 1), ("BSND", 1)])
 @pytest.mark.parametrize("bs", [16, 48, 128, 512])
 def test_paged_layouts_and_block_sizes(layout, cache_layout, bs):
