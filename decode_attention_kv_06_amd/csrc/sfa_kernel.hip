@@ -574,29 +574,68 @@ __global__ __launch_bounds__(256, 1) void sfa_kernel(const SfaParams P) {
 // out = sum_s w_s o_s / sum_s w_s with w_s = l_s 2^(m_s - max m), and rounds.
 template <bool BF>
 __global__ __launch_bounds__(256) void sfa_combine_kernel(const SfaParams P) {
-    using M = Mfma<BF>;
+    typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
     const int lane = threadIdx.x & 63;
     const int row = blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (row >= P.R * P.QN) return;
     const int qr = row / P.QN, hh = row - qr * P.QN;
     const float2 *ml = reinterpret_cast<const float2 *>(P.part_ml);
     auto prow = [&](int s) -> int64_t { return ((int64_t)qr * P.n_sc + s) * P.QN + hh; };
+    // lane l merges elements 8 l .. 8 l + 7 of the head's row: one 16-byte
+    // load per chunk, the loads of four chunks in flight together
+    const char *po = reinterpret_cast<const char *>(P.part_o) + 16 * lane;
+    auto part = [&](int s) { return *reinterpret_cast<const u32x4v *>(po + prow(s) * (kD * 2)); };
+    auto elem = [](const u32x4v &x, int e) -> float {
+        const uint32_t w = x[e >> 1];
+        const uint32_t h = (e & 1) ? (w >> 16) : (w & 0xFFFFu);
+        return BF ? __builtin_bit_cast(float, h << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+    };
     float Mx = kNegInf;
     for (int s = 0; s < P.n_sc; s++) Mx = fmaxf(Mx, ml[prow(s)].x);
-    float L = 0.f, o[kD / 64];
+    float L = 0.f, o[8];
 #pragma unroll
-    for (int e = 0; e < kD / 64; e++) o[e] = 0.f;
-    for (int s = 0; s < P.n_sc; s++) {
+    for (int e = 0; e < 8; e++) o[e] = 0.f;
+    int s = 0;
+    for (; s + 4 <= P.n_sc; s += 4) {
+        u32x4v x[4];
+        float w[4];
+#pragma unroll
+        for (int u = 0; u < 4; u++) x[u] = part(s + u);
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const float2 v = ml[prow(s + u)];
+            w[u] = v.y * __builtin_amdgcn_exp2f(v.x - Mx);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            L += w[u];
+#pragma unroll
+            for (int e = 0; e < 8; e++) o[e] += w[u] * elem(x[u], e);
+        }
+    }
+    for (; s < P.n_sc; s++) {
+        const u32x4v x = part(s);
         const float2 v = ml[prow(s)];
         const float w = v.y * __builtin_amdgcn_exp2f(v.x - Mx);
         L += w;
-        const int64_t base = prow(s) * kD + lane;
 #pragma unroll
-        for (int e = 0; e < kD / 64; e++) o[e] += w * M::load(P.part_o, base + 64 * e);
+        for (int e = 0; e < 8; e++) o[e] += w * elem(x, e);
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
+    u32x4v y;
 #pragma unroll
-    for (int e = 0; e < kD / 64; e++) M::store(P.out, ((int64_t)qr * P.QN + hh) * kD + lane + 64 * e, o[e] * inv);
+    for (int e = 0; e < 8; e += 2) {
+        uint32_t lo, hi;
+        if (BF) {
+            lo = __builtin_bit_cast(uint16_t, (__bf16)(o[e] * inv));
+            hi = __builtin_bit_cast(uint16_t, (__bf16)(o[e + 1] * inv));
+        } else {
+            lo = __builtin_bit_cast(uint16_t, (_Float16)(o[e] * inv));
+            hi = __builtin_bit_cast(uint16_t, (_Float16)(o[e + 1] * inv));
+        }
+        y[e >> 1] = lo | (hi << 16);
+    }
+    *reinterpret_cast<u32x4v *>(reinterpret_cast<char *>(P.out) + (((int64_t)qr * P.QN + hh) * kD + 8 * lane) * 2) = y;
 }
 
 }  // namespace sfa_detail

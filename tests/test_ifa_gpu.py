@@ -108,6 +108,18 @@ def test_int8_antiquant(qdt, mode):
     compare(inp, out)
 
 
+@pytest.mark.parametrize("N,Nkv,split", [(16, 2, 16), (16, 2, 48), (16, 2, 1024), (24, 2, 0), (40, 4, 32),
+                                         (24, 2, 64)])
+def test_int8_group_of_8_splits_and_padded_groups(N, Nkv, split):
+    """int8 keys with head groups of 8 (the matrix-core kernel): pieces that start and end inside
+    a window, and a second head group that is partly padding (g = 12, 10)."""
+    spec = IfaSpec("aq_g8", 319 + N + split, "bf16", "i8", B=3, N=N, Nkv=Nkv, D=128, layout="BNSD", S=800,
+                   len_range=(1, 800), antiquant="per_channel", pad_off=(0, 30))
+    inp = make_ifa(spec)
+    out, _ = run_gpu(inp, split=split)
+    compare(inp, out)
+
+
 @pytest.mark.parametrize("kv", ["i8", "f16"])
 def test_negative_scale(kv):
     """A negative scale reverses the score order; for int8 keys with head groups of 8 the
