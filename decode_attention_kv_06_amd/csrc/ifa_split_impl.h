@@ -334,6 +334,7 @@ void split_kernel(const SplitParams P) {
         const int32_t *btab = nullptr;
         int q_first = 0;
         bool tbl_in_lds = false;
+        const bool two_blk = PAGED && P.block_size >= TT;   // a tile spans at most two blocks
         uint32_t blk_b = 0, head_b = 0, row_b = 0;
         if constexpr (PAGED) {
             btab = P.block_table + b * P.max_blocks;
@@ -430,6 +431,39 @@ void split_kernel(const SplitParams P) {
         };
         auto issue_k = [&](int ts, uint64_t skip) {
             if constexpr (PAGED) {
+              if (two_blk) {
+                // A tile spans at most two blocks, q0 and q1 (q1 = q0 or q0 + 1):
+                // two uniform block-id reads, and per row a select between the
+                // two block bases by the row's place in block q0.
+                const int last = min(ts + TT, hi) - 1;
+                const uint32_t q0 = div_bs((uint32_t)ts, P.bs_magic, P.bs_shift);
+                const uint32_t q1 = div_bs((uint32_t)last, P.bs_magic, P.bs_shift);
+                int b0, b1;
+                if (tbl_in_lds) {
+                    const __attribute__((address_space(3))) int32_t *lt = (const __attribute__((address_space(3))) int32_t *)wtbl;
+                    b0 = lt[q0 - q_first];
+                    b1 = lt[q1 - q_first];
+                } else {
+                    const __attribute__((address_space(1))) int32_t *gt = (const __attribute__((address_space(1))) int32_t *)btab;
+                    b0 = gt[q0];
+                    b1 = gt[q1];
+                }
+                b0 = __builtin_amdgcn_readfirstlane(b0);
+                b1 = __builtin_amdgcn_readfirstlane(b1);
+                const bool ok0 = (unsigned)b0 < (unsigned)P.num_blocks, ok1 = (unsigned)b1 < (unsigned)P.num_blocks;
+                // row offset within block q0 of tile row 0, and of the last row
+                const int rel0 = ts - (int)q0 * P.block_size, rel_last = last - (int)q0 * P.block_size;
+                // base of block q0, and of block q1 shifted back by one block's rows
+                const int64_t s0 = (int64_t)(uint32_t)b0 * blk_b + head_b;
+                const int64_t s1 = (int64_t)(uint32_t)b1 * blk_b + head_b - (int64_t)P.block_size * row_b;
+#pragma unroll
+                for (int i = 0; i < RT; i++) {
+                    const int rel = min(rel0 + i * RPI + r, rel_last);
+                    const bool sel = rel >= P.block_size;
+                    okr[i] = sel ? ok1 : ok0;
+                    offs[i] = okr[i] ? (sel ? s1 : s0) + (int64_t)((uint32_t)rel * row_b) + lane_byte : 0;
+                }
+              } else {
 #pragma unroll
                 for (int i = 0; i < RT; i++) {
                     const int t = min(ts + i * RPI + r, hi - 1);
@@ -444,6 +478,7 @@ void split_kernel(const SplitParams P) {
                     // never dereference an out-of-range block id: read block 0 instead
                     offs[i] = okr[i] ? (int64_t)(uint32_t)blk * blk_b + (head_b + rr * row_b) + lane_byte : 0;
                 }
+              }
             }
             const char *ptr[RT];
             row_ptrs(ts, PAGED ? kb : kp, ptr);

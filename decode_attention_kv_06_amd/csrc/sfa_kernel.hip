@@ -8,9 +8,10 @@
 //
 // Mapping to the hardware:
 //  * one workgroup (4 waves) per (batch, block of 64 heads, chunk of
-//    indices); each wave owns 16 heads.  The head blocks of one chunk get
-//    workgroup ids that differ by a multiple of 8, which places them on the
-//    same XCD, so the second read of a gathered row is an L2 hit.
+//    indices); each wave owns 16 heads.  Each XCD takes a contiguous range
+//    of (batch, chunk) groups with all their head blocks, so the second read
+//    of a gathered row, and the query and block-table rows that the chunks
+//    of a batch share, are L2 hits.
 //  * at the start the chunk's valid indices are compacted (in order) into an
 //    LDS table of physical row numbers.
 //  * tiles of 32 gathered rows (1152 B of key + rope, 1024 B of value each)
@@ -51,6 +52,10 @@ constexpr int kRP = 1056;
 constexpr int kRopeOff = kT * kRP;      // rope rows of a key slot: 32 x 128 B, columns swizzled
 constexpr int kSlot = kRopeOff + kT * 128;   // one ring slot (the key half of a tile is the larger)
 constexpr int kChunkMax = kSfaChunkMax;   // sparse entries per workgroup (a multiple of 256)
+// Output staging at the end: each wave's 64 heads x 128 columns (256 B rows at
+// a 272-byte pitch, so the 2-byte writes of four heads a lane group apart fall
+// in distinct banks); two waves share one ring slot.
+constexpr int kStgPitch = 272;
 constexpr int kKIns = 9;                // DMA instructions per wave for a key half-tile (8 rows + rope)
 constexpr int kVIns = 8;                // ... for a value half-tile
 constexpr float kNegInf = -__builtin_huge_valf();
@@ -58,6 +63,7 @@ constexpr float kMaxInit = -1.0e30f;
 constexpr float kLazy = 8.0f;           // raise the running max only past this many log2 units
 
 static_assert(kT == 8 * kWavesPerBlock, "each wave copies 8 rows of a tile");
+static_assert(2 * 64 * kStgPitch <= kRopeOff + kT * 128, "two waves' output blocks fit one ring slot");
 static_assert(4 * kSlot + kWavesPerBlock * 64 * 16 + 4 * kChunkMax + 4 * 64 * 2 + 4 * 4 * 3 <= 160 * 1024, "LDS budget");
 static_assert(kChunkMax % 256 == 0, "two entries per thread");
 
@@ -191,11 +197,16 @@ __global__ __launch_bounds__(256, 1) void sfa_kernel(const SfaParams P) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, l16 = lane & 15;
 
-    // workgroup -> (query row, chunk, head block); head blocks of one chunk share an XCD
+    // workgroup -> (query row, chunk, head block).  Workgroup ids congruent
+    // mod 8 run on one XCD; XCD x takes the contiguous range of (query row,
+    // chunk) groups [x g8, (x + 1) g8) with all their head blocks, so the
+    // chunks of a query row (one query and block-table row) and the head
+    // blocks of a chunk (the same gathered rows) meet in one L2.
     const int id = blockIdx.x;
     const int x8 = id & 7, k8 = id >> 3;
     const int hb = k8 % P.n_hb;
-    const int grp = (k8 / P.n_hb) * 8 + x8;
+    const int g8 = (P.R * P.n_sc + 7) >> 3;
+    const int grp = x8 * g8 + k8 / P.n_hb;
     if (grp >= P.R * P.n_sc) return;               // whole workgroup leaves together
     const int qr = grp / P.n_sc, sc = grp - qr * P.n_sc;
 
@@ -553,20 +564,31 @@ __global__ __launch_bounds__(256, 1) void sfa_kernel(const SfaParams P) {
         }
     }
     __syncthreads();
-    void *dst = P.direct ? P.out : P.part_o;
-    const int64_t row0 = P.direct ? (int64_t)qr * P.QN : prow;
+    // The wave's 64 x 128 block of the output, scaled and rounded, is staged
+    // in LDS (the ring slots are free once every wave has passed the barrier
+    // above) and written with 16-byte stores: 256 contiguous bytes per head,
+    // instead of 2-byte stores that scatter 32-byte pieces.
+    char *stg = (wave < 2 ? s_slot0 : s_slot2) + (wave & 1) * (64 * kStgPitch);
 #pragma unroll
     for (int hg = 0; hg < kWavesPerBlock; hg++) {
         if (hg >= n_act) continue;
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-            const int hh = hb * 64 + hg * 16 + 4 * g + i;
-            if (hh >= P.QN) continue;
-            const float inv = s_linv[hg * 16 + 4 * g + i];
-            const int64_t base = (row0 + hh) * kD + 128 * wave + l16;
+            const int row = hg * 16 + 4 * g + i;
+            const float inv = s_linv[row];
 #pragma unroll
-            for (int j = 0; j < 8; j++) M::store(dst, base + 16 * j, acc[hg][j][i] * inv);
+            for (int j = 0; j < 8; j++) M::store(stg, row * (kStgPitch / 2) + 16 * j + l16, acc[hg][j][i] * inv);
         }
+    }
+    char *dst = reinterpret_cast<char *>(P.direct ? P.out : P.part_o);
+    const int64_t row0 = P.direct ? (int64_t)qr * P.QN : prow;
+#pragma unroll
+    for (int k = 0; k < 16; k++) {
+        const int row = 4 * k + (lane >> 4);            // head of the block
+        const int hh = hb * 64 + row;
+        if (row >= 16 * n_act || hh >= P.QN) continue;
+        const u32x4 x = *reinterpret_cast<const u32x4 *>(stg + row * kStgPitch + 16 * l16);
+        *reinterpret_cast<u32x4 *>(dst + ((row0 + hh) * kD + 128 * wave + 8 * l16) * 2) = x;
     }
 }
 
@@ -582,7 +604,7 @@ __global__ __launch_bounds__(256) void sfa_combine_kernel(const SfaParams P) {
     const float2 *ml = reinterpret_cast<const float2 *>(P.part_ml);
     auto prow = [&](int s) -> int64_t { return ((int64_t)qr * P.n_sc + s) * P.QN + hh; };
     // lane l merges elements 8 l .. 8 l + 7 of the head's row: one 16-byte
-    // load per chunk, the loads of four chunks in flight together
+    // load per chunk
     const char *po = reinterpret_cast<const char *>(P.part_o) + 16 * lane;
     auto part = [&](int s) { return *reinterpret_cast<const u32x4v *>(po + prow(s) * (kD * 2)); };
     auto elem = [](const u32x4v &x, int e) -> float {
@@ -590,36 +612,41 @@ __global__ __launch_bounds__(256) void sfa_combine_kernel(const SfaParams P) {
         const uint32_t h = (e & 1) ? (w >> 16) : (w & 0xFFFFu);
         return BF ? __builtin_bit_cast(float, h << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)h);
     };
-    float Mx = kNegInf;
-    for (int s = 0; s < P.n_sc; s++) Mx = fmaxf(Mx, ml[prow(s)].x);
+    // One memory round trip for the common case: lane s holds (m, l) of chunk
+    // s (s < 64), and the rows of the first U chunks are requested with them.
+    const int n = P.n_sc;
+    constexpr int U = 8;
+    float2 v0 = make_float2(kNegInf, 0.f);
+    if (lane < n) v0 = ml[prow(lane)];
+    u32x4v x[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) x[u] = part(min(u, n - 1));
+    float Mx = v0.x;
+    for (int s0 = 64; s0 < n; s0 += 64)
+        if (s0 + lane < n) Mx = fmaxf(Mx, ml[prow(s0 + lane)].x);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) Mx = fmaxf(Mx, __shfl_xor(Mx, o));
+    // weight of chunk `lane` (0 past the last chunk: l = 0 there)
+    const float w0 = v0.y * __builtin_amdgcn_exp2f(v0.x - Mx);
     float L = 0.f, o[8];
 #pragma unroll
     for (int e = 0; e < 8; e++) o[e] = 0.f;
-    int s = 0;
-    for (; s + 4 <= P.n_sc; s += 4) {
-        u32x4v x[4];
-        float w[4];
+    // chunks in order: the first U from registers, the rest one by one
 #pragma unroll
-        for (int u = 0; u < 4; u++) x[u] = part(s + u);
+    for (int u = 0; u < U; u++) {
+        if (u >= n) break;
+        const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w0), u));
+        L += w;
 #pragma unroll
-        for (int u = 0; u < 4; u++) {
-            const float2 v = ml[prow(s + u)];
-            w[u] = v.y * __builtin_amdgcn_exp2f(v.x - Mx);
-        }
-#pragma unroll
-        for (int u = 0; u < 4; u++) {
-            L += w[u];
-#pragma unroll
-            for (int e = 0; e < 8; e++) o[e] += w[u] * elem(x[u], e);
-        }
+        for (int e = 0; e < 8; e++) o[e] += w * elem(x[u], e);
     }
-    for (; s < P.n_sc; s++) {
-        const u32x4v x = part(s);
+    for (int s = U; s < n; s++) {
+        const u32x4v xs = part(s);
         const float2 v = ml[prow(s)];
         const float w = v.y * __builtin_amdgcn_exp2f(v.x - Mx);
         L += w;
 #pragma unroll
-        for (int e = 0; e < 8; e++) o[e] += w * elem(x, e);
+        for (int e = 0; e < 8; e++) o[e] += w * elem(xs, e);
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
     u32x4v y;

@@ -142,6 +142,19 @@ def test_paged_layouts_and_block_sizes(layout, cache_layout, bs):
     compare(inp, out)
 
 
+@pytest.mark.parametrize("bs", [32, 128])
+def test_paged_long_segments_read_block_ids_from_memory(bs):
+    """Segments spanning more block ids than a wave stages in LDS (256) read them from the
+    block table in memory; a forced piece of 320 blocks leaves whole rows of more than 256 blocks."""
+    S = 300 * bs
+    spec = IfaSpec("paged_long", 330 + bs, "bf16", "bf16", B=2, N=8, Nkv=2, D=128, layout="BNSD", S=S,
+                   len_range=(260 * bs, S), paged=True, block_size=bs, max_blocks=300, num_blocks=620,
+                   mask="bool", mask_p=0.05)
+    inp = make_ifa(spec)
+    out, _ = run_gpu(inp, split=320 * bs)
+    compare(inp, out)
+
+
 def test_paged_int8():
     spec = IfaSpec("paged_i8", 317, "f16", "i8", B=3, N=8, Nkv=2, D=128, layout="BNSD", S=512,
                    len_range=(1, 512), paged=True, block_size=64, max_blocks=8, num_blocks=26,
