@@ -46,6 +46,8 @@ __device__ __forceinline__ float wave_max(float x) {
 // One wave per (b, h) row.  The split states are read lane-parallel (lane i
 // holds split i, 64 at a time); the weighted sum over splits runs in split
 // order in every lane, so the result does not depend on timing.
+// PL = D / 64 output elements per lane.
+template <int PL>
 __global__ __launch_bounds__(256) void combine_kernel(const CombineParams P) {
     const int lane = threadIdx.x & 63;
     const int row = blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -75,16 +77,17 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineParams P) {
 
     // (m, l) of up to 64 splits in one load round, lane i holding split i
     const bool bf = P.out_bf16 != 0;
-    constexpr int kMaxPerLane = 8;          // D <= 512
-    const int per_lane = D / 64;            // D >= 64
+    constexpr int kMaxPerLane = PL;
+    constexpr int per_lane = PL;
     float o[kMaxPerLane];
 #pragma unroll
     for (int e = 0; e < kMaxPerLane; e++) o[e] = 0.f;
     float L = 0.f;
     float M = -__builtin_huge_valf();
     // The accumulators of the first U splits are requested together with the
-    // (m, l) pairs (one memory round trip for rows of up to U splits).
-    constexpr int U = 8;
+    // (m, l) pairs (one memory round trip for rows of up to U splits): 16 for
+    // head dims up to 256, 8 for 512, in at most 64 registers.
+    constexpr int U = PL >= 8 ? 8 : 16;
     float v[U][kMaxPerLane];
     auto load_acc = [&](int first, int cnt_total) {
 #pragma unroll
@@ -163,7 +166,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineParams P) {
 hipError_t launch_combine(const CombineParams &p, hipStream_t s) {
     const int rows = p.nb * p.N;
     const int blocks = (rows + kWavesPerBlock - 1) / kWavesPerBlock;
-    hipLaunchKernelGGL(combine_kernel, dim3(blocks), dim3(64 * kWavesPerBlock), 0, s, p);
+    switch (p.D / 64) {
+    case 1: hipLaunchKernelGGL(combine_kernel<1>, dim3(blocks), dim3(64 * kWavesPerBlock), 0, s, p); break;
+    case 2: hipLaunchKernelGGL(combine_kernel<2>, dim3(blocks), dim3(64 * kWavesPerBlock), 0, s, p); break;
+    case 4: hipLaunchKernelGGL(combine_kernel<4>, dim3(blocks), dim3(64 * kWavesPerBlock), 0, s, p); break;
+    default: hipLaunchKernelGGL(combine_kernel<8>, dim3(blocks), dim3(64 * kWavesPerBlock), 0, s, p); break;
+    }
     return hipGetLastError();
 }
 

@@ -108,6 +108,17 @@ def test_int8_antiquant(qdt, mode):
     compare(inp, out)
 
 
+@pytest.mark.parametrize("D", [64, 256, 512])
+def test_forced_small_splits_every_head_dim(D):
+    """Rows of up to about 90 partial states: several load rounds of the combine and its outer
+    loop over groups of 64 splits, for the head dims whose combine keeps 1, 4 or 8 elements a lane."""
+    spec = IfaSpec("split_d", 340 + D, "bf16", "bf16", B=2, N=4, Nkv=2, D=D, layout="BNSD", S=1500,
+                   len_range=(900, 1500), mask="bool", mask_p=0.1)
+    inp = make_ifa(spec)
+    out, _ = run_gpu(inp, split=16)
+    compare(inp, out)
+
+
 @pytest.mark.parametrize("N,Nkv,split", [(16, 2, 16), (16, 2, 48), (16, 2, 1024), (24, 2, 0), (40, 4, 32),
                                          (24, 2, 64)])
 def test_int8_group_of_8_splits_and_padded_groups(N, Nkv, split):
