@@ -198,6 +198,13 @@ struct Cfg {
 template <int G>
 constexpr int waves_per_eu() { return G == 1 ? 3 : 2; }
 
+// One segment of a wave's piece: batch bl of the slice, row rj = j*n_hg + hg,
+// window [lo, lo + nseg), partial slot.
+struct SegDesc {
+    int bl, rj, lo, nseg;
+    int64_t slot;
+};
+
 // EXTRA selects the optional score terms compiled in: EX_NONE, EX_MASK
 // (attenMask), or EX_PSE (pseShift, with attenMask checked at run time).
 template <int KV, int D, int G, bool PAGED, int EXTRA>
@@ -230,43 +237,82 @@ void split_kernel(const SplitParams P) {
     // position) space; it is cut into segments at row boundaries, and every
     // segment leaves one partial softmax state.
     const int64_t f1 = min(P.total, (int64_t)(wave_id + 1) * P.piece);
-    for (int64_t f = (int64_t)wave_id * P.piece; f < f1;) {
-        // Batch of position f: the number of batches whose rows start at or before f.
+    // The segment that starts at position f: its batch is the number of
+    // batches whose rows start at or before f.
+    auto decode = [&](int64_t f) -> SegDesc {
         int cnt = 0;
         for (int e0 = 0; e0 < P.nb; e0 += 64) {
             const int e = e0 + lane;
             const bool le = e < P.nb && P.pre[e] <= f;
             cnt += __popcll(__ballot(le));
         }
-        const int bl = __builtin_amdgcn_readfirstlane(cnt - 1);
-        const int len = P.len[bl];
-        const int64_t within = f - P.pre[bl];
-        const int rj = (int)(within / len);               // row of the batch: j * n_hg + hg
-        const int t0 = (int)(within - (int64_t)rj * len);
-        const int nseg = (int)min((int64_t)(len - t0), f1 - f);
+        SegDesc d;
+        d.bl = __builtin_amdgcn_readfirstlane(cnt - 1);
+        const int len = P.len[d.bl];
+        const int64_t within = f - P.pre[d.bl];
+        d.rj = (int)(within / len);
+        const int t0 = (int)(within - (int64_t)d.rj * len);
+        d.nseg = (int)min((int64_t)(len - t0), f1 - f);
+        d.lo = P.lo[d.bl] + t0;
+        const int64_t row_start = P.pre[d.bl] + (int64_t)d.rj * len;
+        d.slot = P.sbase[d.bl] + (int64_t)d.rj * P.maxseg[d.bl] + (wave_id - row_start / P.piece);
+        return d;
+    };
+    // 16-bit query of the head group (register hh holds head hh ^ hl on the
+    // scatter path, the lane-dependent order its reduce-scatter needs; head hh
+    // otherwise)
+    auto load_q16 = [&](uint32_t (&qd)[G][4], int64_t bq, int hbq, int hgq) {
+#pragma unroll
+        for (int hh = 0; hh < G; hh++) {
+            const int hq = SCATTER ? hh ^ hl : hh;
+            const bool ok = hgq * G + hq < P.g;
+            const int64_t off = ((bq * P.N + hbq + (ok ? hq : 0)) * D + 8 * c) * 2;
+            u32x4 x = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(P.q) + off);
+#pragma unroll
+            for (int w = 0; w < 4; w++) qd[hh][w] = ok ? x[w] : 0u;
+        }
+    };
+    // Dense caches: this lane's byte offset of row (lo + r) of the segment's
+    // K and V row, and the base pointers (tensor lists: batch b's own tensors).
+    auto dense_rows = [&](const SegDesc &d, const char *&kq, const char *&vq) {
+        const int64_t bq = P.b0 + d.bl;
+        const int jq = d.rj / P.n_hg;
+        const char *kb_ = kb, *vb_ = vb;
+        int64_t boff = bq * P.sB, sN = P.sN;
+        if (P.k_list) {
+            kb_ = reinterpret_cast<const char *const *>(P.k_list)[bq];
+            vb_ = reinterpret_cast<const char *const *>(P.v_list)[bq];
+            boff = 0;
+            if (P.list_bnsd) sN = (int64_t)P.list_seq[d.bl] * P.sS;
+        }
+        const int64_t base = (boff + (int64_t)jq * sN) * EB + lane_byte + (int64_t)(d.lo + r) * (P.sS * EB);
+        kq = kb_ + base;
+        vq = vb_ + base;
+    };
+    // Plain dense streams chain their segments: during the last tile of a
+    // segment the wave requests the next segment's query and first K and V
+    // rows, so a new segment starts with its operands already in flight.
+    constexpr bool kChain = !PAGED && EXTRA == EX_NONE && !I8 && !(D == 64 && G == 8);   // (that one would spill)
+    bool pref = false;                  // the next segment's query and first tile are in flight
+    SegDesc nx{0, 0, 0, 0, 0};
+    uint32_t qv[G][4];
+    uint32_t kr[RT][W], vr[RT][W];
+    for (int64_t f = (int64_t)wave_id * P.piece; f < f1;) {
+        const bool chained = kChain && pref;
+        pref = false;
+        const SegDesc sg = chained ? nx : decode(f);
+        const int bl = sg.bl, rj = sg.rj, nseg = sg.nseg;   // row of the batch: j * n_hg + hg
         const int j = rj / P.n_hg, hg = rj - j * P.n_hg;
-        const int lo = P.lo[bl] + t0;
+        const int lo = sg.lo;
         const int hi = lo + nseg;
         const int64_t b = P.b0 + bl;
-        const int64_t row_start = P.pre[bl] + (int64_t)rj * len;
-        const int64_t slot = P.sbase[bl] + (int64_t)rj * P.maxseg[bl] + (wave_id - row_start / P.piece);
+        const int64_t slot = sg.slot;
 
         // ------------------------------------------------------ query
         const int hbase = j * P.g + hg * G;
-        // register hh of the query holds head hh ^ hl on the scatter path (the
-        // lane-dependent order its reduce-scatter needs), head hh otherwise
-        uint32_t qv[G][4];
         float qmul = P.score_mul;
         if constexpr (!I8) {
-#pragma unroll
-            for (int hh = 0; hh < G; hh++) {
-                const int hq = SCATTER ? hh ^ hl : hh;
-                const bool ok = hg * G + hq < P.g;
-                const int64_t off = ((b * P.N + hbase + (ok ? hq : 0)) * D + 8 * c) * 2;
-                u32x4 x = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(P.q) + off);
-#pragma unroll
-                for (int w = 0; w < 4; w++) qv[hh][w] = ok ? x[w] : 0u;
-            }
+            if (!chained) load_q16(qv, b, hbase, hg);
         } else {
             // q' = q * s_K (K's antiquant scale) in fp16, multiplied by a power
             // of two so the largest |q'| of the wave sits just under 2^15; the
@@ -315,18 +361,7 @@ void split_kernel(const SplitParams P) {
         int64_t sS_b = 0;
         if constexpr (!PAGED) {
             sS_b = P.sS * EB;
-            // per-batch caches (tensor lists): batch b's own tensor, batch index 0
-            const char *kb_ = kb, *vb_ = vb;
-            int64_t boff = b * P.sB, sN = P.sN;
-            if (P.k_list) {
-                kb_ = reinterpret_cast<const char *const *>(P.k_list)[b];
-                vb_ = reinterpret_cast<const char *const *>(P.v_list)[b];
-                boff = 0;
-                if (P.list_bnsd) sN = (int64_t)P.list_seq[bl] * P.sS;
-            }
-            const int64_t base = (boff + (int64_t)j * sN) * EB + lane_byte + (int64_t)(lo + r) * sS_b;
-            kp = kb_ + base;
-            vp_ = vb_ + base;
+            dense_rows(sg, kp, vp_);
         }
         const int lim = hi - 1 - lo - r;     // last valid row index relative to row lo + r
         // Paged: the block ids of the segment are staged into this wave's LDS
@@ -381,11 +416,12 @@ void split_kernel(const SplitParams P) {
         // every head of the group excludes are never read: their registers
         // keep the previous tile's (finite) values, and their p is 0.
         constexpr int MB = MASKED ? G : 1;
-        uint32_t kr[RT][W], vr[RT][W];
+        if (!chained) {
 #pragma unroll
-        for (int i = 0; i < RT; i++)
+            for (int i = 0; i < RT; i++)
 #pragma unroll
-            for (int w = 0; w < W; w++) kr[i][w] = vr[i][w] = 0u;
+                for (int w = 0; w < W; w++) kr[i][w] = vr[i][w] = 0u;
+        }
         bool okr[RT];
         uint32_t mbr[MB];       // mask byte of position ts + lane (per head for per-head masks), one tile ahead
         uint32_t pbr[PR][PH];   // pseShift bits: scatter path of ts + i*RPI + r, else of ts + lane
@@ -559,11 +595,11 @@ void split_kernel(const SplitParams P) {
             load_mask(ts);
             skip_cur = mask_bits(mcur);
         }
-        issue_k(ts, skip_cur);
+        if (!chained) issue_k(ts, skip_cur);
         if constexpr (MASKED) {
             if (ts + TT < hi) load_mask(ts + TT);
         }
-        issue_v(ts, skip_cur);
+        if (!chained) issue_v(ts, skip_cur);
         issue_pse(ts);
         while (true) {
             // QK: partial dot products of the resident K rows, then the DPP
@@ -648,6 +684,25 @@ void split_kernel(const SplitParams P) {
                     if (ts + 2 * TT < hi) load_mask(ts + 2 * TT);
                 }
                 issue_k(ts + TT, skip_next);
+            }
+            // last tile: the next segment's query and K rows, into the
+            // registers this tile's scores have consumed
+            const char *nvp = nullptr;
+            int nlim = 0;
+            if constexpr (kChain) {
+                if (!more && f + nseg < f1) {
+                    nx = decode(f + nseg);
+                    const int nj = nx.rj / P.n_hg, nhg = nx.rj - nj * P.n_hg;
+                    load_q16(qv, P.b0 + nx.bl, nj * P.g + nhg * G, nhg);
+                    const char *nkp;
+                    dense_rows(nx, nkp, nvp);
+                    nlim = nx.nseg - 1 - r;
+                    const char *ptr[RT];
+#pragma unroll
+                    for (int i = 0; i < RT; i++) ptr[i] = nkp + (int64_t)min(i * RPI, nlim) * sS_b;
+                    load_rows(ptr, kr, 0);
+                    pref = true;
+                }
             }
 
             if constexpr (SCATTER) {
@@ -769,7 +824,17 @@ void split_kernel(const SplitParams P) {
                     for (int e = 0; e < 8; e++) acc[hh][e] = dot2(pp, vp[e], acc[hh][e], DotK{});
                 }
             }
-            if (!more) break;
+            if (!more) {
+                if constexpr (kChain) {
+                    if (pref) {
+                        const char *ptr[RT];
+#pragma unroll
+                        for (int i = 0; i < RT; i++) ptr[i] = nvp + (int64_t)min(i * RPI, nlim) * sS_b;
+                        load_rows(ptr, vr, 0);
+                    }
+                }
+                break;
+            }
             issue_v(ts + TT, skip_next);
 #pragma unroll
             for (int hh = 0; hh < MB; hh++) mcur[hh] = mnext[hh];

@@ -108,6 +108,20 @@ def test_int8_antiquant(qdt, mode):
     compare(inp, out)
 
 
+@pytest.mark.parametrize("layout,dt", [("BSH", "bf16"), ("BNSD", "f16")])
+@pytest.mark.parametrize("D", [64, 128, 256, 512])
+@pytest.mark.parametrize("N,Nkv", [(4, 4), (8, 4), (8, 2), (16, 2)])
+def test_plain_dense_chained_segments(layout, dt, D, N, Nkv):
+    """Plain dense caches (no mask or bias) request the next segment's query and first tile
+    during the last tile of the current one; forced pieces of 48 positions give most waves
+    several segments, over rows of every length from 0."""
+    spec = IfaSpec("chain", 360 + D + N + Nkv, dt, dt, B=4, N=N, Nkv=Nkv, D=D, layout=layout, S=300,
+                   len_range=(0, 300))
+    inp = make_ifa(spec)
+    out, _ = run_gpu(inp, split=48)
+    compare(inp, out)
+
+
 @pytest.mark.parametrize("D", [64, 256, 512])
 def test_forced_small_splits_every_head_dim(D):
     """Rows of up to about 90 partial states: several load rounds of the combine and its outer
