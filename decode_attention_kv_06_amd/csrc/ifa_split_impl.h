@@ -272,8 +272,8 @@ void split_kernel(const SplitParams P) {
             for (int w = 0; w < 4; w++) qd[hh][w] = ok ? x[w] : 0u;
         }
     };
-    // Dense caches: this lane's byte offset of row (lo + r) of the segment's
-    // K and V row, and the base pointers (tensor lists: batch b's own tensors).
+    // Dense caches: this lane's pointers into row lo + r of the segment's K and
+    // V (tensor lists: batch b's own tensors, batch index 0).
     auto dense_rows = [&](const SegDesc &d, const char *&kq, const char *&vq) {
         const int64_t bq = P.b0 + d.bl;
         const int jq = d.rj / P.n_hg;
@@ -292,7 +292,8 @@ void split_kernel(const SplitParams P) {
     // Plain dense streams chain their segments: during the last tile of a
     // segment the wave requests the next segment's query and first K and V
     // rows, so a new segment starts with its operands already in flight.
-    constexpr bool kChain = !PAGED && EXTRA == EX_NONE && !I8 && !(D == 64 && G == 8);   // (that one would spill)
+    // (Not for D = 64 with head groups of 8: the extra live state would spill.)
+    constexpr bool kChain = !PAGED && EXTRA == EX_NONE && !I8 && !(D == 64 && G == 8);
     bool pref = false;                  // the next segment's query and first tile are in flight
     SegDesc nx{0, 0, 0, 0, 0};
     uint32_t qv[G][4];
