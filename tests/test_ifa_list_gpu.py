@@ -49,3 +49,18 @@ def test_lists_over_two_launch_slices():
     inp = make_ifa(spec)
     out, _ = run_gpu(inp)
     compare(inp, out)
+
+
+@pytest.mark.parametrize("layout", ["BSH", "BNSD"])
+def test_lists_with_chained_segments(layout):
+    """Forced pieces of 48 positions: most waves chain several segments, each reading its next
+    segment's base pointers from the tensor lists (BNSD lists: head stride from each tensor)."""
+    spec = IfaSpec("kv_list_chain", 604, "bf16", "bf16", B=4, N=8, Nkv=2, D=128, layout=layout, S=400,
+                   len_range=(0, 380), kv_list=True, list_slack=30)
+    inp = make_ifa(spec)
+    out, _ = run_gpu(inp, split=48)
+    compare(inp, out)
+    padded = dict(inp)
+    padded["k_list"] = None
+    ref, _ = run_gpu(padded, split=48)
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
