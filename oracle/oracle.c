@@ -190,7 +190,8 @@ int oracle_ifa(const void *q, int q_dtype, const void *k, const void *v, int kv_
         const int64_t Sb = k_list ? list_seq[b] : S;     /* positions of this batch's cache */
         const void *kb = k_list ? k_list[b] : k, *vb = k_list ? v_list[b] : v;
         const int64_t L = actual ? actual[b] : Sb;
-        if (L > Sb) { err |= 1; continue; }
+        if (L < 0 || L > Sb) { err |= 1; continue; }
+        if (paged && L > max_blocks * block_size) { err |= 1; continue; }   /* past the block table */
         int64_t lo = 0, hi = L;
         if (!paged && pad && actual) {
             int64_t p = pad[b] < 0 ? 0 : pad[b];
@@ -208,6 +209,7 @@ int oracle_ifa(const void *q, int q_dtype, const void *k, const void *v, int kv_
         int64_t cnt = 0;
         for (int64_t s = lo; s < hi; s++) {
             if (mask) {
+                if (s >= mS) { err |= 1; break; }       /* the mask is shorter than the window */
                 int64_t mi = ((mB == 1 ? 0 : b) * mN + (mN == 1 ? 0 : h)) * mS + s;
                 if (mask[mi]) continue;
             }
@@ -328,7 +330,10 @@ int oracle_sfa(const void *q, const void *q_rope, const void *key, const void *k
             Lkv = lkv[b] - kv0;
         } else {
             Lkv = lkv ? lkv[b] : kv_seq;
-            if (layout_kv == 1) kv0 = b * kv_seq;
+            if (layout_kv == 1) {
+                kv0 = b * kv_seq;
+                if (Lkv > kv_seq) { err |= 1; continue; }   /* a length past the batch's cache */
+            }
         }
         int64_t limit = Lkv;
         if (sparse_mode == 3 && Lkv - Lq + s + 1 < limit) limit = Lkv - Lq + s + 1;

@@ -54,7 +54,7 @@ MUTANTS = {
     "sfa_block_index_not_scaled": ("const int64_t t = idx * sparse_block_size + u;", "const int64_t t = idx + u;"),
     "sfa_tnd_query_start_ignored": ("s = qr - start;", "s = qr;"),
     "sfa_tnd_cache_start_ignored": ("kv0 = b > 0 ? lkv[b - 1] : 0;", "kv0 = 0;"),
-    "sfa_bsnd_cache_batch_stride": ("if (layout_kv == 1) kv0 = b * kv_seq;", "if (layout_kv == 1) kv0 = b;"),
+    "sfa_bsnd_cache_batch_stride": ("kv0 = b * kv_seq;", "kv0 = b;"),
 }
 
 

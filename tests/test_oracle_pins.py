@@ -439,6 +439,41 @@ def test_pse_shorter_than_attended_range_is_rejected():
         oracle.ifa(short)
 
 
+def test_mask_shorter_than_the_window_is_rejected():
+    # the mask must cover every attended position (V2 page, attenMask); a
+    # shorter one is an input error, never a read past its end
+    spec = IfaSpec("pin", 938, "bf16", "bf16", B=2, N=2, Nkv=1, D=8, S=24, len_range=(24, 24), mask="u8",
+                   mask_p=0.1)
+    inp = make_ifa(spec)
+    short = dict(inp)
+    short["mask"] = inp["mask"][..., :20].contiguous()
+    with pytest.raises(ValueError):
+        oracle.ifa(short)
+    # a mask that stops exactly at the window's end is fine
+    lens = dict(inp)
+    lens["actual_seq_lengths"] = np.asarray([20, 13], dtype=np.int64)
+    lens["mask"] = short["mask"]
+    assert np.isfinite(oracle.ifa(lens)).all()
+
+
+def test_negative_length_and_length_past_the_block_table_are_rejected():
+    # V2 page, actualSeqLengths: a length lies in [0, S]; README page
+    # attention: the block table covers every attended position
+    spec = IfaSpec("pin", 939, "f16", "f16", B=2, N=2, Nkv=1, D=8, S=30, len_range=(5, 20))
+    inp = make_ifa(spec)
+    neg = dict(inp)
+    neg["actual_seq_lengths"] = np.asarray([-1, 5], dtype=np.int64)
+    with pytest.raises(ValueError):
+        oracle.ifa(neg)
+    spec = IfaSpec("pin", 939, "bf16", "bf16", B=2, N=2, Nkv=1, D=8, S=64, len_range=(10, 40), paged=True,
+                   block_size=16, max_blocks=3, num_blocks=8)
+    inp = make_ifa(spec)
+    far = dict(inp)
+    far["actual_seq_lengths"] = np.asarray([49, 10], dtype=np.int64)     # 3 blocks of 16 reach 48
+    with pytest.raises(ValueError):
+        oracle.ifa(far)
+
+
 def test_bias_of_minus_infinity_everywhere_is_an_empty_set():
     spec = IfaSpec("pin", 937, "f16", "f16", B=2, N=2, Nkv=1, D=8, S=20, len_range=(5, 20), pse=True)
     inp = make_ifa(spec)

@@ -141,6 +141,18 @@ def test_bsnd_cache_equals_paged_cache():
     np.testing.assert_allclose(oracle.sfa(_bsnd_from_paged(inp)), oracle.sfa(inp), rtol=0, atol=0)
 
 
+def test_bsnd_length_past_the_batch_cache_is_rejected():
+    # a BSND cache holds KV_S positions per batch; a longer length is an input
+    # error for the oracle, never a read into the next batch or past the end
+    bsnd = _bsnd_from_paged(make_sfa(small(lkv=[200, 317])))
+    bad = dict(bsnd)
+    lkv = bsnd["actual_seq_lengths_kv"].clone()
+    lkv[1] = bsnd["kv_seq"] + 1
+    bad["actual_seq_lengths_kv"] = lkv
+    with pytest.raises(ValueError):
+        oracle.sfa(bad)
+
+
 def test_tnd_cache_equals_bsnd_cache():
     spec = small(QS=2, sparse_mode=0, lkv=[200, 317])
     bsnd = _bsnd_from_paged(make_sfa(spec))
