@@ -7,6 +7,7 @@ no fallback path, and a missing library is an error.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import Optional
@@ -117,13 +118,41 @@ def _host_i64(a) -> Optional[np.ndarray]:
     return np.ascontiguousarray(np.asarray(a, dtype=np.int64).reshape(-1))
 
 
-def _stream(stream):
+def _on_stream(stream):
+    """Context that makes `stream` (None: the current stream; a torch stream;
+    or a raw HIP stream handle) current while a call allocates its workspace,
+    copies its pointer arrays and launches: those allocations then belong to
+    the launch stream, so torch's caching allocator hands their memory to
+    other work only after the call's kernels on that stream."""
     if stream is None:
-        stream = torch.cuda.current_stream()
-    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+        return contextlib.nullcontext()
+    if not isinstance(stream, torch.cuda.Stream):
+        stream = torch.cuda.ExternalStream(int(stream))
+    return torch.cuda.stream(stream)
 
 
-def _run(name: str, args, workspace: Optional[torch.Tensor], stream, device) -> int:
+def _check_operands(q: torch.Tensor, operands: dict, int32: tuple = ()) -> None:
+    """Reject operands the kernels cannot read as the C ABI describes them:
+    every tensor must be a contiguous GPU tensor on the query's device (a CPU
+    tensor would hand a host address to a kernel, a strided view would be
+    read as if it were dense), and index / length tensors must be int32."""
+    for name in int32:
+        t = operands.get(name)
+        if t is not None and t.dtype != torch.int32:
+            raise ValueError("%s must be torch.int32, got %s" % (name, t.dtype))
+    for name, t in operands.items():
+        if t is not None and not t.is_contiguous():
+            raise ValueError("%s must be contiguous (an expanded or strided view is read as dense)" % name)
+    if not q.is_cuda:
+        raise ValueError("query must be a GPU tensor, got one on %s" % q.device)
+    for name, t in operands.items():
+        if t is not None and t.device != q.device:
+            raise ValueError("%s must be on the query's device %s, got %s" % (name, q.device, t.device))
+
+
+def _run(name: str, args, workspace: Optional[torch.Tensor], device) -> int:
+    """Size the workspace, allocate one when none (or too small a one) is
+    given, and call the entry point on the current stream."""
     L = lib()
     nbytes = ctypes.c_size_t(0)
     rc = getattr(L, name + "_workspace_size")(ctypes.byref(args), ctypes.byref(nbytes))
@@ -132,7 +161,7 @@ def _run(name: str, args, workspace: Optional[torch.Tensor], stream, device) -> 
     if workspace is None or workspace.numel() < nbytes.value:
         workspace = torch.empty(max(int(nbytes.value), 1), dtype=torch.uint8, device=device)
     rc = getattr(L, name)(ctypes.byref(args), ctypes.c_void_p(workspace.data_ptr()),
-                          ctypes.c_size_t(workspace.numel()), _stream(stream))
+                          ctypes.c_size_t(workspace.numel()), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
     if rc != IFA_OK:
         raise IfaError(rc, name)
     return int(nbytes.value)
@@ -184,12 +213,19 @@ def _set_quant(a, quant_scale2, quant_offset2):
     a.quant_count, a.dtype_quant = quant_scale2.numel(), _DT[quant_scale2.dtype]
 
 
-def ifa_decode_args(q, k, v, out, *, num_heads, num_key_value_heads=0, input_layout="BSH", scale_value=None,
+def ifa_decode_args(q, k, v, out, *, num_heads, num_key_value_heads=0, input_layout="BSH", scale_value,
                     actual_seq_lengths=None, kv_padding_size=None, atten_mask=None, pse_shift=None,
                     antiquant_scale=None, antiquant_offset=None, antiquant_mode=0, split_tokens=0, keep=None,
                     key_list=None, value_list=None, quant_scale2=None, quant_offset2=None):
     """Fill an IfaDecodeArgs from tensors; `keep` collects arrays that must outlive the call.
-    With key_list / value_list (per-batch tensors of batch 1), k and v must be None."""
+    With key_list / value_list (per-batch tensors of batch 1), k and v must be None.
+    scale_value is required: the scale is an argument of the operator, not
+    something this marshalling layer derives."""
+    _check_operands(q, dict(query=q, key=k, value=v, attention_out=out, atten_mask=atten_mask, pse_shift=pse_shift,
+                            antiquant_scale=antiquant_scale, antiquant_offset=antiquant_offset,
+                            quant_scale2=quant_scale2, quant_offset2=quant_offset2))
+    for t in list(key_list or []) + list(value_list or []):
+        _check_operands(q, {"key_list/value_list entry": t})
     N = int(num_heads)
     kref = k if key_list is None else key_list[0]
     if input_layout == "BSH":
@@ -221,7 +257,7 @@ def ifa_decode_args(q, k, v, out, *, num_heads, num_key_value_heads=0, input_lay
     _set_quant(a, quant_scale2, quant_offset2)
     a.input_layout = input_layout.encode()
     a.batch, a.num_heads, a.num_key_value_heads, a.head_dim, a.kv_seq_len = B, N, int(num_key_value_heads), D, S
-    a.scale_value = float(scale_value if scale_value is not None else 1.0 / float(D) ** 0.5)
+    a.scale_value = float(scale_value)
     a.actual_seq_lengths = None if lens is None else lens.ctypes.data
     a.kv_padding_size = None if pads is None else pads.ctypes.data
     a.kv_padding_size_count = 0 if pads is None else len(pads)
@@ -236,14 +272,20 @@ def ifa_decode_args(q, k, v, out, *, num_heads, num_key_value_heads=0, input_lay
 def ifa_decode(q, k, v, out, *, workspace=None, stream=None, **kw) -> int:
     """IncreFlashAttention over a dense padded cache; writes `out`, returns workspace bytes used."""
     keep: list = []
-    a = ifa_decode_args(q, k, v, out, keep=keep, **kw)
-    return _run("ifa_decode", a, workspace, stream, q.device)
+    with _on_stream(stream):     # the list pointer arrays and the workspace belong to the launch stream
+        a = ifa_decode_args(q, k, v, out, keep=keep, **kw)
+        return _run("ifa_decode", a, workspace, q.device)
 
 
 def ifa_paged_args(q, key_cache, value_cache, out, block_table, *, num_heads, num_key_value_heads=0,
-                   input_layout="BNSD", scale_value=None, actual_seq_lengths=None, atten_mask=None,
+                   input_layout="BNSD", scale_value, actual_seq_lengths=None, atten_mask=None,
                    pse_shift=None, antiquant_scale=None, antiquant_offset=None, antiquant_mode=0, kv_cache_layout=0,
                    split_tokens=0, keep=None, quant_scale2=None, quant_offset2=None):
+    """Fill an IfaPagedArgs from tensors; block_table is a device int32 tensor."""
+    _check_operands(q, dict(query=q, key_cache=key_cache, value_cache=value_cache, attention_out=out,
+                            block_table=block_table, atten_mask=atten_mask, pse_shift=pse_shift,
+                            antiquant_scale=antiquant_scale, antiquant_offset=antiquant_offset,
+                            quant_scale2=quant_scale2, quant_offset2=quant_offset2), int32=("block_table",))
     N = int(num_heads)
     nkv = int(num_key_value_heads) or N
     if kv_cache_layout == 0:
@@ -262,7 +304,7 @@ def ifa_paged_args(q, key_cache, value_cache, out, block_table, *, num_heads, nu
     a.dtype_q, a.dtype_kv, a.dtype_out = _DT[q.dtype], _DT[key_cache.dtype], _DT[out.dtype]
     a.input_layout = input_layout.encode()
     a.batch, a.num_heads, a.num_key_value_heads, a.head_dim = q.shape[0], N, int(num_key_value_heads), D
-    a.scale_value = float(scale_value if scale_value is not None else 1.0 / float(D) ** 0.5)
+    a.scale_value = float(scale_value)
     a.actual_seq_lengths = None if lens is None else lens.ctypes.data
     a.atten_mask, a.dtype_mask, a.mask_batch, a.mask_heads, a.mask_seq = _ptr(mask), dmask, mB, mN, mS
     a.pse_shift, a.pse_batch, a.pse_seq = _ptr(pse), pB, pS
@@ -279,16 +321,22 @@ def ifa_paged_args(q, key_cache, value_cache, out, block_table, *, num_heads, nu
 def ifa_decode_paged(q, key_cache, value_cache, out, block_table, *, workspace=None, stream=None, **kw) -> int:
     """IncreFlashAttention over a paged cache; writes `out`, returns workspace bytes used."""
     keep: list = []
-    a = ifa_paged_args(q, key_cache, value_cache, out, block_table, keep=keep, **kw)
-    return _run("ifa_decode_paged", a, workspace, stream, q.device)
+    with _on_stream(stream):
+        a = ifa_paged_args(q, key_cache, value_cache, out, block_table, keep=keep, **kw)
+        return _run("ifa_decode_paged", a, workspace, q.device)
 
 
 def sfa_args(query, query_rope, key, key_rope, value, sparse_indices, block_table, actual_seq_lengths_kv, out, *,
-             scale_value=None, actual_seq_lengths_query=None, sparse_mode=0, sparse_block_size=1,
+             scale_value, actual_seq_lengths_query=None, sparse_mode=0, sparse_block_size=1,
              attention_mode=2, layout_query="BSND", layout_kv="PA_BSND", split_hint=0, keep=None):
     """Fill an SfaMlaArgs.  query BSND [B, Q_S, Q_N, D] or TND [Q_T, Q_N, D] (B = the length of
     actual_seq_lengths_query); key PA_BSND [blocks, block_size, 1, D], BSND [B, KV_S, 1, D] or
-    TND [KV_T, 1, D]."""
+    TND [KV_T, 1, D].  Index, table and length tensors are device int32."""
+    _check_operands(query, dict(query=query, query_rope=query_rope, key=key, key_rope=key_rope, value=value,
+                                sparse_indices=sparse_indices, block_table=block_table,
+                                actual_seq_lengths_kv=actual_seq_lengths_kv,
+                                actual_seq_lengths_query=actual_seq_lengths_query, attention_out=out),
+                    int32=("sparse_indices", "block_table", "actual_seq_lengths_kv", "actual_seq_lengths_query"))
     if layout_query == "TND":
         QT, QN, D = query.shape
         if actual_seq_lengths_query is None:
@@ -318,7 +366,7 @@ def sfa_args(query, query_rope, key, key_rope, value, sparse_indices, block_tabl
     else:
         a.kv_tokens = key.shape[0]
     a.q_tokens = QT
-    a.scale_value = float(scale_value if scale_value is not None else 1.0 / float(D + DR) ** 0.5)
+    a.scale_value = float(scale_value)
     a.sparse_block_size, a.sparse_mode, a.attention_mode = sparse_block_size, sparse_mode, attention_mode
     lq, lk = layout_query.encode(), layout_kv.encode()
     if keep is not None:
@@ -332,6 +380,7 @@ def sfa_decode_mla(query, query_rope, key, key_rope, value, sparse_indices, bloc
                    out, *, workspace=None, stream=None, **kw) -> int:
     """SparseFlashAttention (MLA-absorb); writes `out`, returns workspace bytes used."""
     keep: list = []
-    a = sfa_args(query, query_rope, key, key_rope, value, sparse_indices, block_table, actual_seq_lengths_kv, out,
-                 keep=keep, **kw)
-    return _run("sfa_decode_mla", a, workspace, stream, query.device)
+    with _on_stream(stream):
+        a = sfa_args(query, query_rope, key, key_rope, value, sparse_indices, block_table, actual_seq_lengths_kv,
+                     out, keep=keep, **kw)
+        return _run("sfa_decode_mla", a, workspace, query.device)

@@ -11,6 +11,11 @@ from decode_attention_kv_06_amd.workloads import SfaSpec
 
 # max-abs tolerances on the output dtype (fp32 accumulation on the GPU)
 TOL = {torch.float16: 5e-3, torch.bfloat16: 2e-2}
+# bounds on rms(error) / rms(output): rounding the output and P to the
+# 16-bit dtype (unit roundoff 2^-9 bf16, 2^-12 fp16) keeps the ratio near
+# 0.2 % for bf16 and a few 0.01 % for fp16; a 3 % error in the score scale
+# puts it at a few percent
+RMS_TOL = {torch.float16: 3e-3, torch.bfloat16: 1e-2}
 # bound on the fp32 result's error before an int8 output is rounded: P enters
 # P.V rounded to the KV dtype, which dominates (bf16 about 8x fp16)
 TOL_BEFORE_QUANT = {torch.float16: 1e-3, torch.bfloat16: 1e-2}
@@ -75,16 +80,27 @@ def compare_int8(inp, out, tol=None):
     return int((diff > 0).sum())
 
 
-def compare(inp, out, rows=None, tol=None):
-    """max-abs check against the oracle; returns (max_err, rms_err, rms_ref)."""
+def check_close(got: np.ndarray, ref: np.ndarray, tol: float, rms_tol: float):
+    """The two parity bars on float outputs: max-abs error within `tol` (the
+    output dtype's bound), and the RMS of the error within `rms_tol` of the
+    reference's RMS.  The second catches a systematic error (a slightly wrong
+    scale, a dropped term) that stays under the max-abs bar on long, nearly
+    uniform softmax rows, where every output element is small."""
+    assert np.isfinite(got).all(), "non-finite output"
+    err = np.abs(got - ref)
+    mx, rms, rref = float(err.max(initial=0)), float(np.sqrt((err ** 2).mean())), float(np.sqrt((ref ** 2).mean()))
+    say("  max_abs_err=%.3e rms_err=%.3e rms_out=%.3e rms_rel=%.2e (tol %.1e, rms tol %.1e)" % (
+        mx, rms, rref, rms / rref if rref > 0 else 0.0, tol, rms_tol))
+    assert mx <= tol, "max abs error %.3e > %.1e" % (mx, tol)
+    assert rms <= rms_tol * rref or rms <= 1e-12, "rms error %.3e > %.1e x rms output %.3e" % (rms, rms_tol, rref)
+    return mx, rms, rref
+
+
+def compare(inp, out, rows=None, tol=None, rms_tol=None):
+    """Parity against the oracle (check_close); returns (max_err, rms_err, rms_ref)."""
     got = out.detach().to(torch.float64).cpu().numpy().reshape(-1, inp["spec"].D)
     if rows is not None:
         got = got[np.asarray(rows)]
     ref = oracle_of(inp, rows=rows).reshape(got.shape)
-    tol = TOL[out.dtype] if tol is None else tol
-    assert np.isfinite(got).all(), "non-finite output"
-    err = np.abs(got - ref)
-    mx, rms, rref = float(err.max(initial=0)), float(np.sqrt((err ** 2).mean())), float(np.sqrt((ref ** 2).mean()))
-    say("  max_abs_err=%.3e rms_err=%.3e rms_out=%.3e (tol %.1e)" % (mx, rms, rref, tol))
-    assert mx <= tol, "max abs error %.3e > %.1e" % (mx, tol)
-    return mx, rms, rref
+    return check_close(got, ref, TOL[out.dtype] if tol is None else tol,
+                       RMS_TOL[out.dtype] if rms_tol is None else rms_tol)

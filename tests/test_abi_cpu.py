@@ -366,3 +366,72 @@ def test_paged_int8_output_validation():
     ok = paged_args(dtype_out=bd.DT_I8, quant_scale2=FAKE, quant_count=4 * 64, dtype_quant=bd.DT_F32)
     assert ws_size("ifa_decode_paged_workspace_size", ok)[0] == 0
     assert ws_size("ifa_decode_paged_workspace_size", paged_args(dtype_out=bd.DT_I8))[0] == 161001
+
+
+# ---------------------------------------------------------------- runtime failure
+def test_run_without_a_device_returns_the_runtime_code():
+    """V2 page, Return Value: a failure of the runtime underneath is 361001.
+    On a machine with no GPU a valid call reaches the HIP runtime and fails
+    there; with the planner choosing the split it stops at the device query,
+    before any launch, and with a forced split at the launch itself."""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present; this case needs a machine without one")
+    L = bd.lib()
+    ws = ctypes.c_void_p(0x2000)
+    for split in (0, 64):
+        assert L.ifa_decode(ctypes.byref(dense_args(split_tokens=split)), ws, 1 << 20, None) == 361001
+        assert L.ifa_decode_paged(ctypes.byref(paged_args(split_tokens=split)), ws, 1 << 20, None) == 361001
+    for split in (0, 2):
+        assert L.sfa_decode_mla(ctypes.byref(sfa_args(split_hint=split)), ws, 1 << 26, None) == 361001
+
+
+# ---------------------------------------------------------------- Python binding
+def _cpu_ifa_tensors():
+    import torch
+    q = torch.zeros(2, 1, 8 * 128, dtype=torch.bfloat16)
+    k = torch.zeros(2, 64, 2 * 128, dtype=torch.bfloat16)
+    return q, k, k.clone(), torch.empty_like(q)
+
+
+def test_binding_rejects_host_tensors_before_calling_the_library():
+    q, k, v, out = _cpu_ifa_tensors()
+    with pytest.raises(ValueError, match="GPU tensor"):
+        bd.ifa_decode_args(q, k, v, out, num_heads=8, num_key_value_heads=2, input_layout="BSH", scale_value=0.1)
+
+
+def test_binding_rejects_strided_views_and_wide_index_tensors():
+    import torch
+    q, k, v, out = _cpu_ifa_tensors()
+    mask = torch.zeros(1, 1, 1, 64, dtype=torch.bool).expand(2, 8, 1, 64)     # stride-0 view
+    with pytest.raises(ValueError, match="contiguous"):
+        bd.ifa_decode_args(q, k, v, out, num_heads=8, num_key_value_heads=2, input_layout="BSH", scale_value=0.1,
+                           atten_mask=mask)
+    with pytest.raises(ValueError, match="contiguous"):
+        bd.ifa_decode_args(q, k[:, ::2], v[:, ::2], out, num_heads=8, num_key_value_heads=2, input_layout="BSH",
+                           scale_value=0.1)
+    qp = torch.zeros(2, 8, 1, 128, dtype=torch.bfloat16)
+    cache = torch.zeros(4, 2, 32, 128, dtype=torch.bfloat16)
+    bt64 = torch.zeros(2, 2, dtype=torch.int64)             # torch's default integer dtype
+    with pytest.raises(ValueError, match="int32"):
+        bd.ifa_paged_args(qp, cache, cache, torch.empty_like(qp), bt64, num_heads=8, num_key_value_heads=2,
+                          scale_value=0.1, actual_seq_lengths=[10, 20])
+    q5 = torch.zeros(1, 1, 4, 512, dtype=torch.bfloat16)
+    qr = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    kc = torch.zeros(2, 16, 1, 512, dtype=torch.bfloat16)
+    kr = torch.zeros(2, 16, 1, 64, dtype=torch.bfloat16)
+    idx = torch.zeros(1, 1, 1, 8, dtype=torch.int32)
+    bt = torch.zeros(1, 2, dtype=torch.int32)
+    lkv = torch.full((1,), 20, dtype=torch.int32)
+    for bad in ("sparse_indices", "block_table", "actual_seq_lengths_kv"):
+        t = dict(sparse_indices=idx, block_table=bt, actual_seq_lengths_kv=lkv)
+        t[bad] = t[bad].long()
+        with pytest.raises(ValueError, match="int32"):
+            bd.sfa_args(q5, qr, kc, kr, kc, t["sparse_indices"], t["block_table"], t["actual_seq_lengths_kv"],
+                        torch.empty_like(q5), scale_value=0.04)
+
+
+def test_binding_requires_the_scale():
+    q, k, v, out = _cpu_ifa_tensors()
+    with pytest.raises(TypeError):
+        bd.ifa_decode_args(q, k, v, out, num_heads=8, num_key_value_heads=2, input_layout="BSH")

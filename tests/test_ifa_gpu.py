@@ -305,3 +305,26 @@ def test_per_head_mask_with_padded_head_group():
     inp = make_ifa(spec)
     out, _ = run_gpu(inp)
     compare(inp, out)
+
+
+@pytest.mark.parametrize("lists", [False, True])
+def test_non_current_stream_without_workspace(lists):
+    # the binding allocates the workspace (and, for tensor lists, copies the
+    # pointer arrays) on the launch stream, which is not the current stream
+    spec = small_variant("dense_gqa_bf16_bsh")
+    if lists:
+        spec = replace(spec, kv_list=True, layout="BNSD", cfg_id=spec.cfg_id + 1)
+    inp = make_ifa(spec)
+    dev = harness.to_device(inp)
+    out = harness.alloc_out(dev)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    assert torch.cuda.current_stream() != s
+    say("GPU step: side stream, binding-allocated workspace, lists=%s" % lists)
+    for _ in range(3):   # later calls reuse freed blocks of the caching allocator
+        harness.call(dev, out, stream=s)
+        junk = torch.empty(8 << 20, dtype=torch.uint8, device="cuda")
+        junk.fill_(0xFF)
+    s.synchronize()
+    torch.cuda.synchronize()
+    compare(inp, out)
