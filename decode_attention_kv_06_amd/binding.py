@@ -22,6 +22,7 @@ IFA_OK = 0
 IFA_ERR_PARAM_NULLPTR = 161001
 IFA_ERR_PARAM_INVALID = 161002
 IFA_ERR_RUNTIME = 361001
+NOALLOC_SCRATCH_BYTES = 32 << 20      # IFA_NOALLOC_SCRATCH_BYTES of ifa_decode.h
 
 DT_F16, DT_BF16, DT_I8, DT_U8, DT_BOOL, DT_F32 = 1, 2, 3, 4, 5, 6
 _DT = {torch.float16: DT_F16, torch.bfloat16: DT_BF16, torch.int8: DT_I8, torch.uint8: DT_U8, torch.bool: DT_BOOL,
@@ -95,6 +96,8 @@ def lib() -> ctypes.CDLL:
             run = getattr(L, name)
             run.argtypes = [ctypes.POINTER(st), P, ctypes.c_size_t, P]
             run.restype = ctypes.c_int
+        L.ifa_decode_noalloc.argtypes = [ctypes.POINTER(IfaDecodeArgs), P]
+        L.ifa_decode_noalloc.restype = ctypes.c_int
         L.ifa_status_string.argtypes = [ctypes.c_int]
         L.ifa_status_string.restype = ctypes.c_char_p
         L.ifa_abi_version.restype = ctypes.c_int
@@ -275,6 +278,20 @@ def ifa_decode(q, k, v, out, *, workspace=None, stream=None, **kw) -> int:
     with _on_stream(stream):     # the list pointer arrays and the workspace belong to the launch stream
         a = ifa_decode_args(q, k, v, out, keep=keep, **kw)
         return _run("ifa_decode", a, workspace, q.device)
+
+
+def ifa_decode_noalloc(q, k, v, out, *, stream=None, **kw) -> None:
+    """ifa_decode on the library's built-in scratch (no workspace, nothing
+    allocated by the library); raises IfaError(161002) when the call needs more
+    scratch than the library holds.  With key_list / value_list this wrapper
+    builds the two device pointer arrays itself, which allocates: a caller
+    that cannot allocate passes its own arrays to the C entry point."""
+    keep: list = []
+    with _on_stream(stream):
+        a = ifa_decode_args(q, k, v, out, keep=keep, **kw)
+        rc = lib().ifa_decode_noalloc(ctypes.byref(a), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    if rc != IFA_OK:
+        raise IfaError(rc, "ifa_decode_noalloc")
 
 
 def ifa_paged_args(q, key_cache, value_cache, out, block_table, *, num_heads, num_key_value_heads=0,

@@ -541,6 +541,32 @@ Launch paged_launch(const ifa_paged_args *a, const IfaPlan &p) {
     return L;
 }
 
+// ----------------------------------------------------------------- built-in scratch
+
+// Device memory of ifa_decode_noalloc: the split kernel's partial states
+// (sums, maxima, normalisers) for callers that cannot allocate a workspace.
+// Every GPU the library runs on holds its own copy for the life of the
+// process.  In host code `scratch` names a host-side stand-in, never the
+// device address: kernels and copies get the address hipGetSymbolAddress
+// returns for the current device, taken once per device.
+constexpr size_t kScratchBytes = (size_t)IFA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+void *g_scratch[64];   // per-device address of `scratch`, null until first use
+
+int scratch_address(void **out) {
+    int dev = 0;
+    if (current_device(&dev) != IFA_OK || dev < 0 || dev >= 64) return IFA_ERR_RUNTIME;
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (!g_scratch[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return IFA_ERR_RUNTIME;
+        g_scratch[dev] = ptr;
+    }
+    *out = g_scratch[dev];
+    return IFA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -577,6 +603,24 @@ int ifa_decode(const ifa_decode_args *a, void *ws, size_t ws_bytes, ifa_stream_t
     rc = finish_plan(p, a->split_tokens);
     if (rc) return rc;
     return run(p, dense_launch(a, p, c), ws, ws_bytes, reinterpret_cast<hipStream_t>(stream));
+}
+
+int ifa_decode_noalloc(const ifa_decode_args *a, ifa_stream_t stream) {
+    IfaPlan p;
+    IfaCommon c;
+    int rc = plan_dense(a, p, c);
+    if (rc) return rc;
+    rc = finish_plan(p, a->split_tokens);
+    if (rc) return rc;
+    if (p.workspace > kScratchBytes) {
+        fprintf(stderr, "ifa_decode_noalloc: the call needs %zu bytes of scratch, more than the built-in %zu\n",
+                p.workspace, kScratchBytes);
+        return IFA_ERR_PARAM_INVALID;
+    }
+    void *ws = nullptr;
+    rc = scratch_address(&ws);
+    if (rc) return rc;
+    return run(p, dense_launch(a, p, c), ws, kScratchBytes, reinterpret_cast<hipStream_t>(stream));
 }
 
 int ifa_decode_paged_workspace_size(const ifa_paged_args *a, size_t *bytes) {

@@ -301,6 +301,24 @@ int ifa_decode(const ifa_decode_args *args, void *workspace, size_t workspace_by
 int ifa_decode_paged(const ifa_paged_args *args, void *workspace, size_t workspace_bytes, ifa_stream_t stream);
 int sfa_decode_mla(const sfa_mla_args *args, void *workspace, size_t workspace_bytes, ifa_stream_t stream);
 
+/*
+ * ifa_decode without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  It validates and computes exactly as ifa_decode
+ * does, with the same kernels, and keeps the partial states in a built-in
+ * device array of IFA_NOALLOC_SCRATCH_BYTES (32 MiB) that every GPU the
+ * library runs on holds until the process ends.  A call whose workspace
+ * (the size ifa_decode_workspace_size returns) exceeds that returns
+ * IFA_ERR_PARAM_INVALID and launches nothing.  It allocates nothing and
+ * calls no allocating routine; the first call on a device looks up that
+ * device's copy of the array (a HIP runtime failure there is
+ * IFA_ERR_RUNTIME).  All calls on one GPU share its array: calls that may
+ * overlap on one GPU (other streams, other threads) race and must not be
+ * issued; calls ordered on one stream are safe.
+ */
+#define IFA_NOALLOC_SCRATCH_BYTES (32u << 20)
+int ifa_decode_noalloc(const ifa_decode_args *args, ifa_stream_t stream);
+
 /* A static string naming a status code. */
 const char *ifa_status_string(int status);
 
