@@ -1,20 +1,39 @@
 #!/usr/bin/env python3
 """Decode-attention benchmark on one MI355X.
 
-Times the library's decode call on a seeded synthetic workload resident in
-HBM and prints one JSON line: µs per call, achieved HBM GB/s over the
-algorithmic bytes, the dominant kernel's roofline fraction (timed live with
-HIP events that the library records around that kernel on the call's
-stream), and the fp64 CPU oracle timed on the host cores as a baseline.
+Times the library's decode calls on seeded synthetic workloads resident in
+HBM and prints one JSON line.  The headline is the dense GQA decode (bf16,
+BSH, 64 batches, 32 query heads over 8 KV heads, head dim 128, lengths
+U[1024, 8192]); the same line carries a record for each other workload:
+the tiny fp16 decode, the paged decode with a mask, the int8-cache decode
+with left padding and the sparse MLA decode.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--flush]
+Protocol, per workload:
+  * inputs, output and workspace are allocated once, outside every timed region;
+  * warm-up: at least --warmup calls and at least --warmup-ms of them (the
+    clocks need tens of milliseconds of work to settle);
+  * timed, flushed (the headline): --steps iterations of [evict the caches:
+    write (zero) a 512 MiB buffer, twice the 256 MiB last-level cache, then
+    read it back with the read probe so that the flush's own dirty lines are
+    written back before the call rather than during it; event; call; event],
+    the flush outside the event pair.  The library also records two events on
+    the call's stream around its dominant kernel, which give that kernel's
+    duration for the roofline;
+  * timed, warm (secondary, labelled): --steps back-to-back calls between two
+    events, nothing in between, plus the host wall time of that loop;
+  * median, p10 and p90 of the flushed call times; GB/s = algorithmic bytes /
+    median, as a fraction of the 8 TB/s HBM peak and of the read ceiling the
+    library's read probe measures on this device under the same flush.
 
 Algorithmic bytes count what the method must move: the K/V rows of the
-attended window (unmasked rows only when a mask is given), the mask bytes of
-the window, block-table entries used, antiquant parameters, the positional
-bias of the window, q and the output;
-for the sparse path the selected rows (512 + 64 + 512 elements), the indices,
-the block-table entries used, q, q_rope and the output.
+attended window (for a mask, the rows some query head of the KV head
+attends), the mask bytes of the window, block-table entries used, antiquant
+parameters, the positional bias of the window, q and the output; for the
+sparse path the selected rows (512 + 64 + 512 elements), the indices, the
+block-table entries used, q, q_rope and the output.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME|all] [--flush write-read|write|read|none]
+    python bench.py --read-ceiling            # only the read probe
 """
 from __future__ import annotations
 
@@ -31,8 +50,16 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode attention µs/call + achieved HBM GB/s (% of MI355X peak) at 1 GPU"
 HBM_PEAK_GBS = 8000.0
-CPU_BASELINE_S = 10.0      # seconds of oracle time the CPU baseline is measured over
+FLUSH_BYTES = 512 << 20
+CEILING_BYTES = 1 << 30                  # read-probe buffer: about one dense decode's K/V bytes
+CPU_BASELINE_S = 10.0                    # seconds of oracle time per CPU-baseline leg
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.txt")
+HEADLINE = "dense_gqa_bf16_bsh"
+OTHERS = ["tiny_dense_f16", "paged_bf16_bs128", "int8_leftpad_f16", "sfa_mla_bf16"]
+
+
+def log(msg: str) -> None:
+    print("bench: " + msg, file=sys.stderr, flush=True)
 
 
 def sources_sha() -> str:
@@ -64,6 +91,7 @@ def measured_traffic(workload: str):
     return None
 
 
+# ------------------------------------------------------------------ bytes
 def algorithmic_bytes(inp) -> dict:
     import numpy as np
     from decode_attention_kv_06_amd.workloads import SfaSpec
@@ -79,6 +107,7 @@ def algorithmic_bytes(inp) -> dict:
         qo = R * s.QN * (s.D + s.DR) * eb + R * s.QN * s.D * eb
         return {"total": kv + extra + qo, "kv": kv, "streamed": kv + extra + qo}
     B, N, nkv, D = s.B, s.N, s.nkv, s.D
+    g = N // nkv
     eb = 1 if s.kv_dtype == "i8" else 2
     S = inp["S"]
     L = np.asarray(inp["lengths_drawn"], dtype=np.int64)
@@ -91,18 +120,21 @@ def algorithmic_bytes(inp) -> dict:
         bad = (lo < 0) | (hi < 0)
         lo[bad] = hi[bad] = 0
     n_win = (hi - lo).astype(np.int64)
-    attended = n_win.copy()
+    head_rows = n_win * nkv                  # (position, KV head) rows of each window
     mask_bytes = 0
     m = inp["mask"]
     if m is not None:
         mm = m.numpy().astype(bool)
         for b in range(B):
-            row = mm[b if mm.shape[0] == B else 0, :, 0, lo[b]:hi[b]]
-            attended[b] = int((~row).all(axis=0).sum()) if mm.shape[1] > 1 else int((~row[0]).sum())
+            row = mm[b if mm.shape[0] == B else 0, :, 0, lo[b]:hi[b]]      # [1 | N, window]
+            if mm.shape[1] == 1:
+                head_rows[b] = int((~row[0]).sum()) * nkv
+            else:   # a KV head's row is needed when any query head of its group attends it
+                head_rows[b] = sum(int((~row[j * g:(j + 1) * g]).any(axis=0).sum()) for j in range(nkv))
             mask_bytes += row.size
-    row_bytes = nkv * D * eb * 2
-    kv = int(attended.sum()) * row_bytes
-    streamed = int(n_win.sum()) * row_bytes
+    row_bytes = D * eb * 2                   # one K row and one V row of one KV head
+    kv = int(head_rows.sum()) * row_bytes
+    streamed = int(n_win.sum()) * nkv * row_bytes
     qo = 2 * B * N * D * 2
     extra = mask_bytes
     if s.paged:
@@ -131,6 +163,11 @@ def sfa_attended_rows(inp) -> int:
     pos = idx[:, :, None] * sbs + np.arange(sbs)
     ok = (idx[:, :, None] >= 0) & (pos < limit[:, None, None])
     return int(ok.sum())
+
+
+def sfa_flops(inp) -> int:
+    s = inp["spec"]
+    return sfa_attended_rows(inp) * s.QN * 2 * (s.D + s.DR + s.D)
 
 
 def describe_config(inp) -> dict:
@@ -162,26 +199,65 @@ def describe_config(inp) -> dict:
     return c
 
 
-def cpu_baseline(inp, alg_bytes: int) -> dict:
+# ------------------------------------------------------------------ CPU baseline
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_rate(inp, alg_bytes: int, threads: int) -> dict:
+    """The fp64 oracle as it stands, at `threads` threads, on a bounded sample:
+    output rows spread over the whole workload (every batch and head), as
+    many as take about CPU_BASELINE_S seconds, repeated whole when one pass
+    over every row takes less.  GB/s = the sample's share of the
+    algorithmic bytes / time."""
+    import numpy as np
     import oracle
     from decode_attention_kv_06_amd.workloads import SfaSpec
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
-    # whole-workload oracle runs, repeated until about 10 s of CPU time have
-    # been timed (a single run when one already takes that long)
-    run = oracle.sfa if isinstance(inp["spec"], SfaSpec) else oracle.ifa
+    s = inp["spec"]
+    sparse = isinstance(s, SfaSpec)
+    run = oracle.sfa if sparse else oracle.ifa
+    total_rows = inp["q_rows"] * s.QN if sparse else s.B * s.N
+    used = oracle.set_threads(threads)
+    probe = np.arange(0, total_rows, max(1, total_rows // (4 * used)))    # a few rows per thread
     t0 = time.perf_counter()
-    n = 0
+    run(inp, rows=probe)
+    per_row = (time.perf_counter() - t0) / len(probe)
+    n_rows = int(min(total_rows, max(len(probe), CPU_BASELINE_S / max(per_row, 1e-9))))
+    rows = np.unique(np.linspace(0, total_rows - 1, n_rows).astype(np.int64))
+    t0 = time.perf_counter()
+    passes = 0
     while True:
-        run(inp)
-        n += 1
+        run(inp, rows=None if len(rows) == total_rows else rows)
+        passes += 1
         dt = time.perf_counter() - t0
-        if dt >= CPU_BASELINE_S or dt / n * (n + 1) > 3 * CPU_BASELINE_S:
+        if len(rows) < total_rows or dt >= CPU_BASELINE_S or dt / passes * (passes + 1) > 3 * CPU_BASELINE_S:
             break
-    return {"value": round(n * alg_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": "the whole workload (every output row), %d fp64 oracle run(s) in %.1f s" % (n, dt)}
+    share = len(rows) / total_rows
+    what = ("every output row, %d pass(es)" % passes if len(rows) == total_rows else
+            "%d of %d output rows, evenly spaced over all batches and heads" % (len(rows), total_rows))
+    return {"value": round(passes * share * alg_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": used,
+            "seconds": round(dt, 2), "sample": "%s of the %s workload, fp64 oracle, %.1f s" % (what, s.name, dt)}
 
 
+def cpu_baseline(inp, alg_bytes: int) -> dict:
+    all_threads = len(os.sched_getaffinity(0))
+    many = _oracle_rate(inp, alg_bytes, all_threads)
+    one = _oracle_rate(inp, alg_bytes, 1)
+    res = dict(many)
+    res["kind"] = "oracle"
+    res["cpu_model"] = cpu_model()
+    res["single_thread"] = one
+    return res
 
+
+# ------------------------------------------------------------------ GPU timing
 def build_args(d: dict, o, split: int, keep: list):
     """Entry-point name and its argument struct for the workload on device."""
     from decode_attention_kv_06_amd import binding
@@ -215,16 +291,198 @@ def build_args(d: dict, o, split: int, keep: list):
                                 quant_scale2=d.get("quant_scale2"), quant_offset2=d.get("quant_offset2"))
     return "ifa_decode", a
 
+
+def pct(sorted_vals, q: float) -> float:
+    """Linear-interpolated percentile of an already sorted list."""
+    if len(sorted_vals) == 1:
+        return sorted_vals[0]
+    x = q * (len(sorted_vals) - 1)
+    i = int(math.floor(x))
+    j = min(i + 1, len(sorted_vals) - 1)
+    return sorted_vals[i] + (sorted_vals[j] - sorted_vals[i]) * (x - i)
+
+
+def stats_us(ms_list) -> dict:
+    v = sorted(x * 1e3 for x in ms_list)
+    return {"median": round(pct(v, 0.5), 2), "p10": round(pct(v, 0.1), 2), "p90": round(pct(v, 0.9), 2),
+            "mean": round(sum(v) / len(v), 2)}
+
+
+class Gpu:
+    """Device state shared by every measurement: the stream, the flush
+    buffers and the read probe."""
+
+    def __init__(self, flush: str):
+        import torch
+        from decode_attention_kv_06_amd import binding
+        self.torch = torch
+        self.stream = torch.cuda.current_stream()
+        self.flush_mode = flush
+        self.flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda:0") if flush != "none" else None
+        if self.flush_buf is not None:
+            self.flush_buf.zero_()
+        self.sink = torch.zeros(64, dtype=torch.int32, device="cuda:0")
+        L = binding.lib()
+        L.ifa_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+        L.ifa_read_probe.restype = ctypes.c_int
+        self.lib = L
+        self.s_ptr = ctypes.c_void_p(self.stream.cuda_stream)
+
+    def events(self, n):
+        evs = [self.torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for e in evs:
+            e.record(self.stream)      # creates the underlying hipEvent
+        return evs
+
+    def read(self, buf) -> None:
+        rc = self.lib.ifa_read_probe(ctypes.c_void_p(buf.data_ptr()), ctypes.c_size_t(buf.numel()),
+                                     ctypes.c_void_p(self.sink.data_ptr()), self.s_ptr)
+        if rc != 0:
+            raise RuntimeError("ifa_read_probe returned %d" % rc)
+
+    def flush(self) -> None:
+        """Evict L2 and the last-level cache before a timed call, outside the
+        call's events.  Zeroing 512 MiB evicts every line the call could hit;
+        reading the buffer back afterwards writes the flush's dirty lines to
+        HBM before the call starts.  Zeroing alone leaves up to the whole
+        last-level cache dirty, and a kernel whose loads allocate there then
+        pays for writing it back (measured: the sparse gather kernel 43 -> 68
+        us), which is the flush's cost, not the kernel's."""
+        if self.flush_mode in ("write", "write-read"):
+            self.flush_buf.zero_()
+        if self.flush_mode in ("read", "write-read"):
+            self.read(self.flush_buf)
+
+    def timed(self, one_call, steps: int, warmup: int, warmup_ms: float, kernel_events: bool = True) -> dict:
+        """Warm-up, then the flushed loop (call events and, when the library
+        records them, dominant-kernel events), then the warm loop."""
+        torch = self.torch
+        t_w = time.perf_counter()
+        n_warm = 0
+        while n_warm < warmup or (time.perf_counter() - t_w) * 1e3 < warmup_ms:
+            self.flush()
+            one_call(None, None)
+            n_warm += 1
+            if n_warm % 64 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        cb, ce = self.events(steps), self.events(steps)
+        kb, ke = (self.events(steps), self.events(steps)) if kernel_events else (None, None)
+        torch.cuda.synchronize()
+        for i in range(steps):
+            self.flush()
+            cb[i].record(self.stream)
+            one_call(kb[i] if kb else None, ke[i] if ke else None)
+            ce[i].record(self.stream)
+        torch.cuda.synchronize()
+        call_ms = [cb[i].elapsed_time(ce[i]) for i in range(steps)]
+        kern_ms = [kb[i].elapsed_time(ke[i]) for i in range(steps)] if kb else None
+        # warm: back to back, nothing between the calls
+        e0, e1 = self.events(1)[0], self.events(1)[0]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record(self.stream)
+        for _ in range(steps):
+            one_call(None, None)
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        host_ms = (time.perf_counter() - t0) * 1e3 / steps
+        return {"call": stats_us(call_ms), "kernel": stats_us(kern_ms) if kern_ms else None,
+                "warm_us": round(e0.elapsed_time(e1) / steps * 1e3, 2), "host_us": round(host_ms * 1e3, 2),
+                "warmup_calls": n_warm}
+
+    def read_ceiling(self, steps: int, warmup: int, warmup_ms: float) -> dict:
+        """GB/s of the read probe over CEILING_BYTES, under the same flush."""
+        buf = self.torch.zeros(CEILING_BYTES, dtype=self.torch.uint8, device="cuda:0")
+        r = self.timed(lambda kb, ke: self.read(buf), steps, warmup, warmup_ms, kernel_events=False)
+        del buf
+        med = r["call"]["median"]
+        return {"gbs": round(CEILING_BYTES / (med * 1e-6) / 1e9, 1), "bytes": CEILING_BYTES,
+                "us": r["call"], "flush": self.flush_mode,
+                "what": "ifa_read_probe: 16 B per lane nontemporal loads, 8 in flight per lane, 8 workgroups per CU"}
+
+
+def measure(gpu: Gpu, name: str, args, ceiling_gbs=None) -> tuple:
+    """Run one workload through the protocol; returns (record, host inputs)."""
+    import torch
+    from decode_attention_kv_06_amd import binding, harness
+    from decode_attention_kv_06_amd.workloads import SfaSpec, make_ifa, make_sfa, workloads
+
+    spec = workloads()[name]
+    log("generating %s" % name)
+    inp = make_sfa(spec) if isinstance(spec, SfaSpec) else make_ifa(spec)
+    dev = harness.to_device(inp, "cuda:0")
+    out = harness.alloc_out(dev)
+    alg = algorithmic_bytes(inp)
+    nbytes = harness.call(dev, out, split=args.split)          # sizes the workspace
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda:0")
+    keep: list = []
+    entry, a = build_args(dev, out, args.split, keep)
+    fn = getattr(binding.lib(), entry)
+    a_ref = ctypes.byref(a)
+    ws_ptr, ws_len = ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws.numel())
+
+    def one_call(kb, ke):
+        a.profile_event_begin = kb.cuda_event if kb is not None else None
+        a.profile_event_end = ke.cuda_event if ke is not None else None
+        rc = fn(a_ref, ws_ptr, ws_len, gpu.s_ptr)
+        if rc != 0:
+            raise binding.IfaError(rc, entry)
+
+    steps = args.steps * (10 if name == "tiny_dense_f16" else 1)     # the launch-bound call gets more samples
+    log("timing %s (%d flushed + %d warm calls)" % (name, steps, steps))
+    r = gpu.timed(one_call, steps, args.warmup, args.warmup_ms)
+    torch.cuda.synchronize()
+    med_s = r["call"]["median"] * 1e-6
+    kern_mean_s = r["kernel"]["mean"] * 1e-6
+    gbs = alg["total"] / med_s / 1e9
+    achieved = alg["total"] / kern_mean_s / 1e9
+    sparse = isinstance(spec, SfaSpec)
+    rec = {
+        "config": describe_config(inp),
+        "entry_point": entry,
+        "algorithmic_bytes": alg["total"],
+        "streamed_bytes": alg["streamed"],
+        "us_per_call": r["call"],
+        "gbs": round(gbs, 1),
+        "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "pct_of_measured_ceiling": round(100.0 * gbs / ceiling_gbs, 2) if ceiling_gbs else None,
+        "warm_back_to_back_us_per_call": r["warm_us"],
+        "warm_gbs": round(alg["total"] / (r["warm_us"] * 1e-6) / 1e9, 1),
+        "host_wall_us_per_call": r["host_us"],
+        "timed_calls": steps,
+        "warmup_calls_run": r["warmup_calls"],
+        "roofline": {"bound": "hbm", "kernel": "sfa_kernel (sparse gather)" if sparse else "split_kernel (split-KV)",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(name),
+                     "kernel_us": r["kernel"]},
+    }
+    if name == "tiny_dense_f16":
+        rec["roofline"]["note"] = "launch-bound: 0.24 MB per call, 0.03 us at the HBM peak"
+    if sparse:
+        fl = sfa_flops(inp)
+        rec["mfma"] = {"flops": fl, "tflops": round(fl / kern_mean_s / 1e12, 1),
+                       "pct_of_bf16_dense_peak": round(100.0 * fl / kern_mean_s / 2.5e15, 2)}
+    del dev, out, ws, keep, a
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec, inp
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--steps", type=int, default=100, help="timed calls per loop (10x for the tiny workload)")
     ap.add_argument("--warmup", type=int, default=50, help="untimed calls first (at least this many)")
     ap.add_argument("--warmup-ms", type=float, default=100.0,
                     help="...and at least this long: the GPU takes tens of milliseconds of calls to reach steady clocks")
-    ap.add_argument("--workload", default="dense_gqa_bf16_bsh")
-    ap.add_argument("--flush", action="store_true", help="evict caches between calls (outside the timed events)")
+    ap.add_argument("--workload", default="all",
+                    help="'all' (the dense GQA headline plus a record per other workload) or one workload name")
+    ap.add_argument("--flush", choices=["write-read", "write", "read", "none"], default="write-read",
+                    help="cache eviction before each timed call, outside its events: zero 512 MiB and read it "
+                         "back (default), zero only, read only, or none")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--read-ceiling", action="store_true", help="only measure the read probe")
     ap.add_argument("--split", type=int, default=0, help="force the work-item size (0 = planner)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -232,132 +490,64 @@ def main() -> int:
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         return 2
 
-    import torch
-    from decode_attention_kv_06_amd import binding, harness
-    from decode_attention_kv_06_amd.workloads import SfaSpec, make_ifa, make_sfa, workloads
+    gpu = Gpu(args.flush)
+    log("read ceiling (%d MiB, flush=%s)" % (CEILING_BYTES >> 20, args.flush))
+    ceiling = gpu.read_ceiling(args.steps, args.warmup, args.warmup_ms)
+    if args.read_ceiling:
+        print(json.dumps({"read_ceiling": ceiling}), flush=True)
+        return 0
 
-    spec = workloads()[args.workload]
-    print("bench: generating %s" % args.workload, file=sys.stderr, flush=True)
-    inp = make_sfa(spec) if isinstance(spec, SfaSpec) else make_ifa(spec)
-    dev = harness.to_device(inp, "cuda:0")
-    out = harness.alloc_out(dev)
-    alg = algorithmic_bytes(inp)
-    stream = torch.cuda.current_stream()
+    headline = HEADLINE if args.workload == "all" else args.workload
+    others = OTHERS if args.workload == "all" else []
+    rec, inp = measure(gpu, headline, args, ceiling["gbs"])
+    per_config = {}
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the fp64 CPU oracle (all threads, then one)")
+        cpu = cpu_baseline(inp, rec["algorithmic_bytes"])
+    del inp
+    for name in others:
+        r, inp_o = measure(gpu, name, args, ceiling["gbs"])
+        del inp_o
+        per_config[name] = r
 
-    # workspace sized once, outside the timed region
-    nbytes = harness.call(dev, out, split=args.split)
-    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda:0")
-    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0") if args.flush else None
-
-    def make_events(n):
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
-        for e in evs:
-            e.record(stream)      # creates the underlying hipEvent
-        return evs
-
-    # arguments are marshalled once: the timed loop only calls into the library
-    keep: list = []
-    name, a = build_args(dev, out, args.split, keep)
-    fn = getattr(binding.lib(), name)
-    a_ref = ctypes.byref(a)
-    ws_ptr, ws_len = ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws.numel())
-    s_ptr = ctypes.c_void_p(stream.cuda_stream)
-
-    def one_call(kb=None, ke=None):
-        a.profile_event_begin = kb.cuda_event if kb is not None else None
-        a.profile_event_end = ke.cuda_event if ke is not None else None
-        rc = fn(a_ref, ws_ptr, ws_len, s_ptr)
-        if rc != 0:
-            raise binding.IfaError(rc, name)
-
-    # warm-up: at least W calls and at least --warmup-ms of them (short calls
-    # need hundreds before the clocks settle)
-    t_w = time.perf_counter()
-    n_warm = 0
-    while n_warm < args.warmup or (time.perf_counter() - t_w) * 1e3 < args.warmup_ms:
-        if flush_buf is not None:
-            flush_buf.zero_()
-        one_call()
-        n_warm += 1
-        if n_warm % 64 == 0:
-            torch.cuda.synchronize()
-    torch.cuda.synchronize()
-
-    K = args.steps
-    # Timed region 1 (the throughput `value`): K back-to-back calls bracketed
-    # by a synchronize and two events, nothing recorded per call.  With
-    # --flush every call is preceded by a cache flush and bracketed by its own
-    # events instead, and the flush stays outside them.
-    cb, ce = make_events(K), make_events(K)
-    e0, e1 = make_events(1)[0], make_events(1)[0]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for i in range(K):
-        if flush_buf is not None:
-            flush_buf.zero_()
-            cb[i].record(stream)
-        one_call()
-        if flush_buf is not None:
-            ce[i].record(stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / K
-    gpu_ms_step = e0.elapsed_time(e1) / K
-
-    # Timed region 2 (the roofline): the same K calls, with the events the
-    # library records on the call's stream around its dominant kernel.
-    kb, ke = make_events(K), make_events(K)
-    torch.cuda.synchronize()
-    for i in range(K):
-        if flush_buf is not None:
-            flush_buf.zero_()
-        one_call(kb[i], ke[i])
-    torch.cuda.synchronize()
-
-    kern_ms = sorted(kb[i].elapsed_time(ke[i]) for i in range(K))
-    kern_mean = sum(kern_ms) / K
-    if flush_buf is not None:
-        call_ms = sorted(cb[i].elapsed_time(ce[i]) for i in range(K))
-        call_mean = sum(call_ms) / K
-        call_med = call_ms[K // 2]
-    else:
-        call_mean = call_med = gpu_ms_step
-    per_call_s = (call_mean if args.flush else ms_step) / 1e3
-    value = alg["total"] / per_call_s / 1e9
-    achieved = alg["total"] / (kern_mean / 1e3) / 1e9
-    s = inp["spec"]
-    dtype = s.dtype if isinstance(s, SfaSpec) else s.q_dtype
-    kernel_name = "sfa gather kernel" if isinstance(s, SfaSpec) else "split_kernel (split-KV decode)"
+    from decode_attention_kv_06_amd.workloads import SfaSpec, workloads
+    s = workloads()[headline]
+    med_us = rec["us_per_call"]["median"]
     res = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": rec["gbs"],
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": K,
+        "steps": args.steps,
         "warmup": args.warmup,
-        "warmup_calls_run": n_warm,
-        "ms_per_step": round(ms_step, 5),
+        "ms_per_step": round(med_us / 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": dtype,
+        "dtype": s.dtype if isinstance(s, SfaSpec) else s.q_dtype,
         "data": "synthetic (seeded, generated on the host; see decode_attention_kv_06_amd/workloads.py)",
-        "config": describe_config(inp),
-        "us_per_call": round(per_call_s * 1e6, 2),
-        "us_per_call_gpu_events": round(call_med * 1e3, 2),
-        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
-        "algorithmic_bytes": alg["total"],
-        "streamed_bytes": alg["streamed"],
-        "flush_between_calls": bool(args.flush),
-        "roofline": {"bound": "hbm", "kernel": kernel_name, "achieved": round(achieved, 2),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(args.workload), "kernel_us_mean": round(kern_mean * 1e3, 2)},
+        "config": rec["config"],
+        "us_per_call": med_us,
+        "us_per_call_p10": rec["us_per_call"]["p10"],
+        "us_per_call_p90": rec["us_per_call"]["p90"],
+        "pct_of_hbm_peak": rec["pct_of_hbm_peak"],
+        "pct_of_measured_ceiling": rec["pct_of_measured_ceiling"],
+        "flush_between_calls": args.flush != "none",
+        "flush": "%s %d MiB before every timed call, outside its events" % (args.flush, FLUSH_BYTES >> 20)
+                 if args.flush != "none" else "none",
+        "timing": "per-call HIP events on the call's stream; median, p10 and p90 over the flushed calls",
+        "warm_back_to_back_us_per_call": rec["warm_back_to_back_us_per_call"],
+        "host_wall_us_per_call": rec["host_wall_us_per_call"],
+        "algorithmic_bytes": rec["algorithmic_bytes"],
+        "streamed_bytes": rec["streamed_bytes"],
+        "roofline": rec["roofline"],
+        "read_ceiling": ceiling,
+        "headline": rec,
+        "per_config": per_config,
     }
-    if not args.no_cpu_baseline:
-        print("bench: timing the fp64 CPU oracle", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(inp, alg["total"])
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
     print(json.dumps(res), flush=True)
     return 0
 

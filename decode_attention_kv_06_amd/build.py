@@ -19,7 +19,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libifadecode.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["api.hip", "ifa_split.hip", "ifa_split_f16.hip", "ifa_split_bf16.hip", "ifa_split_i8.hip",
-           "ifa_combine.hip", "sfa.hip", "sfa_kernel.hip"]
+           "ifa_combine.hip", "sfa.hip", "sfa_kernel.hip", "read_probe.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I", INCLUDE, "-I", CSRC]
 

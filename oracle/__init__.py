@@ -47,6 +47,8 @@ def bind(path: str) -> ctypes.CDLL:
     lb.oracle_sfa.argtypes = [P, P, P, P, P, I, P, P, P, P, I, I, I64, I64, I64, I64, I64, I64, I64, I64, I64, I64,
                               I64, I, I64, D, P, I64, P]
     lb.oracle_sfa.restype = I
+    lb.oracle_set_threads.argtypes = [I]
+    lb.oracle_set_threads.restype = I
     lb.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
     lb.oracle_f16_to_f64.restype = D
     lb.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
@@ -159,6 +161,11 @@ def quant_int8(o: np.ndarray, scale: torch.Tensor, offset=None, use=None):
     if rc != 0:
         raise ValueError("oracle_quant_int8 rejected its input (code %d)" % rc)
     return codes, pre
+
+
+def set_threads(n: int) -> int:
+    """Threads the oracle's row loops use from now on; returns the count in effect."""
+    return lib().oracle_set_threads(int(n))
 
 
 def f16_to_f64(bits: int) -> float:

@@ -61,8 +61,23 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 enum { O_F16 = 1, O_BF16 = 2, O_I8 = 3, O_F32 = 6 };
+
+/* Threads the parallel row loops below may use from now on (n >= 1); returns
+ * the count in effect.  Only the CPU-baseline timing changes it. */
+int oracle_set_threads(int n) {
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+    return omp_get_max_threads();
+#else
+    (void)n;
+    return 1;
+#endif
+}
 enum { O_BSH = 0, O_BNSD = 1, O_BSND = 2 };
 
 /* IEEE-754 binary16 -> double, written from the format's definition:

@@ -17,7 +17,9 @@ FAKE = ctypes.c_void_p(0x1000)
 
 
 def header_functions():
-    src = open(os.path.join(ROOT, "include", "ifa_decode.h")).read()
+    """Every function declared by the headers under include/."""
+    inc = os.path.join(ROOT, "include")
+    src = "".join(open(os.path.join(inc, f)).read() for f in sorted(os.listdir(inc)) if f.endswith(".h"))
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:int|const char \*)\s*\**\s*(\w+)\s*\(", src, flags=re.M)))
 
@@ -26,7 +28,7 @@ def test_library_exports_every_declared_function():
     names = header_functions()
     assert {"ifa_decode", "ifa_decode_paged", "sfa_decode_mla", "ifa_decode_workspace_size",
             "ifa_decode_paged_workspace_size", "sfa_decode_mla_workspace_size", "ifa_status_string",
-            "ifa_abi_version"} <= set(names)
+            "ifa_abi_version", "ifa_read_probe"} <= set(names)
     L = bd.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -435,3 +437,13 @@ def test_binding_requires_the_scale():
     q, k, v, out = _cpu_ifa_tensors()
     with pytest.raises(TypeError):
         bd.ifa_decode_args(q, k, v, out, num_heads=8, num_key_value_heads=2, input_layout="BSH")
+
+
+def test_read_probe_rejects_bad_arguments_without_a_device():
+    L = bd.lib()
+    L.ifa_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    assert L.ifa_read_probe(None, 1024, FAKE, None) == 161001
+    assert L.ifa_read_probe(FAKE, 1024, None, None) == 161001
+    assert L.ifa_read_probe(FAKE, 1000, FAKE, None) == 161002          # not a multiple of 16
+    assert L.ifa_read_probe(FAKE, 0, FAKE, None) == 161002
+    assert L.ifa_read_probe(ctypes.c_void_p(0x1008), 1024, FAKE, None) == 161002   # misaligned
