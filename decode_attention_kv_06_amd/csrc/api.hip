@@ -27,6 +27,7 @@ namespace {
 using namespace ifa;
 
 constexpr int kAbiVersion = 5;
+constexpr int kRowModeTiles = 4;     // longest row (in split-kernel tiles) that row mode takes
 
 bool is_float_dt(int dt) { return dt == IFA_DT_F16 || dt == IFA_DT_BF16; }
 
@@ -54,6 +55,8 @@ struct SlicePlan {
 struct IfaPlan {
     int kv = 0, D = 0, G = 0, n_hg = 0, g = 0, N = 0, Nkv = 0, B = 0;
     bool paged = false;
+    bool out_i8 = false;                 // int8 output (finished by the combine)
+    bool row_mode = false;               // one wave per row, finished in place, no combine
     int extra = EX_NONE;                 // split kernel variant (mask / positional bias)
     std::vector<Window> win;             // per batch
     std::vector<int64_t> list_seq;       // per-batch caches: positions of each tensor
@@ -101,6 +104,39 @@ int finish_plan(IfaPlan &p, int64_t split_tokens) {
     const int64_t rows_per_batch = (int64_t)p.Nkv * p.n_hg;
     p.slices.clear();
     p.total_slots = 0;
+    // Row mode: when every row is at most a few tiles long and the rows fit in
+    // the resident waves, one wave per row finishes the call in one launch
+    // (the split kernel writes the output); splitting rows further would buy
+    // less streaming time than the combine launch costs.  16-bit caches and
+    // outputs only (the int8 epilogues live in the combine).
+    p.row_mode = false;
+    if (split_tokens <= 0 && p.kv != KV_I8 && !p.out_i8 && p.B <= kSliceBatches) {
+        const int64_t tile = (int64_t)(p.G >= 8 ? 4 : 8) * (512 / p.D);   // positions per split-kernel tile
+        int32_t max_len = 0;
+        for (const Window &w : p.win) max_len = std::max(max_len, w.hi - w.lo);
+        p.row_mode = max_len <= kRowModeTiles * tile && (int64_t)p.B * rows_per_batch <= waves;
+    }
+    if (p.row_mode) {
+        SlicePlan sp;
+        sp.b0 = 0;
+        sp.nb = p.B;
+        sp.pre.resize(sp.nb + 1);
+        sp.sbase.assign(sp.nb, 0);
+        sp.maxseg.assign(sp.nb, 0);
+        int64_t pos = 0, max_len = 1;
+        for (int i = 0; i < sp.nb; i++) {
+            sp.pre[i] = pos;
+            pos += (int64_t)(p.win[i].hi - p.win[i].lo) * rows_per_batch;
+            max_len = std::max<int64_t>(max_len, p.win[i].hi - p.win[i].lo);
+        }
+        sp.pre[sp.nb] = pos;
+        sp.total = pos;
+        sp.piece = max_len;
+        sp.n_pieces = (int)(sp.nb * rows_per_batch);
+        p.slices.push_back(std::move(sp));
+        p.workspace = 0;
+        return IFA_OK;
+    }
     for (int b0 = 0; b0 < p.B; b0 += kSliceBatches) {
         SlicePlan sp;
         sp.b0 = b0;
@@ -279,6 +315,7 @@ int plan_dense(const ifa_decode_args *a, IfaPlan &p, IfaCommon &c) {
     if (a->atten_mask && a->mask_seq < max_hi) return IFA_ERR_PARAM_INVALID;
     if (a->pse_shift && a->pse_seq < max_hi) return IFA_ERR_PARAM_INVALID;
     p.extra = a->pse_shift ? EX_PSE : a->atten_mask ? EX_MASK : EX_NONE;
+    p.out_i8 = a->dtype_out == IFA_DT_I8;
     return IFA_OK;
 }
 
@@ -326,6 +363,7 @@ int plan_paged(const ifa_paged_args *a, IfaPlan &p, IfaCommon &c) {
     if (a->atten_mask && a->mask_seq < max_hi) return IFA_ERR_PARAM_INVALID;
     if (a->pse_shift && a->pse_seq < max_hi) return IFA_ERR_PARAM_INVALID;
     p.extra = a->pse_shift ? EX_PSE : a->atten_mask ? EX_MASK : EX_NONE;
+    p.out_i8 = a->dtype_out == IFA_DT_I8;
     return IFA_OK;
 }
 
@@ -402,6 +440,8 @@ int run(const IfaPlan &p, const Launch &L, void *ws, size_t ws_bytes, hipStream_
     sp.aq_mode = L.aq_mode;
     sp.q_bf16 = L.q_bf16;
     sp.score_mul = (float)(L.scale * 1.4426950408889634);
+    sp.out = L.out;
+    sp.row_mode = p.row_mode ? 1 : 0;
 
     CombineParams cp;
     memset(&cp, 0, sizeof cp);
@@ -444,11 +484,11 @@ int run(const IfaPlan &p, const Launch &L, void *ws, size_t ws_bytes, hipStream_
         sp.part_ml = part_ml + s.slot_base * p.G * 2;
         cp.part_acc = sp.part_acc;
         cp.part_ml = sp.part_ml;
-        if (s.total > 0 && launch_split(sp, p.kv, p.D, p.G, p.paged, p.extra, stream) != hipSuccess)
+        if ((s.total > 0 || p.row_mode) && launch_split(sp, p.kv, p.D, p.G, p.paged, p.extra, stream) != hipSuccess)
             return IFA_ERR_RUNTIME;
         if (timed && si + 1 == p.slices.size() && hipEventRecord(L.ev_end, stream) != hipSuccess)
             return IFA_ERR_RUNTIME;
-        if (launch_combine(cp, stream) != hipSuccess) return IFA_ERR_RUNTIME;
+        if (!p.row_mode && launch_combine(cp, stream) != hipSuccess) return IFA_ERR_RUNTIME;
     }
     return IFA_OK;
 }

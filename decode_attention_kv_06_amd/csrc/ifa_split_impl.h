@@ -20,6 +20,8 @@
 // The next tile's K/V loads are in flight while the current tile computes.
 #pragma once
 
+#include <type_traits>
+
 #include "internal.h"
 
 namespace ifa {
@@ -235,8 +237,27 @@ void split_kernel(const SplitParams P) {
 
     // This wave's piece of the flattened (batch, KV head, head group,
     // position) space; it is cut into segments at row boundaries, and every
-    // segment leaves one partial softmax state.
-    const int64_t f1 = min(P.total, (int64_t)(wave_id + 1) * P.piece);
+    // segment leaves one partial softmax state.  In row mode the piece is
+    // row wave_id of the slice, whole.
+    int64_t f0 = (int64_t)wave_id * P.piece;
+    int64_t f1 = min(P.total, f0 + P.piece);
+    if constexpr (!I8) {
+        if (P.row_mode) {
+            const int rpb = P.Nkv * P.n_hg;
+            const int bl = wave_id / rpb, rj = wave_id - bl * rpb;
+            const int len = P.len[bl];
+            f0 = P.pre[bl] + (int64_t)rj * len;
+            f1 = f0 + len;
+            if (len == 0) {     // an empty window: zero rows
+                const int j = rj / P.n_hg, hg = rj - j * P.n_hg;
+                using T = std::conditional_t<KV == KV_BF16, __bf16, _Float16>;
+                T *o = reinterpret_cast<T *>(P.out) + ((P.b0 + bl) * P.N + j * P.g + hg * G) * (int64_t)D;
+                const int nh = min(G, P.g - hg * G);
+                for (int i = lane; i < nh * D; i += 64) o[i] = (T)0.f;
+                return;
+            }
+        }
+    }
     // The segment that starts at position f: its batch is the number of
     // batches whose rows start at or before f.
     auto decode = [&](int64_t f) -> SegDesc {
@@ -298,7 +319,7 @@ void split_kernel(const SplitParams P) {
     SegDesc nx{0, 0, 0, 0, 0};
     uint32_t qv[G][4];
     uint32_t kr[RT][W], vr[RT][W];
-    for (int64_t f = (int64_t)wave_id * P.piece; f < f1;) {
+    for (int64_t f = f0; f < f1;) {
         const bool chained = kChain && pref;
         pref = false;
         const SegDesc sg = chained ? nx : decode(f);
@@ -866,6 +887,24 @@ void split_kernel(const SplitParams P) {
             }
         }
 
+        if constexpr (!I8) {
+            if (P.row_mode) {   // the row is whole: normalise, round to nearest even, write out
+                if (r == 0) {
+                    using T = std::conditional_t<KV == KV_BF16, __bf16, _Float16>;
+                    typedef T t8 __attribute__((ext_vector_type(8)));
+#pragma unroll
+                    for (int hh = 0; hh < G; hh++) {
+                        if (hg * G + hh >= P.g) break;
+                        t8 o;
+#pragma unroll
+                        for (int e = 0; e < 8; e++) o[e] = (T)(l[hh] > 0.f ? acc[hh][e] / l[hh] : 0.f);
+                        *reinterpret_cast<t8 *>(reinterpret_cast<T *>(P.out) + (b * P.N + hbase + hh) * D + 8 * c) = o;
+                    }
+                }
+                f += nseg;
+                continue;
+            }
+        }
         if (r == 0) {
 #pragma unroll
             for (int hh = 0; hh < G; hh++) {

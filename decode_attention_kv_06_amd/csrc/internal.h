@@ -25,6 +25,8 @@ enum SplitExtra { EX_NONE = 0, EX_MASK = 1, EX_PSE = 2 };
 // boundaries.  Each segment writes one partial softmax state (G heads) to
 // slot sbase[b] + (j*n_hg + hg)*maxseg[b] + (w - first piece of the row);
 // the combine kernel recomputes the same slots from the same tables.
+// Small problems (every row a few tiles long) run in row mode instead: wave
+// w takes row w whole and writes its output, so one launch does the call.
 struct SplitParams {
     const void *q;          // [B, N, D] (any query layout, S = 1)
     const void *k;          // cache base
@@ -37,6 +39,7 @@ struct SplitParams {
     const void *k_scale;    // int8 only: antiquant scale, q dtype
     const void *const *k_list;   // per-batch caches: device array of B device pointers, or nullptr
     const void *const *v_list;
+    void *out;              // row mode: the output [B, N, D] (query dtype), written in place
     int64_t sB, sN, sS;     // dense element strides of (b, j, s)
     int64_t blk_stride, head_stride, row_stride;   // paged element strides
     int64_t mask_sB, mask_sH;                      // mask strides (0 = broadcast)
@@ -52,6 +55,8 @@ struct SplitParams {
     int32_t aq_mode;        // int8: 1 per-tensor, 2 per-channel
     int32_t q_bf16;         // int8 kernels: query dtype is bf16
     int32_t list_bnsd;      // per-batch BNSD caches: the head stride is list_seq[b] * sS
+    int32_t row_mode;       // one wave per (b, j, hg) row, normalised and written out by that wave
+                            // (16-bit caches and outputs); no partial states, no combine
     float score_mul;        // scale * log2(e)
     int32_t nb;             // batches in this slice
     int32_t b0;             // first batch of the slice
