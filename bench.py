@@ -399,7 +399,7 @@ class Gpu:
         med = r["call"]["median"]
         return {"gbs": round(CEILING_BYTES / (med * 1e-6) / 1e9, 1), "bytes": CEILING_BYTES,
                 "us": r["call"], "flush": self.flush_mode,
-                "what": "ifa_read_probe: 16 B per lane nontemporal loads, 8 in flight per lane, 8 workgroups per CU"}
+                "what": "ifa_read_probe: 16 B per lane nontemporal loads, 8 in flight per lane, one workgroup of 4 waves per CU"}
 
 
 def measure(gpu: Gpu, name: str, args, ceiling_gbs=None) -> tuple:
