@@ -45,7 +45,7 @@ def bind(path: str) -> ctypes.CDLL:
     lb.oracle_quant_int8.argtypes = [P, I64, I64, P, P, I, P, P]
     lb.oracle_quant_int8.restype = I
     lb.oracle_sfa.argtypes = [P, P, P, P, P, I, P, P, P, P, I, I, I64, I64, I64, I64, I64, I64, I64, I64, I64, I64,
-                              I64, I, I64, D, P, I64, P]
+                              I64, I, I64, D, P, I64, P, P, P]
     lb.oracle_sfa.restype = I
     lb.oracle_set_threads.argtypes = [I]
     lb.oracle_set_threads.restype = I
@@ -120,9 +120,11 @@ def ifa(inp: dict, rows=None, scale=None, use=None) -> np.ndarray:
     return out.reshape(B, N, D) if rows is None else out
 
 
-def sfa(inp: dict, rows=None, use=None) -> np.ndarray:
+def sfa(inp: dict, rows=None, use=None, lse: bool = False):
     """Exact SFA output [query rows, QN, D] (or [len(rows), D]) in float64;
-    rows are (query row) * QN + head."""
+    rows are (query row) * QN + head.  With lse=True also the softmax_max and
+    softmax_sum outputs ([query rows, QN], or [len(rows)]): returns
+    (out, softmax_max, softmax_sum)."""
     s = inp["spec"]
     key = inp["key"].contiguous()
     value = inp["value"].contiguous()
@@ -130,6 +132,8 @@ def sfa(inp: dict, rows=None, use=None) -> np.ndarray:
     R = inp["q_rows"]
     n = R * s.QN if rows is None else len(rows_a)
     out = np.empty((n, s.D), dtype=np.float64)
+    lmax = np.empty(n, dtype=np.float64) if lse else None
+    lsum = np.empty(n, dtype=np.float64) if lse else None
     bt = inp["block_table"]
     lq = inp["actual_seq_lengths_query"]
     lkv = inp["actual_seq_lengths_kv"]
@@ -142,10 +146,15 @@ def sfa(inp: dict, rows=None, use=None) -> np.ndarray:
         _ptr(None if lkv is None else lkv.contiguous()), _ptr(None if lq is None else lq.contiguous()),
         lay_q, lay_kv, s.B, s.QS, R, s.QN, s.D, s.DR, inp["sparse_indices"].shape[-1], s.block_size,
         key.shape[0] if lay_kv == 0 else 0, bt.shape[1] if bt is not None else 0, inp.get("kv_seq", 0),
-        int(s.sparse_mode), int(s.sparse_block_size), float(s.scale_value), _ptr(rows_a), n, _ptr(out))
+        int(s.sparse_mode), int(s.sparse_block_size), float(s.scale_value), _ptr(rows_a), n, _ptr(out),
+        _ptr(lmax), _ptr(lsum))
     if rc != 0:
         raise ValueError("oracle_sfa rejected its input (code %d)" % rc)
-    return out.reshape(R, s.QN, s.D) if rows is None else out
+    if rows is None:
+        out = out.reshape(R, s.QN, s.D)
+        if lse:
+            lmax, lsum = lmax.reshape(R, s.QN), lsum.reshape(R, s.QN)
+    return (out, lmax, lsum) if lse else out
 
 
 def quant_int8(o: np.ndarray, scale: torch.Tensor, offset=None, use=None):

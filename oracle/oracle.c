@@ -115,14 +115,18 @@ static double elem(const void *base, int dtype, int64_t i) {
 }
 
 /* Softmax-weighted sum over n gathered rows.  x[i] are the scores, rows of V
- * are fetched through vrow(i, d).  Writes D doubles to out. */
+ * are fetched through vrow(i, d).  Writes D doubles to out, and, when m_out
+ * and z_out are given, the softmax's maximum score and its sum of
+ * exp(score - maximum) (-inf and 0 when nothing is attended). */
 typedef double (*vfetch_fn)(const void *ctx, int64_t i, int64_t d);
 
 static void softmax_combine(const double *x, int64_t n, int64_t D, vfetch_fn vrow, const void *ctx,
-                            double *w, double *out) {
+                            double *w, double *out, double *m_out, double *z_out) {
     double m = -INFINITY;
     for (int64_t i = 0; i < n; i++)
         if (x[i] > m) m = x[i];
+    if (m_out) *m_out = m;
+    if (z_out) *z_out = 0.0;
     if (n == 0 || m == -INFINITY) {      /* nothing attended (every score -inf counts as none) */
         for (int64_t d = 0; d < D; d++) out[d] = 0.0;
         return;
@@ -132,6 +136,7 @@ static void softmax_combine(const double *x, int64_t n, int64_t D, vfetch_fn vro
         w[i] = exp(x[i] - m);
         z += w[i];
     }
+    if (z_out) *z_out = z;
     for (int64_t d = 0; d < D; d++) {
         double acc = 0.0;
         for (int64_t i = 0; i < n; i++) acc += w[i] * vrow(ctx, i, d);
@@ -262,7 +267,7 @@ int oracle_ifa(const void *q, int q_dtype, const void *k, const void *v, int kv_
             cnt++;
         }
         ifa_vctx c = {vb, kv_dtype, ko, aq_scale, aq_offset, q_dtype, aq_mode, j, Nkv, D};
-        softmax_combine(x, cnt, D, ifa_vfetch, &c, w, o);
+        softmax_combine(x, cnt, D, ifa_vfetch, &c, w, o, NULL, NULL);
         free(x);
         free(w);
         free(ko);
@@ -308,13 +313,18 @@ static double sfa_vfetch(const void *c, int64_t i, int64_t d) {
  *
  *   scale is the float32 scale value widened to double.
  *   rows: list of (query row) * QN + head (NULL -> all); out has nrows*D doubles.
+ *   lse_max, lse_sum (NULL, or nrows doubles each): softmax_max and
+ *   softmax_sum of the README's return_softmax_lse outputs, per output row:
+ *   the maximum of the scaled scores the softmax takes, and the sum of
+ *   exp(score - maximum); -inf and 0 for a row that attends nothing (the
+ *   scores being the softmax's own input, after the scale, is a reading).
  */
 int oracle_sfa(const void *q, const void *q_rope, const void *key, const void *key_rope, const void *value,
                int dtype, const int32_t *sparse_indices, const int32_t *block_table, const int32_t *lkv,
                const int32_t *lq, int layout_q, int layout_kv, int64_t B, int64_t QS, int64_t q_rows,
                int64_t QN, int64_t D, int64_t DR, int64_t sparse_size, int64_t block_size, int64_t num_blocks,
                int64_t max_blocks, int64_t kv_seq, int sparse_mode, int64_t sparse_block_size, double scale,
-               const int64_t *rows, int64_t nrows, double *out) {
+               const int64_t *rows, int64_t nrows, double *out, double *lse_max, double *lse_sum) {
     if (layout_q != 0 && layout_q != 1) return -3;
     if (layout_kv < 0 || layout_kv > 2) return -3;
     if ((layout_q == 1 && !lq) || (layout_kv != 1 && !lkv) || sparse_block_size < 1) return -3;
@@ -384,7 +394,7 @@ int oracle_sfa(const void *q, const void *q_rope, const void *key, const void *k
             }
         }
         sfa_vctx c = {value, dtype, ko};
-        softmax_combine(x, cnt, D, sfa_vfetch, &c, w, o);
+        softmax_combine(x, cnt, D, sfa_vfetch, &c, w, o, lse_max ? lse_max + r : NULL, lse_sum ? lse_sum + r : NULL);
         free(x);
         free(w);
         free(ko);

@@ -16,7 +16,7 @@ from decode_attention_kv_06_amd.workloads import IfaSpec, SfaSpec, make_ifa, mak
 from dataclasses import replace
 
 from test_oracle_pins import _sfa_gather_ref, _sfa_small, dense_kv_bnsd, sdpa_ref, to64
-from test_oracle_sfa_breadth import _bsnd_from_paged, paged_rows, sdpa_rows
+from test_oracle_sfa_breadth import _bsnd_from_paged, paged_rows, scores_rows, sdpa_rows
 from test_oracle_sfa_breadth import small as _sfa_breadth
 
 MUTANTS = {
@@ -55,6 +55,8 @@ MUTANTS = {
     "sfa_tnd_query_start_ignored": ("s = qr - start;", "s = qr;"),
     "sfa_tnd_cache_start_ignored": ("kv0 = b > 0 ? lkv[b - 1] : 0;", "kv0 = 0;"),
     "sfa_bsnd_cache_batch_stride": ("kv0 = b * kv_seq;", "kv0 = b;"),
+    "lse_sum_not_shifted": ("if (z_out) *z_out = z;", "if (z_out) *z_out = z * exp(m);"),
+    "lse_max_of_first_score": ("if (m_out) *m_out = m;", "if (m_out) *m_out = n ? x[0] : m;"),
 }
 
 
@@ -111,7 +113,7 @@ def _battery(lib):
     res.append(("sfa_bound", close(oracle.sfa(inp, use=lib), _sfa_gather_ref(inp))))
     res.append(("quant", _quant_checks(lib)))
     for name, fn in (("sfa_causal", _sfa_causal), ("sfa_block_wise", _sfa_block_wise), ("sfa_tnd_q", _sfa_tnd_q),
-                     ("sfa_tnd_kv", _sfa_tnd_kv), ("sfa_bsnd_kv", _sfa_bsnd_kv)):
+                     ("sfa_tnd_kv", _sfa_tnd_kv), ("sfa_bsnd_kv", _sfa_bsnd_kv), ("sfa_lse", _sfa_lse)):
         try:
             res.append((name, fn(lib, close)))
         except ValueError:
@@ -206,6 +208,21 @@ def _sfa_gather_ref_rows(bsnd):
 def _sfa_bsnd_kv(lib, close):
     inp = make_sfa(_sfa_breadth(QS=2, sparse_mode=0, lkv=[200, 317]))
     return close(oracle.sfa(_bsnd_from_paged(inp), use=lib), _sfa_gather_ref_rows(_bsnd_from_paged(inp)))
+
+
+def _sfa_lse(lib, close):
+    """softmax_max / softmax_sum against torch's max and logsumexp of the gathered scores."""
+    bsnd = _bsnd_from_paged(make_sfa(_sfa_breadth(QS=1, sparse_mode=0, sparse_size=120, lkv=[200, 317])))
+    s = bsnd["spec"]
+    _, mx, sm = oracle.sfa(bsnd, use=lib, lse=True)
+    ok = True
+    for b in range(s.B):
+        idx = bsnd["sparse_indices"][b, 0, 0].long()
+        idx = idx[(idx >= 0) & (idx < s.lkv[b])]
+        x = scores_rows(bsnd, b, b * s.kv_seq + idx)
+        ok &= close(mx[b], torch.amax(x, dim=1).numpy())
+        ok &= close(np.log(sm[b]) + mx[b], torch.logsumexp(x, dim=1).numpy())
+    return ok
 
 
 def _build(src, path):

@@ -193,3 +193,62 @@ def test_generator_keeps_the_causal_domain():
             v = row[row >= 0]
             assert int(v.max()) <= L - spec.lq[b] + s
             assert len(set(v.tolist())) == len(v)
+
+
+# ------------------------------------------------------- softmax_max / softmax_sum
+def scores_rows(inp, qrow, rows):
+    """Scaled scores [QN, len(rows)] of one query row against cache rows, in float64."""
+    s = inp["spec"]
+    key = to64(inp["key"]).reshape(-1, s.D)
+    kr = to64(inp["key_rope"]).reshape(-1, s.DR)
+    q = to64(inp["q"]).reshape(-1, s.QN, s.D)[qrow]
+    qr = to64(inp["q_rope"]).reshape(-1, s.QN, s.DR)[qrow]
+    return (q @ key[rows].T + qr @ kr[rows].T) * s.scale_value
+
+
+@pytest.mark.parametrize("mode", [0, 3])
+def test_softmax_max_and_sum_match_torch_on_the_gathered_scores(mode):
+    # SparseFlashAttention README, parameter table (softmax_max_out: the max of
+    # the query-key scores; softmax_sum_out: the sum of exp(score - max))
+    spec = small(QS=3, lq=[3, 2], sparse_mode=mode, sparse_size=200, lkv=[200, 317], past_limit=True)
+    inp = _bsnd_from_paged(make_sfa(spec))
+    out, mx, sm = oracle.sfa(inp, lse=True)
+    np.testing.assert_allclose(out, oracle.sfa(inp), rtol=0, atol=0)     # the output is unchanged
+    s = inp["spec"]
+    for b in range(2):
+        Lq, Lkv = spec.lq[b], spec.lkv[b]
+        for qs in range(3):
+            r = b * 3 + qs
+            idx = inp["sparse_indices"][b, qs, 0].long()
+            limit = 0 if qs >= Lq else (Lkv if mode == 0 else min(Lkv, Lkv - Lq + qs + 1))
+            idx = idx[(idx >= 0) & (idx < limit)]
+            if len(idx) == 0:
+                assert (mx[r] == -np.inf).all() and (sm[r] == 0).all()
+                continue
+            x = scores_rows(inp, r, b * inp["kv_seq"] + idx)                 # [QN, n]
+            np.testing.assert_allclose(mx[r], torch.amax(x, dim=1).numpy(), rtol=0, atol=1e-12)
+            lse = torch.logsumexp(x, dim=1).numpy()
+            np.testing.assert_allclose(np.log(sm[r]) + mx[r], lse, rtol=0, atol=1e-12)
+    assert (mx[5] == -np.inf).all()           # batch 1 has two query rows: row 5 attends nothing
+
+
+def test_softmax_sum_is_at_least_one_and_shift_invariant():
+    # the maximal score contributes exp(0) = 1; adding a constant to every
+    # rope score (q_rope scaled so its dot with a constant key_rope is fixed)
+    # moves the max by that constant and leaves the sum alone
+    spec = small(sparse_size=100, lkv=[150, 300])
+    inp = _bsnd_from_paged(make_sfa(spec))
+    _, mx, sm = oracle.sfa(inp, lse=True)
+    assert (sm >= 1.0).all()
+    shifted = dict(inp)
+    kr = torch.zeros_like(inp["key_rope"])
+    kr[..., 0] = 1.0
+    qr = torch.zeros_like(inp["q_rope"])
+    qr[..., 0] = 2.0
+    base = dict(inp)
+    base["key_rope"], base["q_rope"] = kr, torch.zeros_like(qr)
+    shifted["key_rope"], shifted["q_rope"] = kr, qr
+    _, m0, s0 = oracle.sfa(base, lse=True)
+    _, m1, s1 = oracle.sfa(shifted, lse=True)
+    np.testing.assert_allclose(m1 - m0, 2.0 * inp["spec"].scale_value, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(s1, s0, rtol=1e-14, atol=0)
