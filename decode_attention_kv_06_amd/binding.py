@@ -67,7 +67,8 @@ class SfaMlaArgs(ctypes.Structure):
         ("max_blocks", I64), ("scale_value", ctypes.c_float), ("sparse_block_size", I64), ("sparse_mode", I64),
         ("attention_mode", I64), ("layout_query", ctypes.c_char_p), ("layout_kv", ctypes.c_char_p),
         ("split_hint", I64), ("profile_event_begin", P), ("profile_event_end", P), ("q_tokens", I64),
-        ("kv_tokens", I64), ("kv_seq", I64)]
+        ("kv_tokens", I64), ("kv_seq", I64), ("softmax_max_out", P), ("softmax_sum_out", P),
+        ("return_softmax_lse", I32)]
 
 
 class IfaError(RuntimeError):
@@ -345,14 +346,23 @@ def ifa_decode_paged(q, key_cache, value_cache, out, block_table, *, workspace=N
 
 def sfa_args(query, query_rope, key, key_rope, value, sparse_indices, block_table, actual_seq_lengths_kv, out, *,
              scale_value, actual_seq_lengths_query=None, sparse_mode=0, sparse_block_size=1,
-             attention_mode=2, layout_query="BSND", layout_kv="PA_BSND", split_hint=0, keep=None):
+             attention_mode=2, layout_query="BSND", layout_kv="PA_BSND", split_hint=0, keep=None,
+             softmax_max_out=None, softmax_sum_out=None):
     """Fill an SfaMlaArgs.  query BSND [B, Q_S, Q_N, D] or TND [Q_T, Q_N, D] (B = the length of
     actual_seq_lengths_query); key PA_BSND [blocks, block_size, 1, D], BSND [B, KV_S, 1, D] or
-    TND [KV_T, 1, D].  Index, table and length tensors are device int32."""
+    TND [KV_T, 1, D].  Index, table and length tensors are device int32.  softmax_max_out /
+    softmax_sum_out (both or neither): fp32 tensors of (query rows) x Q_N elements, which turn on
+    return_softmax_lse."""
+    if (softmax_max_out is None) != (softmax_sum_out is None):
+        raise ValueError("softmax_max_out and softmax_sum_out go together")
+    for t in (softmax_max_out, softmax_sum_out):
+        if t is not None and t.dtype != torch.float32:
+            raise ValueError("softmax_max_out / softmax_sum_out must be torch.float32")
     _check_operands(query, dict(query=query, query_rope=query_rope, key=key, key_rope=key_rope, value=value,
                                 sparse_indices=sparse_indices, block_table=block_table,
                                 actual_seq_lengths_kv=actual_seq_lengths_kv,
-                                actual_seq_lengths_query=actual_seq_lengths_query, attention_out=out),
+                                actual_seq_lengths_query=actual_seq_lengths_query, attention_out=out,
+                                softmax_max_out=softmax_max_out, softmax_sum_out=softmax_sum_out),
                     int32=("sparse_indices", "block_table", "actual_seq_lengths_kv", "actual_seq_lengths_query"))
     if layout_query == "TND":
         QT, QN, D = query.shape
@@ -390,6 +400,9 @@ def sfa_args(query, query_rope, key, key_rope, value, sparse_indices, block_tabl
         keep.extend([lq, lk])
     a.layout_query, a.layout_kv = lq, lk
     a.split_hint = int(split_hint)
+    if softmax_max_out is not None:
+        a.softmax_max_out, a.softmax_sum_out = _ptr(softmax_max_out), _ptr(softmax_sum_out)
+        a.return_softmax_lse = 1
     return a
 
 

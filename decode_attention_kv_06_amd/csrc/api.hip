@@ -26,7 +26,7 @@ namespace {
 
 using namespace ifa;
 
-constexpr int kAbiVersion = 5;
+constexpr int kAbiVersion = 6;
 constexpr int kRowModeTiles = 4;     // longest row (in split-kernel tiles) that row mode takes
 
 bool is_float_dt(int dt) { return dt == IFA_DT_F16 || dt == IFA_DT_BF16; }

@@ -24,7 +24,9 @@ struct SfaParams {
     const int32_t *lq;        // [B]: counts (BSND query) or prefix sums (TND query); nullptr: QS each
     void *out;                // [R, QN, 512]
     void *part_o;             // [R, n_sc, QN, 512], input dtype: each chunk's output normalised by its own sum
-    float *part_ml;           // [R, n_sc, QN, 2]: the chunk's running max (log2 domain) and sum
+    float *part_ml;           // [R, n_sc, QN, 2]: the chunk's score max (log2 domain) and its sum
+                              // of exp2(score - max)
+    float *lse_max, *lse_sum; // [R, QN] softmax_max / softmax_sum (natural log domain), or nullptr
     int64_t sparse_size;
     int64_t kv_seq;           // BSND cache: positions per batch
     int64_t kv_rows;          // rows of the key tensor (bounds every cache row the kernel reads)

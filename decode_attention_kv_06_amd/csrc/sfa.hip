@@ -19,12 +19,14 @@ namespace {
 struct SfaShape {
     int layout_q = 0, layout_kv = 0, sbs_shift = 0;
     int64_t R = 0, q_tokens = 0, kv_tokens = 0, kv_seq = 0, kv_rows = 0;
+    float *lse_max = nullptr, *lse_sum = nullptr;   // return_softmax_lse outputs
 };
 
 int validate(const sfa_mla_args *a, SfaShape &sh) {
     if (!a) return IFA_ERR_PARAM_NULLPTR;
     if (a->struct_size < offsetof(sfa_mla_args, q_tokens)) return IFA_ERR_PARAM_INVALID;
-    const bool breadth = a->struct_size >= sizeof(sfa_mla_args);
+    const bool breadth = a->struct_size >= offsetof(sfa_mla_args, softmax_max_out);
+    const bool lse_fields = a->struct_size >= sizeof(sfa_mla_args);
     sh.q_tokens = breadth ? a->q_tokens : 0;
     sh.kv_tokens = breadth ? a->kv_tokens : 0;
     sh.kv_seq = breadth ? a->kv_seq : 0;
@@ -78,6 +80,17 @@ int validate(const sfa_mla_args *a, SfaShape &sh) {
     if (a->attention_mode != 2) return IFA_ERR_PARAM_INVALID;
     if (!std::isfinite(a->scale_value)) return IFA_ERR_PARAM_INVALID;
     if (a->split_hint < 0 || a->split_hint > 64) return IFA_ERR_PARAM_INVALID;
+    if (lse_fields) {
+        if (a->return_softmax_lse == 1) {
+            // README: softmax_max / softmax_sum are returned only when layout_kv is not PA_BSND
+            if (sh.layout_kv == 0) return IFA_ERR_PARAM_INVALID;
+            if (!a->softmax_max_out || !a->softmax_sum_out) return IFA_ERR_PARAM_NULLPTR;
+            sh.lse_max = a->softmax_max_out;
+            sh.lse_sum = a->softmax_sum_out;
+        } else if (a->return_softmax_lse != 0 || a->softmax_max_out || a->softmax_sum_out) {
+            return IFA_ERR_PARAM_INVALID;
+        }
+    }
     return IFA_OK;
 }
 
@@ -169,6 +182,8 @@ int sfa_run(const sfa_mla_args *a, void *ws, size_t ws_bytes, hipStream_t stream
     p.lkv = a->actual_seq_lengths_kv;
     p.lq = a->actual_seq_lengths_query;
     p.out = a->attention_out;
+    p.lse_max = sh.lse_max;
+    p.lse_sum = sh.lse_sum;
     const size_t rows = (size_t)sh.R * pl.n_sc * a->q_heads;
     p.part_o = ws;
     p.part_ml = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + part_o_bytes(rows));

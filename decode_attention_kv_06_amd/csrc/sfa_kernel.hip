@@ -61,6 +61,7 @@ constexpr int kVIns = 8;                // ... for a value half-tile
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kMaxInit = -1.0e30f;
 constexpr float kLazy = 8.0f;           // raise the running max only past this many log2 units
+constexpr float kLn2 = 0.69314718055994531f;   // log2-domain maxima back to the natural-log domain
 
 static_assert(kT == 8 * kWavesPerBlock, "each wave copies 8 rows of a tile");
 static_assert(2 * 64 * kStgPitch <= kRopeOff + kT * 128, "two waves' output blocks fit one ring slot");
@@ -146,13 +147,17 @@ __device__ __forceinline__ void wait_vmcnt() {
 // max(x, x of lane ^ 16) and max(x, x of lane ^ 32) with the gfx950 row-swap
 // permutes: one swap returns, in every lane, the values of both rows of the
 // pair, so their max (or sum) is the pairwise reduction.  No LDS round trip.
+// The two halves are copied to scalars before the bit casts: a bit cast of a
+// vector element read in place has been compiled as a read of element 0.
 __device__ __forceinline__ float max_xor16(float x) {
     const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x), false, false);
-    return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+    const uint32_t a = r[0], b = r[1];
+    return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
 }
 __device__ __forceinline__ float max_xor32(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x), false, false);
-    return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+    const uint32_t a = r[0], b = r[1];
+    return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
 }
 
 // Workgroup barrier without a memory fence (the copies in flight must stay in
@@ -365,6 +370,7 @@ __global__ __launch_bounds__(256, 1) void sfa_kernel(const SfaParams P) {
 #pragma unroll
         for (int j = 0; j < 8; j++) acc[hg][j] = floatx4{0.f, 0.f, 0.f, 0.f};
     float m_run = kMaxInit, l_run = 0.f;    // head l16 of group `wave` (lanes of one head agree on m_run)
+    float m_true = kNegInf;                 // the largest score itself (m_run is raised lazily, so may lag it)
     const float smul = P.score_mul;
 
     // scores of tile `tile` for head group `wave` from its key slot, the
@@ -422,6 +428,7 @@ __global__ __launch_bounds__(256, 1) void sfa_kernel(const SfaParams P) {
             }
         mt = max_xor16(mt);
         mt = max_xor32(mt);
+        m_true = fmaxf(m_true, mt);
         const bool raise = mt > m_run + kLazy;
         float alpha = 1.f;
         int flag = 0;
@@ -560,7 +567,17 @@ __global__ __launch_bounds__(256, 1) void sfa_kernel(const SfaParams P) {
         l_run += __shfl_xor(l_run, 32);
         if (g == 0) {
             s_linv[wave * 16 + l16] = l_run > 0.f ? 1.f / l_run : 0.f;
-            if (!P.direct && h_ok) *reinterpret_cast<float2 *>(P.part_ml + (prow + h) * 2) = make_float2(m_run, l_run);
+            // the chunk's (max, sum) relative to its largest score, which the
+            // merge and the softmax_max / softmax_sum outputs use
+            const bool any = l_run > 0.f;
+            const float m_out = any ? m_true : m_run;
+            const float l_out = any ? l_run * __builtin_amdgcn_exp2f(m_run - m_true) : 0.f;
+            if (!P.direct && h_ok) *reinterpret_cast<float2 *>(P.part_ml + (prow + h) * 2) = make_float2(m_out, l_out);
+            if (P.direct && h_ok && P.lse_max) {
+                const int64_t o = (int64_t)qr * P.QN + h;
+                P.lse_max[o] = any ? m_out * kLn2 : kNegInf;
+                P.lse_sum[o] = l_out;
+            }
         }
     }
     __syncthreads();
@@ -649,6 +666,11 @@ __global__ __launch_bounds__(256) void sfa_combine_kernel(const SfaParams P) {
         for (int e = 0; e < 8; e++) o[e] += w * elem(xs, e);
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
+    if (P.lse_max && lane == 0) {   // softmax_max / softmax_sum of the row (natural-log domain)
+        const int64_t oi = (int64_t)qr * P.QN + hh;
+        P.lse_max[oi] = L > 0.f ? Mx * kLn2 : kNegInf;
+        P.lse_sum[oi] = L;
+    }
     u32x4v y;
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {

@@ -265,6 +265,18 @@ typedef struct ifa_paged_args {
  *   PA_BSND cache only.
  * split_hint: 0 lets the planner choose the number of index chunks per
  *   query row; a positive value forces it (testing and tuning).
+ * return_softmax_lse (README parameter table: return_softmax_lse,
+ *   softmax_max_out, softmax_sum_out): when 1, the call also writes, per
+ *   query row and head, softmax_max_out = the maximum of the scaled scores
+ *   the softmax takes, and softmax_sum_out = the sum of exp(score - max) over
+ *   the attended positions; -inf and 0 for a row that attends nothing (the
+ *   scores being the softmax's input after scale_value is this library's
+ *   reading).  Shape [B, 1, Q_S, Q_N] for a BSND query, [1, Q_T, Q_N] for a
+ *   TND one: element (query row) * Q_N + head.  Only with a BSND or TND
+ *   cache, as the README allows (IFA_ERR_PARAM_INVALID with PA_BSND); both
+ *   pointers are required then, and must be NULL when return_softmax_lse is
+ *   0.  These are the last fields of the struct (ABI version 6); a shorter
+ *   struct_size means no such outputs.
  */
 typedef struct sfa_mla_args {
     uint32_t struct_size; /* sizeof(sfa_mla_args) */
@@ -288,6 +300,9 @@ typedef struct sfa_mla_args {
     int64_t q_tokens;  /* Q_T of a TND query */
     int64_t kv_tokens; /* KV_T of a TND cache */
     int64_t kv_seq;    /* KV_S of a BSND cache */
+    float *softmax_max_out;     /* return_softmax_lse: device fp32, see above */
+    float *softmax_sum_out;
+    int32_t return_softmax_lse; /* 0 or 1 */
 } sfa_mla_args;
 
 /* Phase 1: validate and return the workspace bytes the run call needs. */

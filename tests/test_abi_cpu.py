@@ -253,8 +253,13 @@ def test_sfa_valid_size_query():
     (dict(layout_kv=b"TND", kv_tokens=0), 161002),
     (dict(layout_kv=b"TND", kv_tokens=10, actual_seq_lengths_kv=None), 161001),
     (dict(layout_kv=b"PA_BNSD"), 161002),
-    (dict(layout_kv=b"BSND", kv_seq=100, struct_size=ctypes.sizeof(bd.SfaMlaArgs) - 24), 161002),
-    (dict(struct_size=ctypes.sizeof(bd.SfaMlaArgs) - 32), 161002),
+    (dict(layout_kv=b"BSND", kv_seq=100, struct_size=bd.SfaMlaArgs.q_tokens.offset), 161002),
+    (dict(struct_size=bd.SfaMlaArgs.q_tokens.offset - 8), 161002),
+    # return_softmax_lse (README: not with a PA_BSND cache; both outputs required; none without the flag)
+    (dict(return_softmax_lse=1, softmax_max_out=FAKE, softmax_sum_out=FAKE), 161002),
+    (dict(layout_kv=b"BSND", kv_seq=100, return_softmax_lse=1, softmax_max_out=FAKE), 161001),
+    (dict(layout_kv=b"BSND", kv_seq=100, softmax_max_out=FAKE, softmax_sum_out=FAKE), 161002),
+    (dict(layout_kv=b"BSND", kv_seq=100, return_softmax_lse=2, softmax_max_out=FAKE, softmax_sum_out=FAKE), 161002),
     (dict(scale_value=float("inf")), 161002),
 ])
 def test_sfa_rejections(kw, code):
@@ -301,7 +306,10 @@ def test_paged_positional_bias_checks():
     dict(layout_kv=b"BSND", kv_seq=100, block_table=None, actual_seq_lengths_kv=None),
     dict(layout_kv=b"TND", kv_tokens=1000, block_table=None),
     dict(layout_query=b"TND", actual_seq_lengths_query=FAKE, q_tokens=7),
-    dict(struct_size=ctypes.sizeof(bd.SfaMlaArgs) - 24),              # a struct without the breadth fields
+    dict(struct_size=bd.SfaMlaArgs.q_tokens.offset),                  # a struct without the breadth fields
+    dict(layout_kv=b"BSND", kv_seq=100, block_table=None, actual_seq_lengths_kv=None, return_softmax_lse=1,
+         softmax_max_out=FAKE, softmax_sum_out=FAKE),                   # softmax max / sum outputs
+    dict(struct_size=bd.SfaMlaArgs.softmax_max_out.offset, softmax_max_out=FAKE),   # fields invisible: ignored
 ])
 def test_sfa_breadth_accepted(kw):
     assert ws_size("sfa_decode_mla_workspace_size", sfa_args(**kw))[0] == 0

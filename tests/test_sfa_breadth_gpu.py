@@ -86,3 +86,44 @@ def test_multi_token_full_size_sampled_rows():
     n = inp["q_rows"] * inp["spec"].QN
     rows = sorted(set([0, 1, n // 2, n - 1] + list(range(5, n, max(1, n // 97)))))
     compare(inp, out, rows=rows)
+
+
+# ------------------------------------------------------- softmax_max / softmax_sum
+def run_lse(inp, split):
+    """Output plus softmax_max / softmax_sum from one call (return_softmax_lse)."""
+    import torch
+    from decode_attention_kv_06_amd import binding, harness
+    from gpu_util import say
+    dev = harness.to_device(inp)
+    out = harness.alloc_out(dev)
+    n = inp["q_rows"] * inp["spec"].QN
+    mx = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
+    sm = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
+    say("GPU step: sfa_decode_mla with return_softmax_lse, %s/%s split=%d" % (
+        inp["spec"].layout_q, inp["spec"].layout_kv, split))
+    binding.sfa_decode_mla(dev["q"], dev["q_rope"], dev["key"], dev["key_rope"], dev["value"],
+                           dev["sparse_indices"], dev["block_table"], dev["actual_seq_lengths_kv"], out,
+                           softmax_max_out=mx, softmax_sum_out=sm, **harness.sfa_options(dev, split))
+    torch.cuda.synchronize()
+    return out, mx.cpu().double().numpy(), sm.cpu().double().numpy()
+
+
+@pytest.mark.parametrize("split", [1, 3])
+@pytest.mark.parametrize("layout_kv", ["BSND", "TND"])
+def test_softmax_max_and_sum(layout_kv, split):
+    import numpy as np
+    import oracle
+    kw = dict(layout_kv=layout_kv, lkv=[700, 1200, 64], QS=2, lq=[2, 1, 2], sparse_mode=3, QN=32,
+              sparse_size=600, cfg_id=550)
+    if layout_kv == "BSND":
+        kw["kv_seq"] = 1200
+    inp = make_sfa(small(**kw))
+    out, mx, sm = run_lse(inp, split)
+    compare(inp, out)                                     # the output is the same call's
+    _, rmx, rsm = oracle.sfa(inp, lse=True)
+    rmx, rsm = rmx.reshape(-1), rsm.reshape(-1)
+    empty = rsm == 0
+    assert empty.any() and (~empty).any()                 # batch 1's second query row attends nothing
+    assert (mx[empty] == -np.inf).all() and (sm[empty] == 0).all()
+    np.testing.assert_allclose(mx[~empty], rmx[~empty], rtol=0, atol=1e-3)
+    np.testing.assert_allclose(sm[~empty], rsm[~empty], rtol=2e-3, atol=0)
