@@ -127,3 +127,37 @@ def test_softmax_max_and_sum(layout_kv, split):
     assert (mx[empty] == -np.inf).all() and (sm[empty] == 0).all()
     np.testing.assert_allclose(mx[~empty], rmx[~empty], rtol=0, atol=1e-3)
     np.testing.assert_allclose(sm[~empty], rsm[~empty], rtol=2e-3, atol=0)
+
+
+@pytest.mark.parametrize("split", [1, 3])
+@pytest.mark.parametrize("layout_kv", ["PA_BSND", "BSND"])
+def test_peaked_scores(layout_kv, split):
+    """Scores spread over hundreds of log2 units, so that a running max taken
+    from part of a tile (or raised late) overflows exp2 and poisons the row.
+    The softmax is then nearly one-hot, and a row's largest score sits in any
+    of the four lane groups of its head."""
+    import numpy as np
+    import oracle
+    kw = dict(layout_kv=layout_kv, QS=2, lq=[2, 2, 1], sparse_mode=3, sparse_size=500, scale=4.0, cfg_id=560)
+    if layout_kv == "BSND":
+        kw.update(lkv=[900, 1500, 300], kv_seq=1500)
+    inp = make_sfa(small(**kw))
+    if layout_kv == "PA_BSND":
+        out, _ = run_gpu(inp, split=split)
+        assert torch_isfinite(out)
+        compare(inp, out)
+        return
+    out, mx, sm = run_lse(inp, split)
+    assert torch_isfinite(out)
+    compare(inp, out)
+    _, rmx, rsm = oracle.sfa(inp, lse=True)
+    rmx, rsm = rmx.reshape(-1), rsm.reshape(-1)
+    live = rsm > 0
+    assert np.abs(rmx[live]).max() > 100                  # the scores really are that spread
+    np.testing.assert_allclose(mx[live], rmx[live], rtol=1e-5, atol=1e-3)
+    np.testing.assert_allclose(sm[live], rsm[live], rtol=2e-3, atol=0)
+
+
+def torch_isfinite(t):
+    import torch
+    return bool(torch.isfinite(t.float()).all())
