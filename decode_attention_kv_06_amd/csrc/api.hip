@@ -105,16 +105,17 @@ int finish_plan(IfaPlan &p, int64_t split_tokens) {
     p.slices.clear();
     p.total_slots = 0;
     // Row mode: when every row is at most a few tiles long and the rows fit in
-    // the resident waves, one wave per row finishes the call in one launch
-    // (the split kernel writes the output); splitting rows further would buy
-    // less streaming time than the combine launch costs.  16-bit caches and
-    // outputs only (the int8 epilogues live in the combine).
+    // the resident waves, one workgroup per row finishes the call in one
+    // launch: its four waves take a quarter of the window each (one tile at
+    // most), merge their states in LDS and write the output.  A second launch
+    // for the combine would cost more than the whole stream.  16-bit caches
+    // and outputs only (the int8 epilogues live in the combine).
     p.row_mode = false;
     if (split_tokens <= 0 && p.kv != KV_I8 && !p.out_i8 && p.B <= kSliceBatches) {
         const int64_t tile = (int64_t)(p.G >= 8 ? 4 : 8) * (512 / p.D);   // positions per split-kernel tile
         int32_t max_len = 0;
         for (const Window &w : p.win) max_len = std::max(max_len, w.hi - w.lo);
-        p.row_mode = max_len <= kRowModeTiles * tile && (int64_t)p.B * rows_per_batch <= waves;
+        p.row_mode = max_len <= kRowModeTiles * tile && (int64_t)p.B * rows_per_batch * kWavesPerBlock <= waves;
     }
     if (p.row_mode) {
         SlicePlan sp;
@@ -132,7 +133,7 @@ int finish_plan(IfaPlan &p, int64_t split_tokens) {
         sp.pre[sp.nb] = pos;
         sp.total = pos;
         sp.piece = max_len;
-        sp.n_pieces = (int)(sp.nb * rows_per_batch);
+        sp.n_pieces = (int)(sp.nb * rows_per_batch * kWavesPerBlock);   // one workgroup per row
         p.slices.push_back(std::move(sp));
         p.workspace = 0;
         return IFA_OK;

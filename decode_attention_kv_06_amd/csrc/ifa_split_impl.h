@@ -237,23 +237,28 @@ void split_kernel(const SplitParams P) {
 
     // This wave's piece of the flattened (batch, KV head, head group,
     // position) space; it is cut into segments at row boundaries, and every
-    // segment leaves one partial softmax state.  In row mode the piece is
-    // row wave_id of the slice, whole.
+    // segment leaves one partial softmax state.  In row mode workgroup
+    // blockIdx.x takes row blockIdx.x of the slice, its waves a quarter of the
+    // window each.
     int64_t f0 = (int64_t)wave_id * P.piece;
     int64_t f1 = min(P.total, f0 + P.piece);
+    __shared__ float2 s_ml[kWavesPerBlock][G];   // row mode: each wave's (m, l) per head
     if constexpr (!I8) {
         if (P.row_mode) {
             const int rpb = P.Nkv * P.n_hg;
-            const int bl = wave_id / rpb, rj = wave_id - bl * rpb;
+            const int row = blockIdx.x;
+            const int bl = row / rpb, rj = row - bl * rpb;
             const int len = P.len[bl];
-            f0 = P.pre[bl] + (int64_t)rj * len;
-            f1 = f0 + len;
-            if (len == 0) {     // an empty window: zero rows
+            const int quarter = (len + kWavesPerBlock - 1) / kWavesPerBlock;
+            const int64_t r0 = P.pre[bl] + (int64_t)rj * len;
+            f0 = r0 + min(len, wave * quarter);
+            f1 = r0 + min(len, (wave + 1) * quarter);
+            if (len == 0) {     // an empty window: zero rows (the whole workgroup returns)
                 const int j = rj / P.n_hg, hg = rj - j * P.n_hg;
                 using T = std::conditional_t<KV == KV_BF16, __bf16, _Float16>;
                 T *o = reinterpret_cast<T *>(P.out) + ((P.b0 + bl) * P.N + j * P.g + hg * G) * (int64_t)D;
                 const int nh = min(G, P.g - hg * G);
-                for (int i = lane; i < nh * D; i += 64) o[i] = (T)0.f;
+                for (int i = threadIdx.x; i < nh * D; i += 64 * kWavesPerBlock) o[i] = (T)0.f;
                 return;
             }
         }
@@ -888,17 +893,15 @@ void split_kernel(const SplitParams P) {
         }
 
         if constexpr (!I8) {
-            if (P.row_mode) {   // the row is whole: normalise, round to nearest even, write out
+            if (P.row_mode) {   // the wave's quarter of the row goes to LDS for the merge below
                 if (r == 0) {
-                    using T = std::conditional_t<KV == KV_BF16, __bf16, _Float16>;
-                    typedef T t8 __attribute__((ext_vector_type(8)));
+                    extern __shared__ __attribute__((aligned(16))) float s_part[];   // [wave][G][D]
 #pragma unroll
                     for (int hh = 0; hh < G; hh++) {
-                        if (hg * G + hh >= P.g) break;
-                        t8 o;
-#pragma unroll
-                        for (int e = 0; e < 8; e++) o[e] = (T)(l[hh] > 0.f ? acc[hh][e] / l[hh] : 0.f);
-                        *reinterpret_cast<t8 *>(reinterpret_cast<T *>(P.out) + (b * P.N + hbase + hh) * D + 8 * c) = o;
+                        float4 *dst = reinterpret_cast<float4 *>(s_part + (wave * G + hh) * D + 8 * c);
+                        dst[0] = make_float4(acc[hh][0], acc[hh][1], acc[hh][2], acc[hh][3]);
+                        dst[1] = make_float4(acc[hh][4], acc[hh][5], acc[hh][6], acc[hh][7]);
+                        if (c == 0) s_ml[wave][hh] = make_float2(m[hh], l[hh]);
                     }
                 }
                 f += nseg;
@@ -918,6 +921,49 @@ void split_kernel(const SplitParams P) {
         }
         f += nseg;
     }   // segments
+
+    if constexpr (!I8) {
+        if (P.row_mode) {
+            // Merge the four quarters of the row in a fixed order (a wave with
+            // an empty quarter contributes nothing), normalise, round to
+            // nearest even and write the output.
+            extern __shared__ __attribute__((aligned(16))) float s_part[];   // [wave][G][D]
+            if (f0 == f1) {
+                for (int i = lane; i < G * D; i += 64) s_part[wave * G * D + i] = 0.f;
+                if (lane < G) s_ml[wave][lane] = make_float2(kMaxInit, 0.f);
+            }
+            __syncthreads();
+            const int rpb = P.Nkv * P.n_hg;
+            const int row = blockIdx.x;
+            const int bl = row / rpb, rj = row - bl * rpb;
+            const int j = rj / P.n_hg, hg = rj - j * P.n_hg;
+            const int nh = min(G, P.g - hg * G);
+            using T = std::conditional_t<KV == KV_BF16, __bf16, _Float16>;
+            typedef T t8 __attribute__((ext_vector_type(8)));
+            T *o = reinterpret_cast<T *>(P.out) + ((P.b0 + bl) * P.N + j * P.g + hg * G) * (int64_t)D;
+            for (int it = threadIdx.x; it < nh * (D / 8); it += 64 * kWavesPerBlock) {
+                const int hh = it / (D / 8), c8 = it - hh * (D / 8);
+                float mx = kMaxInit;
+#pragma unroll
+                for (int w = 0; w < kWavesPerBlock; w++) mx = fmaxf(mx, s_ml[w][hh].x);
+                float L = 0.f, a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int w = 0; w < kWavesPerBlock; w++) {
+                    const float2 ml = s_ml[w][hh];
+                    const float wt = __builtin_amdgcn_exp2f(ml.x - mx);
+                    L += ml.y * wt;
+                    const float4 *src = reinterpret_cast<const float4 *>(s_part + (w * G + hh) * D + 8 * c8);
+                    const float4 x0 = src[0], x1 = src[1];
+                    a[0] += x0.x * wt; a[1] += x0.y * wt; a[2] += x0.z * wt; a[3] += x0.w * wt;
+                    a[4] += x1.x * wt; a[5] += x1.y * wt; a[6] += x1.z * wt; a[7] += x1.w * wt;
+                }
+                t8 v;
+#pragma unroll
+                for (int e = 0; e < 8; e++) v[e] = (T)(L > 0.f ? a[e] / L : 0.f);
+                *reinterpret_cast<t8 *>(o + hh * D + 8 * c8) = v;
+            }
+        }
+    }
 }
 
 // int8 cache, D = 128, head groups of 8, dense, no mask or bias: the
@@ -1232,10 +1278,13 @@ const void *ptr_pm(bool paged, int extra) {
 template <int KV, int D, int G, bool PAGED, int EXTRA>
 hipError_t launch_one(const SplitParams &p, hipStream_t s) {
     const int blocks = (p.n_pieces + kWavesPerBlock - 1) / kWavesPerBlock;
-    if constexpr (KV == KV_I8 && D == 128 && G == 8 && !PAGED && EXTRA == EX_NONE)
+    if constexpr (KV == KV_I8 && D == 128 && G == 8 && !PAGED && EXTRA == EX_NONE) {
         hipLaunchKernelGGL(split_kernel_i8m<KV_I8>, dim3(blocks), dim3(64 * kWavesPerBlock), 0, s, p);
-    else
-        hipLaunchKernelGGL((split_kernel<KV, D, G, PAGED, EXTRA>), dim3(blocks), dim3(64 * kWavesPerBlock), 0, s, p);
+    } else {
+        // row mode: every wave's partial state of the row, merged in LDS
+        const size_t lds = p.row_mode ? (size_t)kWavesPerBlock * G * D * sizeof(float) : 0;
+        hipLaunchKernelGGL((split_kernel<KV, D, G, PAGED, EXTRA>), dim3(blocks), dim3(64 * kWavesPerBlock), lds, s, p);
+    }
     return hipGetLastError();
 }
 

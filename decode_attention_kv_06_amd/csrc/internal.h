@@ -25,8 +25,10 @@ enum SplitExtra { EX_NONE = 0, EX_MASK = 1, EX_PSE = 2 };
 // boundaries.  Each segment writes one partial softmax state (G heads) to
 // slot sbase[b] + (j*n_hg + hg)*maxseg[b] + (w - first piece of the row);
 // the combine kernel recomputes the same slots from the same tables.
-// Small problems (every row a few tiles long) run in row mode instead: wave
-// w takes row w whole and writes its output, so one launch does the call.
+// Small problems (every row a few tiles long) run in row mode instead:
+// workgroup w takes row w, each of its waves a quarter of the window; the
+// waves merge their states in LDS and write the output, so one launch does
+// the call.
 struct SplitParams {
     const void *q;          // [B, N, D] (any query layout, S = 1)
     const void *k;          // cache base
@@ -55,7 +57,7 @@ struct SplitParams {
     int32_t aq_mode;        // int8: 1 per-tensor, 2 per-channel
     int32_t q_bf16;         // int8 kernels: query dtype is bf16
     int32_t list_bnsd;      // per-batch BNSD caches: the head stride is list_seq[b] * sS
-    int32_t row_mode;       // one wave per (b, j, hg) row, normalised and written out by that wave
+    int32_t row_mode;       // one workgroup per (b, j, hg) row, merged, normalised and written out by it
                             // (16-bit caches and outputs); no partial states, no combine
     float score_mul;        // scale * log2(e)
     int32_t nb;             // batches in this slice

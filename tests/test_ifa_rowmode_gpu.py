@@ -1,5 +1,6 @@
-"""Row mode: small decodes run as one launch, one wave per (batch, KV head,
-head group) row, the split kernel writing the normalised output itself.
+"""Row mode: small decodes run as one launch, one workgroup per (batch, KV
+head, head group) row, whose four waves each take a quarter of the window and
+merge their states in LDS before writing the normalised output.
 
 The planner takes it when every window is at most four tiles long and the
 rows fit in the resident waves, for 16-bit caches and outputs; the call then
@@ -73,6 +74,27 @@ def test_masks_biases_and_paged_caches(extra, paged):
     assert (o[1] == 0).all()                   # the empty window
     if inp["mask"] is not None:
         assert (o[2, 5] == 0).all()
+    compare(inp, out)
+
+
+def group(g):
+    G = 1
+    while G < g and G < 8:
+        G *= 2
+    return G
+
+
+@pytest.mark.parametrize("N,Nkv,D", [(4, 4, 128), (8, 4, 256), (16, 2, 512), (24, 2, 64), (12, 1, 128)])
+def test_head_group_sizes(N, Nkv, D):
+    # groups of 1, 2, 8 (the largest LDS merge: 4 waves x 8 heads x 512 floats), and 12 or
+    # 24 heads per KV head split into padded groups of 8
+    G = group(N // Nkv)
+    S = 4 * tile(D, G)
+    spec = IfaSpec("rowmode_g", 630 + N + D, "bf16", "bf16", B=3, N=N, Nkv=Nkv, D=D, layout="BSND", S=S,
+                   lengths=[S, 1, 4 * tile(D, G) // 3 + 5])
+    inp = make_ifa(spec)
+    out, n = run_mode(inp)
+    assert n == 0
     compare(inp, out)
 
 
