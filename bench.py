@@ -402,6 +402,33 @@ class Gpu:
                 "what": "ifa_read_probe: 16 B per lane nontemporal loads, 8 in flight per lane, one workgroup of 4 waves per CU"}
 
 
+def graph_replay_us(fn, a, a_ref, ws_ptr, ws_len, calls: int = 50, replays: int = 5) -> float:
+    """Device time per call of `calls` back-to-back calls captured in one HIP
+    graph and replayed (warm): what a captured serving loop pays per call,
+    without the per-call host path of an eager launch.  Small calls only."""
+    import torch
+    from decode_attention_kv_06_amd import binding
+    a.profile_event_begin = a.profile_event_end = None
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        for _ in range(calls):
+            rc = fn(a_ref, ws_ptr, ws_len, sp)
+            if rc != 0:
+                raise binding.IfaError(rc, "captured call")
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (calls * replays)
+    del g
+    return round(us, 2)
+
+
 def measure(gpu: Gpu, name: str, args, ceiling_gbs=None) -> tuple:
     """Run one workload through the protocol; returns (record, host inputs)."""
     import torch
@@ -433,6 +460,7 @@ def measure(gpu: Gpu, name: str, args, ceiling_gbs=None) -> tuple:
     log("timing %s (%d flushed + %d warm calls)" % (name, steps, steps))
     r = gpu.timed(one_call, steps, args.warmup, args.warmup_ms)
     torch.cuda.synchronize()
+    graph_us = graph_replay_us(fn, a, a_ref, ws_ptr, ws_len) if r["warm_us"] < 100.0 else None
     med_s = r["call"]["median"] * 1e-6
     kern_mean_s = r["kernel"]["mean"] * 1e-6
     gbs = alg["total"] / med_s / 1e9
@@ -450,6 +478,7 @@ def measure(gpu: Gpu, name: str, args, ceiling_gbs=None) -> tuple:
         "warm_back_to_back_us_per_call": r["warm_us"],
         "warm_gbs": round(alg["total"] / (r["warm_us"] * 1e-6) / 1e9, 1),
         "host_wall_us_per_call": r["host_us"],
+        "graph_replay_us_per_call": graph_us,
         "timed_calls": steps,
         "warmup_calls_run": r["warmup_calls"],
         "roofline": {"bound": "hbm", "kernel": "sfa_kernel (sparse gather)" if sparse else "split_kernel (split-KV)",

@@ -5,7 +5,7 @@ import pytest
 import torch
 
 from decode_attention_kv_06_amd import harness
-from decode_attention_kv_06_amd.workloads import IfaSpec, make_ifa, make_sfa, small_variant
+from decode_attention_kv_06_amd.workloads import IfaSpec, make_ifa, make_sfa, small_variant, workloads
 from gpu_util import say
 
 pytestmark = pytest.mark.gpu
@@ -18,6 +18,7 @@ CASES = {
                                               S=700, len_range=(1, 700), pse=True, out_int8="per_channel",
                                               qs_range=(5.0, 25.0))),
     "sparse": lambda: make_sfa(small_variant("sfa_mla_bf16")),
+    "tiny_row_mode": lambda: make_ifa(workloads()["tiny_dense_f16"]),
 }
 
 
