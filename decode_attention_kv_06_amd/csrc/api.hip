@@ -46,6 +46,7 @@ struct Window { int32_t lo, hi; };
 struct SlicePlan {
     int b0 = 0, nb = 0;
     int64_t total = 0, piece = 0;
+    int32_t seg_cost = 0;
     int n_pieces = 0;
     std::vector<int64_t> pre;         // nb + 1 entries
     std::vector<int32_t> sbase, maxseg;
@@ -152,9 +153,16 @@ int finish_plan(IfaPlan &p, int64_t split_tokens) {
         }
         sp.pre[sp.nb] = pos;
         sp.total = pos;
+        // Each row start is charged about a tile and a half of positions: a
+        // wave whose piece starts a new row (a new query, first tiles, a
+        // partial state written) measured about that much longer.  With an
+        // explicit work-item size a piece is exactly that many positions.
+        const int64_t tile = (int64_t)(p.G >= 8 ? 4 : 8) * (512 / p.D);
+        sp.seg_cost = split_tokens > 0 ? 0 : (int32_t)(3 * tile / 2);
+        const int64_t total_cost = pos + (int64_t)sp.seg_cost * rows_per_batch * sp.nb;
         if (split_tokens > 0) sp.piece = split_tokens;
-        else sp.piece = std::max<int64_t>(64, (pos + waves - 1) / std::max(1, waves));
-        sp.n_pieces = (int)((pos + sp.piece - 1) / sp.piece);
+        else sp.piece = std::max<int64_t>(64, (total_cost + waves - 1) / std::max(1, waves));
+        sp.n_pieces = (int)((total_cost + sp.piece - 1) / sp.piece);
         int64_t slots = 0;
         for (int i = 0; i < sp.nb; i++) {
             const int64_t len = p.win[b0 + i].hi - p.win[b0 + i].lo;
@@ -162,7 +170,7 @@ int finish_plan(IfaPlan &p, int64_t split_tokens) {
             sp.sbase[i] = (int32_t)slots;
             slots += rows_per_batch * sp.maxseg[i];
         }
-        if (slots > INT32_MAX || pos / sp.piece > INT32_MAX) return IFA_ERR_PARAM_INVALID;
+        if (slots > INT32_MAX || total_cost / sp.piece > INT32_MAX) return IFA_ERR_PARAM_INVALID;
         sp.slot_base = p.total_slots;
         sp.slots = slots;
         p.total_slots += slots;
@@ -471,6 +479,7 @@ int run(const IfaPlan &p, const Launch &L, void *ws, size_t ws_bytes, hipStream_
         sp.b0 = cp.b0 = s.b0;
         sp.total = s.total;
         sp.piece = cp.piece = s.piece;
+        sp.seg_cost = cp.seg_cost = s.seg_cost;
         sp.n_pieces = s.n_pieces;
         for (int i = 0; i < s.nb; i++) {
             sp.pre[i] = cp.pre[i] = s.pre[i];

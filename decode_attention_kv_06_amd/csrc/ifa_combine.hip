@@ -64,7 +64,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineParams P) {
     int nch = 0;
     int64_t slot0 = 0;
     if (len > 0) {
-        const int64_t start = P.pre[bl] + (int64_t)rj * len;
+        const int64_t start = row_cost(P, bl, rj);        // the row's first cost unit
         nch = (int)((start + len - 1) / P.piece - start / P.piece + 1);
         slot0 = P.sbase[bl] + (int64_t)rj * P.maxseg[bl];
     }

@@ -207,6 +207,32 @@ struct SegDesc {
     int64_t slot;
 };
 
+// The position at cost c of the work sequence (a cost inside a row-start
+// charge maps to the start of that row).  Wave-uniform: the batch is found
+// with ballots over the slice's batches.
+__device__ __forceinline__ int64_t cost_to_pos(const SplitParams &P, int64_t c, int lane) {
+    const int64_t gap = (int64_t)P.seg_cost * P.Nkv * P.n_hg;   // row-start charges of one batch
+    int cnt = 0;
+    for (int e0 = 0; e0 < P.nb; e0 += 64) {
+        const int e = e0 + lane;
+        cnt += __popcll(__ballot(e < P.nb && P.pre[e] + gap * e <= c));
+    }
+    const int bl = __builtin_amdgcn_readfirstlane(cnt - 1);
+    const int64_t within = c - (P.pre[bl] + gap * bl);
+    const int64_t L = P.len[bl], per = L + P.seg_cost;
+    if (per == 0) return P.pre[bl];
+    const int64_t rj = within / per, t = within - rj * per;
+    return P.pre[bl] + (t < L ? rj * L + t : (rj + 1) * L);
+}
+
+// Position range [f0, f1) of piece w.
+__device__ __forceinline__ void piece_range(const SplitParams &P, int w, int lane, int64_t &f0, int64_t &f1) {
+    const int64_t total_cost = P.total + (int64_t)P.seg_cost * P.Nkv * P.n_hg * P.nb;
+    const int64_t c0 = (int64_t)w * P.piece, c1 = c0 + P.piece;
+    f0 = c0 >= total_cost ? P.total : cost_to_pos(P, c0, lane);
+    f1 = c1 >= total_cost ? P.total : cost_to_pos(P, c1, lane);
+}
+
 // EXTRA selects the optional score terms compiled in: EX_NONE, EX_MASK
 // (attenMask), or EX_PSE (pseShift, with attenMask checked at run time).
 template <int KV, int D, int G, bool PAGED, int EXTRA>
@@ -240,8 +266,8 @@ void split_kernel(const SplitParams P) {
     // segment leaves one partial softmax state.  In row mode workgroup
     // blockIdx.x takes row blockIdx.x of the slice, its waves a quarter of the
     // window each.
-    int64_t f0 = (int64_t)wave_id * P.piece;
-    int64_t f1 = min(P.total, f0 + P.piece);
+    int64_t f0 = 0, f1 = 0;
+    piece_range(P, wave_id, lane, f0, f1);
     __shared__ float2 s_ml[kWavesPerBlock][G];   // row mode: each wave's (m, l) per head
     if constexpr (!I8) {
         if (P.row_mode) {
@@ -280,8 +306,7 @@ void split_kernel(const SplitParams P) {
         const int t0 = (int)(within - (int64_t)d.rj * len);
         d.nseg = (int)min((int64_t)(len - t0), f1 - f);
         d.lo = P.lo[d.bl] + t0;
-        const int64_t row_start = P.pre[d.bl] + (int64_t)d.rj * len;
-        d.slot = P.sbase[d.bl] + (int64_t)d.rj * P.maxseg[d.bl] + (wave_id - row_start / P.piece);
+        d.slot = P.sbase[d.bl] + (int64_t)d.rj * P.maxseg[d.bl] + (wave_id - row_cost(P, d.bl, d.rj) / P.piece);
         return d;
     };
     // 16-bit query of the head group (register hh holds head hh ^ hl on the
@@ -1003,8 +1028,9 @@ void split_kernel_i8m(const SplitParams P) {
     const char *kb = reinterpret_cast<const char *>(P.k);
     const char *vb = reinterpret_cast<const char *>(P.v);
 
-    const int64_t f1 = min(P.total, (int64_t)(wave_id + 1) * P.piece);
-    for (int64_t f = (int64_t)wave_id * P.piece; f < f1;) {
+    int64_t f0 = 0, f1 = 0;
+    piece_range(P, wave_id, lane, f0, f1);
+    for (int64_t f = f0; f < f1;) {
         int cnt = 0;
         for (int e0 = 0; e0 < P.nb; e0 += 64) {
             const int e = e0 + lane;
@@ -1020,8 +1046,7 @@ void split_kernel_i8m(const SplitParams P) {
         const int lo = P.lo[bl] + t0;
         const int hi = lo + nseg;
         const int64_t b = P.b0 + bl;
-        const int64_t row_start = P.pre[bl] + (int64_t)rj * len;
-        const int64_t slot = P.sbase[bl] + (int64_t)rj * P.maxseg[bl] + (wave_id - row_start / P.piece);
+        const int64_t slot = P.sbase[bl] + (int64_t)rj * P.maxseg[bl] + (wave_id - row_cost(P, bl, rj) / P.piece);
         const int hbase = j * P.g + hg * G;
 
         // ------------------------------------------------ query (matrix A operand)

@@ -19,11 +19,13 @@ enum SplitExtra { EX_NONE = 0, EX_MASK = 1, EX_PSE = 2 };
 
 // Arguments of the split-KV decode kernel.
 //
-// Work is balanced exactly: the rows (b, kv head j, head group hg), each of
-// the batch's window length, are laid end to end, and wave w takes positions
-// [w*piece, (w+1)*piece) of that sequence, cut into segments at row
-// boundaries.  Each segment writes one partial softmax state (G heads) to
-// slot sbase[b] + (j*n_hg + hg)*maxseg[b] + (w - first piece of the row);
+// Work is balanced in cost units: the rows (b, kv head j, head group hg),
+// each of the batch's window length, are laid end to end, every row followed
+// by seg_cost units that stand for the cost of starting a row, and wave w
+// takes the positions whose costs fall in [w*piece, (w+1)*piece), cut into
+// segments at row boundaries (a wave that meets a row start gets that many
+// positions fewer).  Each segment writes one partial softmax state (G heads)
+// to slot sbase[b] + (j*n_hg + hg)*maxseg[b] + (w - first piece of the row);
 // the combine kernel recomputes the same slots from the same tables.
 // Small problems (every row a few tiles long) run in row mode instead:
 // workgroup w takes row w, each of its waves a quarter of the window; the
@@ -47,7 +49,8 @@ struct SplitParams {
     int64_t mask_sB, mask_sH;                      // mask strides (0 = broadcast)
     int64_t pse_sB, pse_sH;                        // pseShift strides (pse_sB 0 = broadcast)
     int64_t total;          // positions over all rows of the slice
-    int64_t piece;          // positions per wave
+    int64_t piece;          // cost units per wave
+    int32_t seg_cost;       // cost units charged per row start (0: a piece is `piece` positions)
     int32_t n_pieces;
     int32_t N, Nkv, g, n_hg;
     int32_t max_blocks, block_size, num_blocks;
@@ -78,6 +81,7 @@ struct CombineParams {
     const void *v_scale;    // int8: antiquant (scale, offset) of V, q dtype
     const void *v_offset;
     int64_t piece;
+    int32_t seg_cost;
     int32_t N, Nkv, g, G, n_hg, D;
     int32_t out_bf16;
     int32_t aq_mode;
@@ -91,6 +95,13 @@ struct CombineParams {
     int32_t sbase[kSliceBatches];
     int32_t maxseg[kSliceBatches];
 };
+
+// Cost coordinate of the first position of row rj of slice batch bl (the
+// rows before it each add seg_cost to their positions).
+template <class PP>
+__device__ __forceinline__ int64_t row_cost(const PP &P, int bl, int rj) {
+    return P.pre[bl] + (int64_t)rj * P.len[bl] + (int64_t)P.seg_cost * ((int64_t)P.Nkv * P.n_hg * bl + rj);
+}
 
 hipError_t launch_split(const SplitParams &p, int kv, int D, int G, bool paged, int extra, hipStream_t s);
 hipError_t launch_combine(const CombineParams &p, hipStream_t s);
