@@ -284,6 +284,30 @@ def test_large_batch_runs_in_slices():
     compare(inp, out)
 
 
+@pytest.mark.parametrize("kv", ["bf16", "i8"])
+def test_rows_shorter_than_the_row_start_charge(kv):
+    """The planner cuts pieces in cost units that charge each row start about a
+    tile and a half of positions.  With many rows of 1-20 positions most of
+    the cost is charges, so many pieces hold no position at all, and one long
+    row keeps the call off row mode; the combine must still find every
+    row's pieces."""
+    B = 100
+    lengths = [3000] + [int(x) for x in np.random.default_rng(77).integers(1, 21, B - 1)]
+    lengths[5] = 0
+    kw = dict(antiquant="per_channel", q_dtype="f16") if kv == "i8" else {}
+    spec = IfaSpec("short_rows", 330, kw.pop("q_dtype", "bf16"), kv, B=B, N=8 if kv == "bf16" else 64,
+                   Nkv=8, D=128, layout="BNSD", S=3000, lengths=lengths, **kw)
+    inp = make_ifa(spec)
+    dev = harness.to_device(inp)
+    out = harness.alloc_out(dev)
+    out.fill_(float("nan"))
+    say("GPU step: short rows under the cost split, kv=%s" % kv)
+    n = harness.call(dev, out)
+    torch.cuda.synchronize()
+    assert n > 0                                   # the split path, not row mode
+    compare(inp, out)
+
+
 def test_explicit_stream_and_reused_workspace():
     inp = make_ifa(small_variant("dense_gqa_bf16_bsh"))
     dev = harness.to_device(inp)
