@@ -53,8 +53,12 @@ struct SlicePlan {
     int64_t slot_base = 0, slots = 0;
 };
 
+// The head dim a call runs on: the smallest compiled size that holds D.
+int compiled_head_dim(int D) { return D <= 64 ? 64 : D <= 128 ? 128 : D <= 256 ? 256 : 512; }
+
 struct IfaPlan {
     int kv = 0, D = 0, G = 0, n_hg = 0, g = 0, N = 0, Nkv = 0, B = 0;
+    int Dc = 0;                          // compiled head dim: the smallest of 64/128/256/512 >= D
     bool paged = false;
     bool out_i8 = false;                 // int8 output (finished by the combine)
     bool row_mode = false;               // one wave per row, finished in place, no combine
@@ -92,7 +96,7 @@ int finish_plan(IfaPlan &p, int64_t split_tokens) {
     p.n_hg = (p.g + p.G - 1) / p.G;
     int waves = 0;
     if (split_tokens <= 0) {
-        waves = resident_waves(p.kv, p.D, p.G, p.paged, p.extra);
+        waves = resident_waves(p.kv, p.Dc, p.G, p.paged, p.extra);
         if (waves <= 0) return IFA_ERR_RUNTIME;
         // A plain dense stream with head groups of 2 or 4 (8-row tiles, 16 KB of
         // K/V in flight per wave) reads HBM faster with half the resident waves,
@@ -113,7 +117,7 @@ int finish_plan(IfaPlan &p, int64_t split_tokens) {
     // and outputs only (the int8 epilogues live in the combine).
     p.row_mode = false;
     if (split_tokens <= 0 && p.kv != KV_I8 && !p.out_i8 && p.B <= kSliceBatches) {
-        const int64_t tile = (int64_t)(p.G >= 8 ? 4 : 8) * (512 / p.D);   // positions per split-kernel tile
+        const int64_t tile = (int64_t)(p.G >= 8 ? 4 : 8) * (512 / p.Dc);   // positions per split-kernel tile
         int32_t max_len = 0;
         for (const Window &w : p.win) max_len = std::max(max_len, w.hi - w.lo);
         p.row_mode = max_len <= kRowModeTiles * tile && (int64_t)p.B * rows_per_batch * kWavesPerBlock <= waves;
@@ -157,7 +161,7 @@ int finish_plan(IfaPlan &p, int64_t split_tokens) {
         // wave whose piece starts a new row (a new query, first tiles, a
         // partial state written) measured about that much longer.  With an
         // explicit work-item size a piece is exactly that many positions.
-        const int64_t tile = (int64_t)(p.G >= 8 ? 4 : 8) * (512 / p.D);
+        const int64_t tile = (int64_t)(p.G >= 8 ? 4 : 8) * (512 / p.Dc);
         sp.seg_cost = split_tokens > 0 ? 0 : (int32_t)(3 * tile / 2);
         const int64_t total_cost = pos + (int64_t)sp.seg_cost * rows_per_batch * sp.nb;
         if (split_tokens > 0) sp.piece = split_tokens;
@@ -176,7 +180,7 @@ int finish_plan(IfaPlan &p, int64_t split_tokens) {
         p.total_slots += slots;
         p.slices.push_back(std::move(sp));
     }
-    const size_t acc = (size_t)p.total_slots * p.G * p.D * sizeof(float);
+    const size_t acc = (size_t)p.total_slots * p.G * p.Dc * sizeof(float);
     const size_t ml = (size_t)p.total_slots * p.G * 2 * sizeof(float);
     p.workspace = (acc + 255) / 256 * 256 + (ml + 255) / 256 * 256;
     if (getenv("IFA_DEBUG_PLAN")) {
@@ -222,7 +226,9 @@ int check_common(const void *q, const void *out, int dq, int dkv, int dout, cons
     if (Nkv_in < 0 || Nkv_in > N) return IFA_ERR_PARAM_INVALID;
     c->Nkv = Nkv_in == 0 ? N : Nkv_in;
     if (N % c->Nkv) return IFA_ERR_PARAM_INVALID;
-    if (D != 64 && D != 128 && D != 256 && D != 512) return IFA_ERR_PARAM_INVALID;
+    // any head dim up to 512 that keeps rows in whole 16-byte lanes; the
+    // kernels run it on the next compiled size (64, 128, 256, 512)
+    if (D < 8 || D > 512 || D % 8) return IFA_ERR_PARAM_INVALID;
     if (!std::isfinite(scale)) return IFA_ERR_PARAM_INVALID;
     if (mask) {
         if (dmask != IFA_DT_BOOL && dmask != IFA_DT_I8 && dmask != IFA_DT_U8) return IFA_ERR_PARAM_INVALID;
@@ -298,6 +304,7 @@ int plan_dense(const ifa_decode_args *a, IfaPlan &p, IfaCommon &c) {
     p.Nkv = (int)c.Nkv;
     p.g = p.N / p.Nkv;
     p.D = (int)a->head_dim;
+    p.Dc = compiled_head_dim(p.D);
     p.kv = kv_kind(a->dtype_kv);
     p.paged = false;
     p.win.resize(p.B);
@@ -356,6 +363,7 @@ int plan_paged(const ifa_paged_args *a, IfaPlan &p, IfaCommon &c) {
     p.Nkv = (int)c.Nkv;
     p.g = p.N / p.Nkv;
     p.D = (int)a->head_dim;
+    p.Dc = compiled_head_dim(p.D);
     p.kv = kv_kind(a->dtype_kv);
     p.paged = true;
     p.win.resize(p.B);
@@ -412,7 +420,7 @@ int run(const IfaPlan &p, const Launch &L, void *ws, size_t ws_bytes, hipStream_
     if (p.workspace && !ws) return IFA_ERR_PARAM_NULLPTR;
     if (ws_bytes < p.workspace) return IFA_ERR_PARAM_INVALID;
     float *part_acc = reinterpret_cast<float *>(ws);
-    const size_t acc_bytes = ((size_t)p.total_slots * p.G * p.D * sizeof(float) + 255) / 256 * 256;
+    const size_t acc_bytes = ((size_t)p.total_slots * p.G * p.Dc * sizeof(float) + 255) / 256 * 256;
     float *part_ml = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + acc_bytes);
 
     SplitParams sp;
@@ -451,6 +459,7 @@ int run(const IfaPlan &p, const Launch &L, void *ws, size_t ws_bytes, hipStream_
     sp.score_mul = (float)(L.scale * 1.4426950408889634);
     sp.out = L.out;
     sp.row_mode = p.row_mode ? 1 : 0;
+    sp.Dr = p.D;
 
     CombineParams cp;
     memset(&cp, 0, sizeof cp);
@@ -462,7 +471,8 @@ int run(const IfaPlan &p, const Launch &L, void *ws, size_t ws_bytes, hipStream_
     cp.g = p.g;
     cp.G = p.G;
     cp.n_hg = p.n_hg;
-    cp.D = p.D;
+    cp.D = p.Dc;
+    cp.Dr = p.D;
     cp.out_bf16 = L.q_bf16;
     cp.aq_mode = L.aq_mode;
     cp.out_i8 = L.out_i8;
@@ -490,11 +500,11 @@ int run(const IfaPlan &p, const Launch &L, void *ws, size_t ws_bytes, hipStream_
             sp.list_seq[i] = p.list_seq.empty() ? 0 : (int32_t)p.list_seq[s.b0 + i];
         }
         sp.pre[s.nb] = cp.pre[s.nb] = s.pre[s.nb];
-        sp.part_acc = part_acc + s.slot_base * p.G * p.D;
+        sp.part_acc = part_acc + s.slot_base * p.G * p.Dc;
         sp.part_ml = part_ml + s.slot_base * p.G * 2;
         cp.part_acc = sp.part_acc;
         cp.part_ml = sp.part_ml;
-        if ((s.total > 0 || p.row_mode) && launch_split(sp, p.kv, p.D, p.G, p.paged, p.extra, stream) != hipSuccess)
+        if ((s.total > 0 || p.row_mode) && launch_split(sp, p.kv, p.Dc, p.G, p.paged, p.extra, stream) != hipSuccess)
             return IFA_ERR_RUNTIME;
         if (timed && si + 1 == p.slices.size() && hipEventRecord(L.ev_end, stream) != hipSuccess)
             return IFA_ERR_RUNTIME;

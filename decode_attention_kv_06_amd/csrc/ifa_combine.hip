@@ -135,20 +135,21 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineParams P) {
     for (int e = 0; e < kMaxPerLane; e++) {
         if (e >= per_lane) break;
         const int d = lane + 64 * e;
+        if (d >= P.Dr) break;                    // past the call's head dim
         float res = 0.f;
         if (nch > 0 && L > 0.f) {
             res = o[e] / L;
             if (P.aq_mode) {
                 const int j = h / P.g;
-                const int64_t pi = (P.aq_mode == 1) ? 1 : ((int64_t)P.Nkv + j) * D + d;
+                const int64_t pi = (P.aq_mode == 1) ? 1 : ((int64_t)P.Nkv + j) * P.Dr + d;
                 const float sv = ld_param(P.v_scale, pi, bf), ov = ld_param(P.v_offset, pi, bf);
                 res = sv * res + sv * ov;
             }
         }
-        const int64_t oi = (b * P.N + h) * D + d;
+        const int64_t oi = (b * P.N + h) * P.Dr + d;
         if (P.out_i8) {
             // int8 output: y = res * s + t on the fp32 result, ties to even, saturated
-            const int64_t ci = P.q2_per_channel ? (int64_t)h * D + d : 0;
+            const int64_t ci = P.q2_per_channel ? (int64_t)h * P.Dr + d : 0;
             const float qs = ld_q2(P.q_scale2, ci, P.q2_bf16);
             const float qo = P.q_offset2 ? ld_q2(P.q_offset2, ci, P.q2_bf16) : 0.f;
             const float y = fminf(fmaxf(__builtin_rintf(fmaf(res, qs, qo)), -128.f), 127.f);

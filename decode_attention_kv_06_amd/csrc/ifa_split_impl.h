@@ -255,9 +255,14 @@ void split_kernel(const SplitParams P) {
     const int hl = SCATTER ? head_of_lane<(G >= 2 ? G : 2)>(lane) : 0;   // scatter path: this lane's head
     const int r = lane / LPR;      // row group
     const int c = lane % LPR;      // 8-element slot within the row
+    // A head dim below the compiled D: lanes past it re-read the row's last
+    // 8-element chunk (every load stays inside the row) and hold a zero query,
+    // so they add nothing to the scores; their output columns are never written.
+    const int cq = min(c, P.Dr / 8 - 1);
+    const bool col_ok = c < P.Dr / 8;
     const char *kb = reinterpret_cast<const char *>(P.k);
     const char *vb = reinterpret_cast<const char *>(P.v);
-    const int64_t lane_byte = (int64_t)8 * c * EB;
+    const int64_t lane_byte = (int64_t)8 * cq * EB;
     __shared__ int32_t s_tbl[kWavesPerBlock][kTblSlots];
     int32_t *wtbl = s_tbl[wave];
 
@@ -282,9 +287,9 @@ void split_kernel(const SplitParams P) {
             if (len == 0) {     // an empty window: zero rows (the whole workgroup returns)
                 const int j = rj / P.n_hg, hg = rj - j * P.n_hg;
                 using T = std::conditional_t<KV == KV_BF16, __bf16, _Float16>;
-                T *o = reinterpret_cast<T *>(P.out) + ((P.b0 + bl) * P.N + j * P.g + hg * G) * (int64_t)D;
+                T *o = reinterpret_cast<T *>(P.out) + ((P.b0 + bl) * P.N + j * P.g + hg * G) * (int64_t)P.Dr;
                 const int nh = min(G, P.g - hg * G);
-                for (int i = threadIdx.x; i < nh * D; i += 64 * kWavesPerBlock) o[i] = (T)0.f;
+                for (int i = threadIdx.x; i < nh * P.Dr; i += 64 * kWavesPerBlock) o[i] = (T)0.f;
                 return;
             }
         }
@@ -317,10 +322,10 @@ void split_kernel(const SplitParams P) {
         for (int hh = 0; hh < G; hh++) {
             const int hq = SCATTER ? hh ^ hl : hh;
             const bool ok = hgq * G + hq < P.g;
-            const int64_t off = ((bq * P.N + hbq + (ok ? hq : 0)) * D + 8 * c) * 2;
+            const int64_t off = ((bq * P.N + hbq + (ok ? hq : 0)) * P.Dr + 8 * cq) * 2;
             u32x4 x = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(P.q) + off);
 #pragma unroll
-            for (int w = 0; w < 4; w++) qd[hh][w] = ok ? x[w] : 0u;
+            for (int w = 0; w < 4; w++) qd[hh][w] = ok && col_ok ? x[w] : 0u;
         }
     };
     // Dense caches: this lane's pointers into row lo + r of the segment's K and
@@ -375,14 +380,14 @@ void split_kernel(const SplitParams P) {
 #pragma unroll
             for (int hh = 0; hh < G; hh++) {
                 const int hq = SCATTER ? hh ^ hl : hh;
-                const bool ok = hg * G + hq < P.g;
-                const int64_t off = ((b * P.N + hbase + (ok ? hq : 0)) * D + 8 * c) * 2;
+                const bool ok = hg * G + hq < P.g && col_ok;
+                const int64_t off = ((b * P.N + hbase + (ok ? hq : 0)) * P.Dr + 8 * cq) * 2;
                 const u32x4 x = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(P.q) + off);
 #pragma unroll
                 for (int e = 0; e < 8; e++) {
                     const uint32_t bits = (x[e >> 1] >> (16 * (e & 1))) & 0xFFFF;
                     float qe = P.q_bf16 ? bf16_to_f32(bits) : f16_to_f32(bits);
-                    const int64_t si = (P.aq_mode == 1) ? 0 : (int64_t)j * D + 8 * c + e;
+                    const int64_t si = (P.aq_mode == 1) ? 0 : (int64_t)j * P.Dr + 8 * cq + e;
                     const uint32_t sb = reinterpret_cast<const uint16_t *>(P.k_scale)[si];
                     const float sc = P.q_bf16 ? bf16_to_f32(sb) : f16_to_f32(sb);
                     qe = ok ? qe * sc : 0.f;
@@ -965,9 +970,10 @@ void split_kernel(const SplitParams P) {
             const int nh = min(G, P.g - hg * G);
             using T = std::conditional_t<KV == KV_BF16, __bf16, _Float16>;
             typedef T t8 __attribute__((ext_vector_type(8)));
-            T *o = reinterpret_cast<T *>(P.out) + ((P.b0 + bl) * P.N + j * P.g + hg * G) * (int64_t)D;
-            for (int it = threadIdx.x; it < nh * (D / 8); it += 64 * kWavesPerBlock) {
-                const int hh = it / (D / 8), c8 = it - hh * (D / 8);
+            T *o = reinterpret_cast<T *>(P.out) + ((P.b0 + bl) * P.N + j * P.g + hg * G) * (int64_t)P.Dr;
+            const int nc = P.Dr / 8;                   // output chunks of 8 columns per head
+            for (int it = threadIdx.x; it < nh * nc; it += 64 * kWavesPerBlock) {
+                const int hh = it / nc, c8 = it - hh * nc;
                 float mx = kMaxInit;
 #pragma unroll
                 for (int w = 0; w < kWavesPerBlock; w++) mx = fmaxf(mx, s_ml[w][hh].x);
@@ -985,7 +991,7 @@ void split_kernel(const SplitParams P) {
                 t8 v;
 #pragma unroll
                 for (int e = 0; e < 8; e++) v[e] = (T)(L > 0.f ? a[e] / L : 0.f);
-                *reinterpret_cast<t8 *>(o + hh * D + 8 * c8) = v;
+                *reinterpret_cast<t8 *>(o + hh * P.Dr + 8 * c8) = v;
             }
         }
     }
@@ -1304,8 +1310,12 @@ template <int KV, int D, int G, bool PAGED, int EXTRA>
 hipError_t launch_one(const SplitParams &p, hipStream_t s) {
     const int blocks = (p.n_pieces + kWavesPerBlock - 1) / kWavesPerBlock;
     if constexpr (KV == KV_I8 && D == 128 && G == 8 && !PAGED && EXTRA == EX_NONE) {
-        hipLaunchKernelGGL(split_kernel_i8m<KV_I8>, dim3(blocks), dim3(64 * kWavesPerBlock), 0, s, p);
-    } else {
+        if (p.Dr == 128) {      // the matrix-core int8 kernel covers full 128-wide rows only
+            hipLaunchKernelGGL(split_kernel_i8m<KV_I8>, dim3(blocks), dim3(64 * kWavesPerBlock), 0, s, p);
+            return hipGetLastError();
+        }
+    }
+    {
         // row mode: every wave's partial state of the row, merged in LDS
         const size_t lds = p.row_mode ? (size_t)kWavesPerBlock * G * D * sizeof(float) : 0;
         hipLaunchKernelGGL((split_kernel<KV, D, G, PAGED, EXTRA>), dim3(blocks), dim3(64 * kWavesPerBlock), lds, s, p);

@@ -60,6 +60,8 @@ struct SplitParams {
     int32_t aq_mode;        // int8: 1 per-tensor, 2 per-channel
     int32_t q_bf16;         // int8 kernels: query dtype is bf16
     int32_t list_bnsd;      // per-batch BNSD caches: the head stride is list_seq[b] * sS
+    int32_t Dr;             // the call's head dim (<= the compiled D; lanes past it re-read the last
+                            // 16-byte chunk of a row and carry a zero query)
     int32_t row_mode;       // one workgroup per (b, j, hg) row, merged, normalised and written out by it
                             // (16-bit caches and outputs); no partial states, no combine
     float score_mul;        // scale * log2(e)
@@ -82,7 +84,8 @@ struct CombineParams {
     const void *v_offset;
     int64_t piece;
     int32_t seg_cost;
-    int32_t N, Nkv, g, G, n_hg, D;
+    int32_t N, Nkv, g, G, n_hg, D;   // D: the compiled head dim (partial-state row length)
+    int32_t Dr;                      // the call's head dim (output row length)
     int32_t out_bf16;
     int32_t aq_mode;
     int32_t out_i8;         // int8 output: quantise with (q_scale2, q_offset2)

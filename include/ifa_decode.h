@@ -114,8 +114,9 @@ enum { IFA_ANTIQUANT_NONE = 0, IFA_ANTIQUANT_PER_TENSOR = 1, IFA_ANTIQUANT_PER_C
  *   two last fields of the struct; a struct_size that stops before them means
  *   no positional bias (pse_shift must then be NULL).
  * Envelope: 1 <= B <= 65536, 1 <= N <= 256, N % N_kv == 0,
- *   head_dim in {64, 128, 256, 512}, dtype_out == dtype_q or IFA_DT_I8,
- *   dtype_kv == dtype_q or IFA_DT_I8.
+ *   8 <= head_dim <= 512 with head_dim % 8 == 0 (the README bounds the head
+ *   dim by 512; whole 16-byte row chunks are this library's requirement),
+ *   dtype_out == dtype_q or IFA_DT_I8, dtype_kv == dtype_q or IFA_DT_I8.
  * Int8 output (dtype_out IFA_DT_I8; README "Constraints": quantScale2
  *   required, quantOffset2 optional, per-tensor or per-channel, fp32, or bf16
  *   with bf16 inputs): each output element o of head h, column d becomes

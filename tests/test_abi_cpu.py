@@ -83,6 +83,16 @@ def test_dense_valid_call_sizes_workspace_without_a_device():
     assert n == 8 * 4 * 128 * 4 + 256
 
 
+@pytest.mark.parametrize("D,Dc", [(8, 64), (40, 64), (96, 128), (136, 256), (200, 256), (264, 512), (504, 512)])
+def test_head_dims_below_a_compiled_size_run_on_it(D, Dc):
+    # any head dim up to 512 in whole 16-byte lanes is accepted; its partial
+    # states take the compiled size's row length, so the workspace matches it
+    rc, n = ws_size("ifa_decode_workspace_size", dense_args(head_dim=D))
+    rc_c, n_c = ws_size("ifa_decode_workspace_size", dense_args(head_dim=Dc))
+    assert rc == 0 and rc_c == 0
+    assert n == n_c
+
+
 LENS = (ctypes.c_int64 * 2)(10, 64)
 BAD_LENS = (ctypes.c_int64 * 2)(10, 65)
 PADS1 = (ctypes.c_int64 * 1)(3)
@@ -102,7 +112,10 @@ PADS1 = (ctypes.c_int64 * 1)(3)
     (dict(num_heads=257), 161002),
     (dict(num_key_value_heads=3), 161002),
     (dict(num_key_value_heads=9), 161002),
-    (dict(head_dim=96), 161002),
+    (dict(head_dim=100), 161002),                  # not whole 16-byte lanes
+    (dict(head_dim=520), 161002),
+    (dict(head_dim=4), 161002),
+    (dict(head_dim=0), 161002),
     (dict(kv_seq_len=0), 161002),
     (dict(scale_value=float("nan")), 161002),
     (dict(actual_seq_lengths=ctypes.cast(BAD_LENS, ctypes.c_void_p)), 161002),
