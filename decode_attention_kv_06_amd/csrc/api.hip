@@ -61,7 +61,7 @@ struct IfaPlan {
     int Dc = 0;                          // compiled head dim: the smallest of 64/128/256/512 >= D
     bool paged = false;
     bool out_i8 = false;                 // int8 output (finished by the combine)
-    bool row_mode = false;               // one wave per row, finished in place, no combine
+    bool row_mode = false;               // one workgroup per row, finished in place, no combine
     int extra = EX_NONE;                 // split kernel variant (mask / positional bias)
     std::vector<Window> win;             // per batch
     std::vector<int64_t> list_seq;       // per-batch caches: positions of each tensor
@@ -86,9 +86,10 @@ int resident_waves(int kv, int D, int G, bool paged, int extra) {
     return slot;
 }
 
-// Exact balancing: the rows (b, j, hg) of a slice are laid end to end and cut
-// into n_pieces equal pieces, one per resident wave of the split kernel, so
-// every wave streams the same number of KV positions.  A row meets at most
+// Balancing: the rows (b, j, hg) of a slice are laid end to end, each row
+// start charged a tile and a half of extra cost, and the cost is cut into
+// n_pieces equal pieces, one per resident wave of the split kernel, so every
+// wave gets the same work (positions plus row starts).  A row meets at most
 // ceil(len / piece) + 1 pieces, which bounds its partial slots.
 int finish_plan(IfaPlan &p, int64_t split_tokens) {
     p.G = 1;
