@@ -54,14 +54,17 @@ def oracle_of(inp, rows=None):
     return oracle.sfa(inp, rows=rows) if isinstance(inp["spec"], SfaSpec) else oracle.ifa(inp, rows=rows)
 
 
-def compare_int8(inp, out, tol=None):
+def compare_int8(inp, out, tol=None, min_clear=0.4):
     """int8 output codes against the oracle's codes of the exact output.
 
     The kernel decides each code from its fp32 result, the oracle from the
     exact one; the two can only differ where the scaled value lies within the
     float result's error of a rounding boundary.  Codes must agree wherever
     the oracle's value before rounding is farther than that margin from a
-    boundary (k + 1/2), and differ by at most 1 elsewhere."""
+    boundary (k + 1/2), and differ by at most 1 elsewhere.  ``min_clear`` is the
+    share of codes that must be decided away from a boundary for the check to
+    mean something (0 for drawn cases whose output can be constant, such as
+    an all-empty call with one per-tensor offset)."""
     s = inp["spec"]
     ref = oracle_of(inp).reshape(-1, s.N * s.D)
     codes, pre = oracle.quant_int8(ref, inp["quant_scale2"], inp["quant_offset2"])
@@ -74,7 +77,7 @@ def compare_int8(inp, out, tol=None):
     diff = np.abs(got - codes.astype(np.int32))
     say("  int8 codes: %d of %d differ, max diff %d; %d codes decided away from a boundary" % (
         int((diff > 0).sum()), diff.size, int(diff.max(initial=0)), int(clear.sum())))
-    assert clear.mean() > 0.4, "the decision margin leaves too few codes to check exactly"
+    assert clear.mean() >= min_clear, "the decision margin leaves too few codes to check exactly"
     assert (diff[clear] == 0).all(), "int8 codes differ away from a rounding boundary"
     assert diff.max(initial=0) <= 1
     return int((diff > 0).sum())
