@@ -16,9 +16,12 @@ Protocol, per workload:
     write (zero) a 512 MiB buffer, twice the 256 MiB last-level cache, then
     read it back with the read probe so that the flush's own dirty lines are
     written back before the call rather than during it; event; call; event],
-    the flush outside the event pair.  The library also records two events on
-    the call's stream around its dominant kernel, which give that kernel's
-    duration for the roofline;
+    the flush outside the event pair;
+  * timed, flushed, instrumented: the same loop again with the library
+    recording two events on the call's stream around its dominant kernel,
+    which give that kernel's duration for the roofline.  It is a loop of its
+    own because those events put a timestamp and a cache release between the
+    call's launches, adding 8-10 us to each call;
   * timed, warm (secondary, labelled): --steps back-to-back calls between two
     events, nothing in between, plus the host wall time of that loop;
   * median, p10 and p90 of the flushed call times; GB/s = algorithmic bytes /
@@ -354,8 +357,12 @@ class Gpu:
             self.read(self.flush_buf)
 
     def timed(self, one_call, steps: int, warmup: int, warmup_ms: float, kernel_events: bool = True) -> dict:
-        """Warm-up, then the flushed loop (call events and, when the library
-        records them, dominant-kernel events), then the warm loop."""
+        """Warm-up, then the flushed loop of plain calls (the call's own
+        events only), then, when the library records them, a second flushed
+        loop with its event pair around the dominant kernel, then the warm
+        loop.  The kernel's events stay out of the loop that times the call:
+        each one puts a timestamp and a cache release between the call's
+        launches, which added 8-10 us to every flushed call."""
         torch = self.torch
         t_w = time.perf_counter()
         n_warm = 0
@@ -367,16 +374,27 @@ class Gpu:
                 torch.cuda.synchronize()
         torch.cuda.synchronize()
         cb, ce = self.events(steps), self.events(steps)
-        kb, ke = (self.events(steps), self.events(steps)) if kernel_events else (None, None)
         torch.cuda.synchronize()
         for i in range(steps):
             self.flush()
             cb[i].record(self.stream)
-            one_call(kb[i] if kb else None, ke[i] if ke else None)
+            one_call(None, None)
             ce[i].record(self.stream)
         torch.cuda.synchronize()
         call_ms = [cb[i].elapsed_time(ce[i]) for i in range(steps)]
-        kern_ms = [kb[i].elapsed_time(ke[i]) for i in range(steps)] if kb else None
+        kern_ms = instr_ms = None
+        if kernel_events:
+            cb, ce = self.events(steps), self.events(steps)
+            kb, ke = self.events(steps), self.events(steps)
+            torch.cuda.synchronize()
+            for i in range(steps):
+                self.flush()
+                cb[i].record(self.stream)
+                one_call(kb[i], ke[i])
+                ce[i].record(self.stream)
+            torch.cuda.synchronize()
+            kern_ms = [kb[i].elapsed_time(ke[i]) for i in range(steps)]
+            instr_ms = [cb[i].elapsed_time(ce[i]) for i in range(steps)]
         # warm: back to back, nothing between the calls
         e0, e1 = self.events(1)[0], self.events(1)[0]
         torch.cuda.synchronize()
@@ -388,6 +406,7 @@ class Gpu:
         torch.cuda.synchronize()
         host_ms = (time.perf_counter() - t0) * 1e3 / steps
         return {"call": stats_us(call_ms), "kernel": stats_us(kern_ms) if kern_ms else None,
+                "call_with_kernel_events": stats_us(instr_ms) if instr_ms else None,
                 "warm_us": round(e0.elapsed_time(e1) / steps * 1e3, 2), "host_us": round(host_ms * 1e3, 2),
                 "warmup_calls": n_warm}
 
@@ -472,6 +491,7 @@ def measure(gpu: Gpu, name: str, args, ceiling_gbs=None) -> tuple:
         "algorithmic_bytes": alg["total"],
         "streamed_bytes": alg["streamed"],
         "us_per_call": r["call"],
+        "us_per_call_with_kernel_events": r["call_with_kernel_events"],
         "gbs": round(gbs, 1),
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "pct_of_measured_ceiling": round(100.0 * gbs / ceiling_gbs, 2) if ceiling_gbs else None,
@@ -565,7 +585,8 @@ def main() -> int:
         "flush_between_calls": args.flush != "none",
         "flush": "%s %d MiB before every timed call, outside its events" % (args.flush, FLUSH_BYTES >> 20)
                  if args.flush != "none" else "none",
-        "timing": "per-call HIP events on the call's stream; median, p10 and p90 over the flushed calls",
+        "timing": "per-call HIP events on the call's stream; median, p10 and p90 over the flushed calls; "
+                  "the dominant kernel's events in a second flushed loop of their own",
         "warm_back_to_back_us_per_call": rec["warm_back_to_back_us_per_call"],
         "host_wall_us_per_call": rec["host_wall_us_per_call"],
         "algorithmic_bytes": rec["algorithmic_bytes"],
