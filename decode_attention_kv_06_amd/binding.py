@@ -71,6 +71,11 @@ class SfaMlaArgs(ctypes.Structure):
         ("return_softmax_lse", I32)]
 
 
+class SfaMlaPlan(ctypes.Structure):
+    _fields_ = [("chunks", ctypes.c_int32), ("chunk_entries", ctypes.c_int32), ("workgroups", ctypes.c_int32),
+                ("all_heads", ctypes.c_int32)]
+
+
 class IfaError(RuntimeError):
     def __init__(self, status: int, what: str):
         super().__init__("%s returned %d (%s)" % (what, status, status_string(status)))
@@ -97,6 +102,8 @@ def lib() -> ctypes.CDLL:
             run = getattr(L, name)
             run.argtypes = [ctypes.POINTER(st), P, ctypes.c_size_t, P]
             run.restype = ctypes.c_int
+        L.sfa_decode_mla_plan.argtypes = [ctypes.POINTER(SfaMlaArgs), ctypes.POINTER(SfaMlaPlan)]
+        L.sfa_decode_mla_plan.restype = ctypes.c_int
         L.ifa_decode_noalloc.argtypes = [ctypes.POINTER(IfaDecodeArgs), P]
         L.ifa_decode_noalloc.restype = ctypes.c_int
         L.ifa_status_string.argtypes = [ctypes.c_int]
@@ -404,6 +411,22 @@ def sfa_args(query, query_rope, key, key_rope, value, sparse_indices, block_tabl
         a.softmax_max_out, a.softmax_sum_out = _ptr(softmax_max_out), _ptr(softmax_sum_out)
         a.return_softmax_lse = 1
     return a
+
+
+def sfa_decode_mla_plan(query, query_rope, key, key_rope, value, sparse_indices, block_table,
+                        actual_seq_lengths_kv, out, **kw) -> dict:
+    """The launch sfa_decode_mla would make for these arguments (sfa_decode_mla_plan):
+    chunks per query row, entries per chunk, workgroups, and whether one workgroup
+    takes every head of a chunk."""
+    keep: list = []
+    a = sfa_args(query, query_rope, key, key_rope, value, sparse_indices, block_table, actual_seq_lengths_kv, out,
+                 keep=keep, **kw)
+    pl = SfaMlaPlan()
+    rc = lib().sfa_decode_mla_plan(ctypes.byref(a), ctypes.byref(pl))
+    if rc != 0:
+        raise IfaError(rc, "sfa_decode_mla_plan")
+    return dict(chunks=pl.chunks, chunk_entries=pl.chunk_entries, workgroups=pl.workgroups,
+                all_heads=bool(pl.all_heads))
 
 
 def sfa_decode_mla(query, query_rope, key, key_rope, value, sparse_indices, block_table, actual_seq_lengths_kv,

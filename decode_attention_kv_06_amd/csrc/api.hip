@@ -26,7 +26,7 @@ namespace {
 
 using namespace ifa;
 
-constexpr int kAbiVersion = 6;
+constexpr int kAbiVersion = 7;
 constexpr int kRowModeTiles = 4;     // longest row (in split-kernel tiles) that row mode takes
 
 bool is_float_dt(int dt) { return dt == IFA_DT_F16 || dt == IFA_DT_BF16; }
@@ -709,6 +709,8 @@ int ifa_decode_paged(const ifa_paged_args *a, void *ws, size_t ws_bytes, ifa_str
 int sfa_decode_mla_workspace_size(const sfa_mla_args *a, size_t *bytes) {
     return ifa::sfa_workspace_size(a, bytes);
 }
+
+int sfa_decode_mla_plan(const sfa_mla_args *a, sfa_mla_plan *plan) { return ifa::sfa_plan_info(a, plan); }
 
 int sfa_decode_mla(const sfa_mla_args *a, void *ws, size_t ws_bytes, ifa_stream_t stream) {
     return ifa::sfa_run(a, ws, ws_bytes, reinterpret_cast<hipStream_t>(stream));

@@ -37,7 +37,8 @@ struct SfaParams {
     int32_t sbs_shift;        // log2 sparse_block_size
     uint32_t bs_magic;
     int32_t bs_shift;
-    int32_t n_hb;             // blocks of 64 heads
+    int32_t n_hb;             // blocks of 64 heads (1 with `wide`)
+    int32_t wide;             // more than 64 heads: sfa_wide_kernel, one workgroup per chunk for every head
     int32_t n_sc;             // index chunks per query row
     int32_t chunk;            // index entries per chunk (chunk << sbs_shift <= kSfaChunkMax rows)
     int32_t direct;           // one chunk per row: write the normalised output directly
@@ -47,6 +48,7 @@ struct SfaParams {
 hipError_t sfa_launch(const SfaParams &p, bool bf16, int grid, hipStream_t s, hipEvent_t ev_begin, hipEvent_t ev_end);
 
 int sfa_workspace_size(const sfa_mla_args *a, size_t *bytes);
+int sfa_plan_info(const sfa_mla_args *a, sfa_mla_plan *out);
 int sfa_run(const sfa_mla_args *a, void *ws, size_t ws_bytes, hipStream_t stream);
 
 }  // namespace ifa

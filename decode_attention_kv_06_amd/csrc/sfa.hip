@@ -99,42 +99,66 @@ size_t part_o_bytes(size_t rows) { return (rows * 512 * 2 + 255) / 256 * 256; }
 
 struct SfaPlan {
     int n_hb = 0, n_sc = 0, chunk = 0, grid = 0;
+    bool wide = false;
     size_t workspace = 0;
 };
 
-// Work split: workgroups of 64 heads x one chunk of one query row's index
-// list, about one per compute unit; a chunk gathers at most kSfaChunkMax
-// rows (entries x sparse_block_size) and a multiple of the 32-row tile when
-// the list is long enough.
-int plan(const sfa_mla_args *a, const SfaShape &sh, SfaPlan &p) {
-    p.n_hb = (int)((a->q_heads + 63) / 64);
-    int n_sc;
-    if (a->split_hint > 0) {
-        n_sc = (int)a->split_hint;
-    } else {
-        int dev = 0, cus = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-            return IFA_ERR_RUNTIME;
-        const int64_t per = sh.R * p.n_hb;
-        n_sc = (int)std::max<int64_t>(1, (cus + per / 2) / per);
-    }
+int device_cus(int *cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return IFA_ERR_RUNTIME;
+    return IFA_OK;
+}
+
+// Chunks of each query row's index list for `per` workgroups per chunk index
+// (query rows x head blocks): the forced count, else about one workgroup per
+// compute unit.  A chunk gathers at most kSfaChunkMax rows (entries x
+// sparse_block_size) and a multiple of the 32-row tile when the list is long
+// enough.  Fills n_sc, chunk and grid (workgroups, rounded to whole XCD
+// rounds of 8 per head block).
+int split_chunks(const sfa_mla_args *a, const SfaShape &sh, int64_t per, int cus, SfaPlan &p) {
+    int64_t n_sc = a->split_hint > 0 ? a->split_hint : std::max<int64_t>(1, (cus + per / 2) / per);
     const int64_t gran = std::max(1, 32 >> sh.sbs_shift), cap = kSfaChunkMax >> sh.sbs_shift;
     int64_t chunk = (a->sparse_size + n_sc - 1) / n_sc;
     chunk = (chunk + gran - 1) / gran * gran;
     if (chunk > cap) chunk = cap;
-    const int64_t n_sc64 = (a->sparse_size + chunk - 1) / chunk;
-    if (n_sc64 > (1 << 20)) return IFA_ERR_PARAM_INVALID;
-    n_sc = (int)n_sc64;
-    p.chunk = (int)chunk;
-    p.n_sc = n_sc;
-    const int64_t groups = sh.R * n_sc;
-    const int64_t grid = (groups + 7) / 8 * 8 * p.n_hb;
+    n_sc = (a->sparse_size + chunk - 1) / chunk;
+    if (n_sc > (1 << 20)) return IFA_ERR_PARAM_INVALID;
+    const int64_t grid = (sh.R * n_sc + 7) / 8 * 8 * p.n_hb;
     if (grid > INT32_MAX) return IFA_ERR_PARAM_INVALID;
+    p.n_sc = (int)n_sc;
+    p.chunk = (int)chunk;
     p.grid = (int)grid;
+    return IFA_OK;
+}
+
+// Work split: workgroups of 64 heads x one chunk of one query row's index
+// list (sfa_kernel), one workgroup per compute unit at most (each takes
+// nearly all of a CU's LDS).  With more than 64 heads, when that grid would
+// not fit on the CUs at once, one workgroup takes every head of a chunk
+// (sfa_wide_kernel): half the workgroups, so the call runs in one round.
+// The CU count is read only when it decides something (no forced chunk
+// count, or more than 64 heads).
+int plan(const sfa_mla_args *a, const SfaShape &sh, SfaPlan &p) {
+    int cus = 0;
+    if (a->split_hint == 0 || a->q_heads > 64) {
+        const int rc = device_cus(&cus);
+        if (rc) return rc;
+    }
+    p.wide = false;
+    p.n_hb = (int)((a->q_heads + 63) / 64);
+    int rc = split_chunks(a, sh, sh.R * p.n_hb, cus, p);
+    if (rc) return rc;
+    if (a->q_heads > 64 && p.grid > cus) {
+        p.wide = true;
+        p.n_hb = 1;
+        rc = split_chunks(a, sh, sh.R, cus, p);
+        if (rc) return rc;
+    }
     p.workspace = 0;
-    if (n_sc > 1) {
-        const size_t rows = (size_t)sh.R * n_sc * a->q_heads;
+    if (p.n_sc > 1) {
+        const size_t rows = (size_t)sh.R * p.n_sc * a->q_heads;
         p.workspace = part_o_bytes(rows) + (rows * 2 * sizeof(float) + 255) / 256 * 256;
     }
     return IFA_OK;
@@ -158,6 +182,21 @@ int sfa_workspace_size(const sfa_mla_args *a, size_t *bytes) {
     rc = plan(a, sh, p);
     if (rc) return rc;
     *bytes = p.workspace;
+    return IFA_OK;
+}
+
+int sfa_plan_info(const sfa_mla_args *a, sfa_mla_plan *out) {
+    if (!out) return IFA_ERR_PARAM_NULLPTR;
+    SfaShape sh;
+    int rc = validate(a, sh);
+    if (rc) return rc;
+    SfaPlan p;
+    rc = plan(a, sh, p);
+    if (rc) return rc;
+    out->chunks = p.n_sc;
+    out->chunk_entries = p.chunk;
+    out->workgroups = p.grid;
+    out->all_heads = p.wide ? 1 : 0;
     return IFA_OK;
 }
 
@@ -205,6 +244,7 @@ int sfa_run(const sfa_mla_args *a, void *ws, size_t ws_bytes, hipStream_t stream
         p.bs_magic = magic_for((uint32_t)a->block_size, &p.bs_shift);
     }
     p.n_hb = pl.n_hb;
+    p.wide = pl.wide;
     p.n_sc = pl.n_sc;
     p.chunk = pl.chunk;
     p.direct = pl.n_sc == 1;

@@ -6,7 +6,8 @@
 // with K~, K~rope, V~ the rows block_table[b][t / bs], t % bs of key,
 // key_rope and value for each valid index t (0 <= t < actual_seq_lengths_kv[b]).
 //
-// Mapping to the hardware:
+// Mapping to the hardware (sfa_kernel; sfa_wide_kernel below takes every
+// head of a chunk in one workgroup when that halves an oversized grid):
 //  * one workgroup (4 waves) per (batch, block of 64 heads, chunk of
 //    indices); each wave owns 16 heads.  Each XCD takes a contiguous range
 //    of (batch, chunk) groups with all their head blocks, so the second read
@@ -175,70 +176,13 @@ __device__ __forceinline__ void ring_barrier() {
 // group's reads in flight during the current MFMAs.
 __device__ __forceinline__ void lds_wait() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-// Half-tile h (key rows of tile h/2 for even h, value rows for odd h) lives in
-// ring slot h % 4.  Before computing half-tile h a wave waits until only its
-// copies of halves h+1 and h+2 may still be in flight.  Halves past the last
-// tile are still copied (the last valid row again, never read), so that count
-// is the same at every step.
-
-template <bool BF>
-__global__ __launch_bounds__(256, 1) void sfa_kernel(const SfaParams P) {
-    using M = Mfma<BF>;
-    using vec8 = typename M::vec8;
-    // the four ring slots as distinct objects, so the compiler can tell a read
-    // of one from the copies in flight into another
-    __shared__ __attribute__((aligned(16))) char s_slot0[kSlot];
-    __shared__ __attribute__((aligned(16))) char s_slot1[kSlot];
-    __shared__ __attribute__((aligned(16))) char s_slot2[kSlot];
-    __shared__ __attribute__((aligned(16))) char s_slot3[kSlot];
-    __shared__ __attribute__((aligned(16))) char s_p[kWavesPerBlock * 64 * 16];   // P of each head group
-    __shared__ int32_t s_rows[kChunkMax];
-    __shared__ float s_alpha[64];           // rescale factor of each head for the current tile
-    __shared__ float s_linv[64];            // 1 / l of each head (single-chunk output)
-    __shared__ __attribute__((aligned(16))) int32_t s_flag[kWavesPerBlock];   // group raised its running max this tile
-    __shared__ int32_t s_cnt[2][kWavesPerBlock];
-
+// The chunk's valid cache rows, compacted in order into the LDS table
+// `s_rows`; returns their count (wave-uniform).  Every thread of the
+// workgroup calls it (it synchronises the workgroup twice).
+__device__ __forceinline__ int compact_chunk(const SfaParams &P, int qr, int sc, int32_t *s_rows,
+                                             int32_t (*s_cnt)[kWavesPerBlock]) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int g = lane >> 4, l16 = lane & 15;
-
-    // workgroup -> (query row, chunk, head block).  Workgroup ids congruent
-    // mod 8 run on one XCD; XCD x takes the contiguous range of (query row,
-    // chunk) groups [x g8, (x + 1) g8) with all their head blocks, so the
-    // chunks of a query row (one query and block-table row) and the head
-    // blocks of a chunk (the same gathered rows) meet in one L2.
-    const int id = blockIdx.x;
-    const int x8 = id & 7, k8 = id >> 3;
-    const int hb = k8 % P.n_hb;
-    const int g8 = (P.R * P.n_sc + 7) >> 3;
-    const int grp = x8 * g8 + k8 / P.n_hb;
-    if (grp >= P.R * P.n_sc) return;               // whole workgroup leaves together
-    const int qr = grp / P.n_sc, sc = grp - qr * P.n_sc;
-
-    // Head groups of 16: wave w computes the scores of group w; every wave
-    // accumulates P.V for all four groups over its own 128 output columns.  A
-    // group past the head count keeps P = 0 and is never stored.
-    const int n_act = min(kWavesPerBlock, (P.QN - hb * 64 + 15) / 16);   // >= 1
-    const bool qk_wave = wave < n_act;
-    if (!qk_wave) *reinterpret_cast<u32x4 *>(s_p + (wave * 64 + lane) * 16) = u32x4{0, 0, 0, 0};
-    if (lane == 0) s_flag[wave] = 0;
-
-    // ---------------------------------------------------- query rows (issued first)
-    const int h = hb * 64 + wave * 16 + l16;          // head of lanes l16 (score layout)
-    const bool h_ok = h < P.QN;
-    vec8 qreg[kDK / 32];
-#pragma unroll
-    for (int ks = 0; ks < kDK / 32; ks++) {
-        u32x4 x = {0, 0, 0, 0};
-        if (h_ok) {
-            const char *src = ks < kD / 32
-                ? reinterpret_cast<const char *>(P.q) + (((int64_t)qr * P.QN + h) * kD + 32 * ks + 8 * g) * 2
-                : reinterpret_cast<const char *>(P.q_rope) + (((int64_t)qr * P.QN + h) * kDR + 32 * (ks - kD / 32) + 8 * g) * 2;
-            x = *reinterpret_cast<const u32x4 *>(src);
-        }
-        qreg[ks] = __builtin_bit_cast(vec8, x);
-    }
-
     // ---------------------------------------------------- the row's batch and attended range
     // Query row -> batch b, place s among the batch's Lq query rows; the
     // cache rows of batch b start at kv0 and hold Lkv positions; positions
@@ -331,6 +275,102 @@ __global__ __launch_bounds__(256, 1) void sfa_kernel(const SfaParams P) {
     }
     __syncthreads();
     nv = __builtin_amdgcn_readfirstlane(nv);
+    return nv;
+}
+
+// Gather copies of one tile half.  Wave w copies tile rows 8w .. 8w+7: one
+// 1 KiB instruction per key row and per value row (the row base is
+// wave-uniform) and one instruction for the eight rope rows (lane l: row
+// 8w + l/8, 16-byte chunk l%8).  `rows` holds, in lane l, the physical row of
+// tile row 8w + l/8; tiles past the last repeat its last row.
+__device__ __forceinline__ int tile_rows(const int32_t *s_rows, int tile, int nv, int lane, int wave) {
+    return s_rows[min(tile * kT + 8 * wave + (lane >> 3), nv - 1)];
+}
+__device__ __forceinline__ void issue_key_half(const SfaParams &P, char *slot, int rows, int lane, int wave) {
+    const char *keyb = reinterpret_cast<const char *>(P.key);
+    const char *ropeb = reinterpret_cast<const char *>(P.key_rope);
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        const int64_t row = __builtin_amdgcn_readlane(rows, 8 * j);
+        dma16(keyb + row * 1024 + lane * 16, slot + (8 * wave + j) * kRP);
+    }
+    const int r = 8 * wave + (lane >> 3);
+    dma16(ropeb + (int64_t)rows * 128 + 16 * ((lane & 7) ^ rope_swz(r)), slot + kRopeOff + wave * 1024);
+}
+__device__ __forceinline__ void issue_value_half(const SfaParams &P, char *slot, int rows, int lane, int wave) {
+    const char *valb = reinterpret_cast<const char *>(P.value);
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        const int64_t row = __builtin_amdgcn_readlane(rows, 8 * j);
+        dma16(valb + row * 1024 + lane * 16, slot + (8 * wave + j) * kRP);
+    }
+}
+
+// Half-tile h (key rows of tile h/2 for even h, value rows for odd h) lives in
+// ring slot h % 4.  Before computing half-tile h a wave waits until only its
+// copies of halves h+1 and h+2 may still be in flight.  Halves past the last
+// tile are still copied (the last valid row again, never read), so that count
+// is the same at every step.
+
+template <bool BF>
+__global__ __launch_bounds__(256, 1) void sfa_kernel(const SfaParams P) {
+    using M = Mfma<BF>;
+    using vec8 = typename M::vec8;
+    // the four ring slots as distinct objects, so the compiler can tell a read
+    // of one from the copies in flight into another
+    __shared__ __attribute__((aligned(16))) char s_slot0[kSlot];
+    __shared__ __attribute__((aligned(16))) char s_slot1[kSlot];
+    __shared__ __attribute__((aligned(16))) char s_slot2[kSlot];
+    __shared__ __attribute__((aligned(16))) char s_slot3[kSlot];
+    __shared__ __attribute__((aligned(16))) char s_p[kWavesPerBlock * 64 * 16];   // P of each head group
+    __shared__ int32_t s_rows[kChunkMax];
+    __shared__ float s_alpha[64];           // rescale factor of each head for the current tile
+    __shared__ float s_linv[64];            // 1 / l of each head (single-chunk output)
+    __shared__ __attribute__((aligned(16))) int32_t s_flag[kWavesPerBlock];   // group raised its running max this tile
+    __shared__ int32_t s_cnt[2][kWavesPerBlock];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, l16 = lane & 15;
+
+    // workgroup -> (query row, chunk, head block).  Workgroup ids congruent
+    // mod 8 run on one XCD; XCD x takes the contiguous range of (query row,
+    // chunk) groups [x g8, (x + 1) g8) with all their head blocks, so the
+    // chunks of a query row (one query and block-table row) and the head
+    // blocks of a chunk (the same gathered rows) meet in one L2.
+    const int id = blockIdx.x;
+    const int x8 = id & 7, k8 = id >> 3;
+    const int hb = k8 % P.n_hb;
+    const int g8 = (P.R * P.n_sc + 7) >> 3;
+    const int grp = x8 * g8 + k8 / P.n_hb;
+    if (grp >= P.R * P.n_sc) return;               // whole workgroup leaves together
+    const int qr = grp / P.n_sc, sc = grp - qr * P.n_sc;
+
+    // Head groups of 16: wave w computes the scores of group w; every wave
+    // accumulates P.V for all four groups over its own 128 output columns.  A
+    // group past the head count keeps P = 0 and is never stored.
+    const int n_act = min(kWavesPerBlock, (P.QN - hb * 64 + 15) / 16);   // >= 1
+    const bool qk_wave = wave < n_act;
+    if (!qk_wave) *reinterpret_cast<u32x4 *>(s_p + (wave * 64 + lane) * 16) = u32x4{0, 0, 0, 0};
+    if (lane == 0) s_flag[wave] = 0;
+
+    // ---------------------------------------------------- query rows (issued first)
+    const int h = hb * 64 + wave * 16 + l16;          // head of lanes l16 (score layout)
+    const bool h_ok = h < P.QN;
+    vec8 qreg[kDK / 32];
+#pragma unroll
+    for (int ks = 0; ks < kDK / 32; ks++) {
+        u32x4 x = {0, 0, 0, 0};
+        if (h_ok) {
+            const char *src = ks < kD / 32
+                ? reinterpret_cast<const char *>(P.q) + (((int64_t)qr * P.QN + h) * kD + 32 * ks + 8 * g) * 2
+                : reinterpret_cast<const char *>(P.q_rope) + (((int64_t)qr * P.QN + h) * kDR + 32 * (ks - kD / 32) + 8 * g) * 2;
+            x = *reinterpret_cast<const u32x4 *>(src);
+        }
+        qreg[ks] = __builtin_bit_cast(vec8, x);
+    }
+
+    const int nv = compact_chunk(P, qr, sc, s_rows, s_cnt);
 
     // ---------------------------------------------------- gather copies
     // Wave w copies tile rows 8w .. 8w+7: one 1 KiB instruction per key row and
@@ -609,6 +649,307 @@ __global__ __launch_bounds__(256, 1) void sfa_kernel(const SfaParams P) {
     }
 }
 
+// All heads of a query row in one workgroup.  The planner takes it when there
+// are more than 64 heads and the workgroups of 64 heads would not all fit on
+// the compute units at once (one workgroup per CU): it halves that grid, so
+// the call runs in one round instead of two.  Wave w
+// scores heads 32w .. 32w+31 (two groups of 16) and accumulates their P.V
+// over all 512 output columns.  So every gathered row is copied into LDS once
+// per chunk, each key operand read from LDS serves both head groups (half
+// the key reads of one wave per 16 heads), P stays in the wave's registers
+// (the score layout is the P.V operand layout), and each wave keeps its own
+// heads' softmax state: no exchange of P, rescale factors or flags between
+// waves.  The register file holds the query of 32 heads (144 registers) and
+// the accumulators of 32 heads x 512 columns (256).  The copy ring, the
+// pipeline and the chunk table are those of sfa_kernel.
+template <bool BF>
+__global__ __launch_bounds__(256, 1) void sfa_wide_kernel(const SfaParams P) {
+    using M = Mfma<BF>;
+    using vec8 = typename M::vec8;
+    __shared__ __attribute__((aligned(16))) char s_slot0[kSlot];
+    __shared__ __attribute__((aligned(16))) char s_slot1[kSlot];
+    __shared__ __attribute__((aligned(16))) char s_slot2[kSlot];
+    __shared__ __attribute__((aligned(16))) char s_slot3[kSlot];
+    __shared__ int32_t s_rows[kChunkMax];
+    __shared__ int32_t s_cnt[2][kWavesPerBlock];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, l16 = lane & 15;
+
+    // workgroup -> (query row, chunk); XCD x (ids congruent mod 8) takes the
+    // contiguous groups [x g8, (x + 1) g8), so the chunks of a query row share
+    // its query and block-table rows in one L2
+    const int id = blockIdx.x;
+    const int x8 = id & 7, k8 = id >> 3;
+    const int g8 = (P.R * P.n_sc + 7) >> 3;
+    const int grp = x8 * g8 + k8;
+    if (grp >= P.R * P.n_sc) return;               // whole workgroup leaves together
+    const int qr = grp / P.n_sc, sc = grp - qr * P.n_sc;
+    const bool act = 32 * wave < P.QN;             // the wave has heads (wave-uniform)
+
+    // ---------------------------------------------------- query rows (issued first)
+    // qreg[hg]: head 32 wave + 16 hg + l16, dims 32 ks + 8 g .. + 7 of q | q_rope
+    vec8 qreg[2][kDK / 32];
+#pragma unroll
+    for (int hg = 0; hg < 2; hg++) {
+        const int h = 32 * wave + 16 * hg + l16;
+#pragma unroll
+        for (int ks = 0; ks < kDK / 32; ks++) {
+            u32x4 x = {0, 0, 0, 0};
+            if (h < P.QN) {
+                const char *src = ks < kD / 32
+                    ? reinterpret_cast<const char *>(P.q) + (((int64_t)qr * P.QN + h) * kD + 32 * ks + 8 * g) * 2
+                    : reinterpret_cast<const char *>(P.q_rope) + (((int64_t)qr * P.QN + h) * kDR + 32 * (ks - kD / 32) + 8 * g) * 2;
+                x = *reinterpret_cast<const u32x4 *>(src);
+            }
+            qreg[hg][ks] = __builtin_bit_cast(vec8, x);
+        }
+    }
+
+    const int nv = compact_chunk(P, qr, sc, s_rows, s_cnt);
+
+    // ---------------------------------------------------- gather copies
+    const int n_tiles = (nv + kT - 1) / kT;
+    auto rows_of = [&](int tile) { return tile_rows(s_rows, tile, nv, lane, wave); };
+    auto issue_k = [&](char *slot, int rows) { issue_key_half(P, slot, rows, lane, wave); };
+    auto issue_v = [&](char *slot, int rows) { issue_value_half(P, slot, rows, lane, wave); };
+
+    // acc[hg][j]: heads 32 wave + 16 hg + 4g + i (i = 0..3), output column 16 j + l16
+    floatx4 acc[2][kD / 16];
+#pragma unroll
+    for (int hg = 0; hg < 2; hg++)
+#pragma unroll
+        for (int j = 0; j < kD / 16; j++) acc[hg][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    // softmax state of head 32 wave + 16 hg + l16 (the lanes of one head agree)
+    float m_run[2] = {kMaxInit, kMaxInit}, l_run[2] = {0.f, 0.f};
+    float m_true[2] = {kNegInf, kNegInf};   // the largest score itself (m_run is raised lazily)
+    vec8 pa[2];                              // P of the current tile, the A operand of P.V
+    // A raised running max rescales the group's accumulators at the start of
+    // the P.V step, behind a wave-uniform flag: any use of the accumulators
+    // by vector instructions inside the score step made the compiler move
+    // all of them between register files on every tile.
+    float alpha_t[2] = {1.f, 1.f};           // rescale factor of head l16 for this tile
+    bool raised[2] = {false, false};         // wave-uniform: the group raised its running max
+    const float smul = P.score_mul;
+
+    // scores of tile `tile` for both head groups from its key slot, the
+    // online-softmax update and P
+    auto qk = [&](int tile, const char *ks_, auto &&pre) {
+        // 36 operand reads (row block i % 2, k-step i / 2), each feeding the
+        // MFMAs of both head groups: four interleaved accumulation chains
+        constexpr int kSteps = 2 * (kDK / 32);
+        auto a_ptr = [&](int i) -> const char * {
+            const int tb = i & 1, ks = i >> 1;
+            const int r = tb * 16 + l16;
+            if (ks < kD / 32) return ks_ + r * kRP + 64 * ks + 16 * g;
+            return ks_ + kRopeOff + r * 128 + 16 * ((4 * (ks - kD / 32) + g) ^ rope_swz(r));
+        };
+        floatx4 sc2[2][2];
+#pragma unroll
+        for (int hg = 0; hg < 2; hg++) sc2[hg][0] = sc2[hg][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+        constexpr int kGrp = 6, kGroups = kSteps / kGrp;
+        static_assert(kSteps % kGrp == 0, "group size");
+        vec8 abuf[2][kGrp];
+#pragma unroll
+        for (int i = 0; i < kGrp; i++) abuf[0][i] = *reinterpret_cast<const vec8 *>(a_ptr(i));
+        pre();
+#pragma unroll
+        for (int j = 0; j < kGroups; j++) {
+            lds_wait();
+            __builtin_amdgcn_sched_barrier(0);
+            if (j + 1 < kGroups) {
+#pragma unroll
+                for (int i = 0; i < kGrp; i++)
+                    abuf[(j + 1) & 1][i] = *reinterpret_cast<const vec8 *>(a_ptr((j + 1) * kGrp + i));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < kGrp; i++) {
+                const int st = j * kGrp + i;
+#pragma unroll
+                for (int hg = 0; hg < 2; hg++)
+                    sc2[hg][st & 1] = M::run(abuf[j & 1][i], qreg[hg][st >> 1], sc2[hg][st & 1]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int hg = 0; hg < 2; hg++) {
+            float p[8];
+            float mt = kNegInf;
+#pragma unroll
+            for (int tb = 0; tb < 2; tb++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int r = tile * kT + tb * 16 + 4 * g + i;
+                    const float s = r < nv ? sc2[hg][tb][i] * smul : kNegInf;
+                    p[tb * 4 + i] = s;
+                    mt = fmaxf(mt, s);
+                }
+            mt = max_xor16(mt);
+            mt = max_xor32(mt);
+            m_true[hg] = fmaxf(m_true[hg], mt);
+            const bool raise = mt > m_run[hg] + kLazy;
+            alpha_t[hg] = 1.f;
+            if (__builtin_amdgcn_ballot_w64(raise)) {
+                const float mn = raise ? mt : m_run[hg];
+                const float alpha = __builtin_amdgcn_exp2f(m_run[hg] - mn);
+                m_run[hg] = mn;
+                l_run[hg] *= alpha;
+                alpha_t[hg] = alpha;
+                raised[hg] = tile > 0;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                p[i] = __builtin_amdgcn_exp2f(p[i] - m_run[hg]);
+                l_run[hg] += p[i];
+            }
+            pa[hg] = M::pack(p);
+        }
+    };
+    // O[h][d] += P[h][t] V~[t][d] for the wave's two head groups over all 512
+    // columns; each transposed V~ operand serves both groups
+    auto pv = [&](const char *vs_, auto &&pre) {
+        const char *v0 = vs_ + (4 * g + (l16 >> 2)) * kRP + 8 * (l16 & 3);
+        const char *v1 = v0 + 16 * kRP;
+        constexpr int kPfV = 4, kGroups = (kD / 16) / kPfV;
+        vec8 bbuf[2][kPfV];
+#pragma unroll
+        for (int i = 0; i < kPfV; i++) bbuf[0][i] = M::tr2(v0 + 32 * i, v1 + 32 * i);
+        pre();
+#pragma unroll
+        for (int hg = 0; hg < 2; hg++) {
+            if (!__builtin_amdgcn_readfirstlane((int)raised[hg])) continue;
+            raised[hg] = false;
+            float ai[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) ai[i] = __shfl(alpha_t[hg], 4 * g + i);
+#pragma unroll
+            for (int j = 0; j < kD / 16; j++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) acc[hg][j][i] *= ai[i];
+        }
+#pragma unroll
+        for (int jg = 0; jg < kGroups; jg++) {
+            lds_wait();
+            __builtin_amdgcn_sched_barrier(0);
+            if (jg + 1 < kGroups) {
+#pragma unroll
+                for (int i = 0; i < kPfV; i++) {
+                    const int j = (jg + 1) * kPfV + i;
+                    bbuf[(jg + 1) & 1][i] = M::tr2(v0 + 32 * j, v1 + 32 * j);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < kPfV; i++)
+#pragma unroll
+                for (int hg = 0; hg < 2; hg++)
+                    acc[hg][jg * kPfV + i] = M::run(pa[hg], bbuf[jg & 1][i], acc[hg][jg * kPfV + i]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    auto end_half = [&]() { lds_wait(); };
+
+    // ---------------------------------------------------- pipeline (as in sfa_kernel)
+    int rows_n = 0;
+    if (n_tiles > 0) {
+        rows_n = rows_of(0);
+        issue_k(s_slot0, rows_n);
+        issue_v(s_slot1, rows_n);
+        rows_n = rows_of(1);
+        issue_k(s_slot2, rows_n);
+    }
+    for (int t = 0; t < n_tiles; t += 2) {
+        wait_vmcnt<kKIns + kVIns>();
+        ring_barrier();
+        {
+            auto pre = [&]() { issue_v(s_slot3, rows_n); rows_n = rows_of(t + 2); };
+            if (act) qk(t, s_slot0, pre);
+            else pre();
+        }
+        end_half();
+        wait_vmcnt<kKIns + kVIns>();
+        ring_barrier();
+        {
+            auto pre = [&]() { issue_k(s_slot0, rows_n); };
+            if (act) pv(s_slot1, pre);
+            else pre();
+        }
+        end_half();
+        if (t + 1 >= n_tiles) break;
+        wait_vmcnt<kKIns + kVIns>();
+        ring_barrier();
+        {
+            auto pre = [&]() { issue_v(s_slot1, rows_n); rows_n = rows_of(t + 3); };
+            if (act) qk(t + 1, s_slot2, pre);
+            else pre();
+        }
+        end_half();
+        wait_vmcnt<kKIns + kVIns>();
+        ring_barrier();
+        {
+            auto pre = [&]() { issue_k(s_slot2, rows_n); };
+            if (act) pv(s_slot3, pre);
+            else pre();
+        }
+        end_half();
+    }
+    wait_vmcnt<0>();
+
+    // ---------------------------------------------------- epilogue
+    const int64_t prow = ((int64_t)qr * P.n_sc + sc) * P.QN;  // partial rows of this chunk
+    float linv[2] = {0.f, 0.f};
+#pragma unroll
+    for (int hg = 0; hg < 2; hg++) {
+        // l of head l16 summed over the four lane groups (m_run already agrees)
+        float l = l_run[hg];
+        l += __shfl_xor(l, 16);
+        l += __shfl_xor(l, 32);
+        linv[hg] = l > 0.f ? 1.f / l : 0.f;
+        const int h = 32 * wave + 16 * hg + l16;
+        if (g == 0 && h < P.QN) {
+            const bool any = l > 0.f;
+            const float m_out = any ? m_true[hg] : m_run[hg];
+            const float l_out = any ? l * __builtin_amdgcn_exp2f(m_run[hg] - m_true[hg]) : 0.f;
+            if (!P.direct) *reinterpret_cast<float2 *>(P.part_ml + (prow + h) * 2) = make_float2(m_out, l_out);
+            if (P.direct && P.lse_max) {
+                const int64_t o = (int64_t)qr * P.QN + h;
+                P.lse_max[o] = any ? m_out * kLn2 : kNegInf;
+                P.lse_sum[o] = l_out;
+            }
+        }
+    }
+    // Every wave is past the ring; wave w stages its 32 heads x 512 columns,
+    // scaled and rounded, in ring slot w (1040-byte rows: the 2-byte writes of
+    // the four lane groups, heads 4 apart, fall in distinct banks) and writes
+    // them with 16-byte stores, one 1 KiB head row per instruction.
+    __syncthreads();
+    if (!act) return;
+    constexpr int kWPitch = 1040;
+    static_assert(32 * kWPitch <= kSlot, "a wave's output block fits one ring slot");
+    char *stg = wave == 0 ? s_slot0 : wave == 1 ? s_slot1 : wave == 2 ? s_slot2 : s_slot3;
+#pragma unroll
+    for (int hg = 0; hg < 2; hg++) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int row = 16 * hg + 4 * g + i;
+            const float inv = __shfl(linv[hg], 4 * g + i);
+#pragma unroll
+            for (int j = 0; j < kD / 16; j++) M::store(stg, row * (kWPitch / 2) + 16 * j + l16, acc[hg][j][i] * inv);
+        }
+    }
+    char *dst = reinterpret_cast<char *>(P.direct ? P.out : P.part_o);
+    const int64_t row0 = P.direct ? (int64_t)qr * P.QN : prow;
+#pragma unroll
+    for (int r = 0; r < 32; r++) {
+        const int hh = 32 * wave + r;
+        if (hh >= P.QN) break;
+        const u32x4 x = *reinterpret_cast<const u32x4 *>(stg + r * kWPitch + 16 * lane);
+        *reinterpret_cast<u32x4 *>(dst + ((row0 + hh) * kD + 8 * lane) * 2) = x;
+    }
+}
+
 // Merges the chunk outputs of one (query row, head) in chunk order:
 // out = sum_s w_s o_s / sum_s w_s with w_s = l_s 2^(m_s - max m), and rounds.
 template <bool BF>
@@ -693,10 +1034,16 @@ hipError_t sfa_launch(const SfaParams &p, bool bf16, int grid, hipStream_t s, hi
                       hipEvent_t ev_end) {
     using namespace sfa_detail;
     if (ev_begin && hipEventRecord(ev_begin, s) != hipSuccess) return hipErrorUnknown;
-    if (bf16)
+    if (p.wide) {
+        if (bf16)
+            hipLaunchKernelGGL(sfa_wide_kernel<true>, dim3(grid), dim3(256), 0, s, p);
+        else
+            hipLaunchKernelGGL(sfa_wide_kernel<false>, dim3(grid), dim3(256), 0, s, p);
+    } else if (bf16) {
         hipLaunchKernelGGL(sfa_kernel<true>, dim3(grid), dim3(256), 0, s, p);
-    else
+    } else {
         hipLaunchKernelGGL(sfa_kernel<false>, dim3(grid), dim3(256), 0, s, p);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (ev_end && hipEventRecord(ev_end, s) != hipSuccess) return hipErrorUnknown;

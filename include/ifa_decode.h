@@ -265,7 +265,10 @@ typedef struct ifa_paged_args {
  *   struct_size that stops before them allows the BSND query and the
  *   PA_BSND cache only.
  * split_hint: 0 lets the planner choose the number of index chunks per
- *   query row; a positive value forces it (testing and tuning).
+ *   query row; a positive value forces it (testing and tuning).  The
+ *   planner reads the device's compute-unit count when split_hint is 0 or
+ *   q_heads > 64 (IFA_ERR_RUNTIME without a device); sfa_decode_mla_plan
+ *   reports what it chose.
  * return_softmax_lse (README parameter table: return_softmax_lse,
  *   softmax_max_out, softmax_sum_out): when 1, the call also writes, per
  *   query row and head, softmax_max_out = the maximum of the scaled scores
@@ -310,6 +313,25 @@ typedef struct sfa_mla_args {
 int ifa_decode_workspace_size(const ifa_decode_args *args, size_t *workspace_bytes);
 int ifa_decode_paged_workspace_size(const ifa_paged_args *args, size_t *workspace_bytes);
 int sfa_decode_mla_workspace_size(const sfa_mla_args *args, size_t *workspace_bytes);
+
+/*
+ * The launch sfa_decode_mla makes for these arguments (the same planner,
+ * with the validation and return codes of sfa_decode_mla_workspace_size):
+ * index chunks per query row, index entries per chunk, workgroups of the
+ * gather kernel, and all_heads = 1 when one workgroup takes every query head
+ * of a chunk, 0 for workgroups of 64 heads.  The planner takes all heads
+ * when there are more than 64 and the 64-head workgroups (one per compute
+ * unit at most) would not all fit on the device at once: that halves the
+ * grid.  For tuning and tests; a call needs none of it.  `plan` is written
+ * only on success.
+ */
+typedef struct sfa_mla_plan {
+    int32_t chunks;
+    int32_t chunk_entries;
+    int32_t workgroups;
+    int32_t all_heads;
+} sfa_mla_plan;
+int sfa_decode_mla_plan(const sfa_mla_args *args, sfa_mla_plan *plan);
 
 /* Phase 2: validate again and enqueue on `stream`.  workspace may be NULL
  * only when the size query returned 0. */

@@ -28,7 +28,7 @@ def test_library_exports_every_declared_function():
     names = header_functions()
     assert {"ifa_decode", "ifa_decode_paged", "sfa_decode_mla", "ifa_decode_workspace_size",
             "ifa_decode_paged_workspace_size", "sfa_decode_mla_workspace_size", "ifa_status_string",
-            "ifa_abi_version", "ifa_read_probe"} <= set(names)
+            "ifa_abi_version", "ifa_read_probe", "sfa_decode_mla_plan"} <= set(names)
     L = bd.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -326,6 +326,41 @@ def test_paged_positional_bias_checks():
 ])
 def test_sfa_breadth_accepted(kw):
     assert ws_size("sfa_decode_mla_workspace_size", sfa_args(**kw))[0] == 0
+
+
+def sfa_plan(a):
+    pl = bd.SfaMlaPlan()
+    rc = bd.lib().sfa_decode_mla_plan(ctypes.byref(a), ctypes.byref(pl))
+    return rc, pl
+
+
+def test_sfa_plan_reports_the_forced_split():
+    # 100 entries in 2 chunks: 50 rounded up to the 32-row tile = 64 entries, so still 2 chunks;
+    # 2 query rows x 2 chunks = 4 groups, rounded up to one round of 8 (XCDs) x 1 head block
+    rc, pl = sfa_plan(sfa_args(split_hint=2))
+    assert rc == 0 and (pl.chunks, pl.chunk_entries, pl.workgroups, pl.all_heads) == (2, 64, 8, 0)
+    # 64 heads, 3 chunks asked: 34 entries rounded up to the tile = 64, so 2 chunks
+    rc, pl = sfa_plan(sfa_args(split_hint=3, q_heads=64))
+    assert rc == 0 and (pl.chunks, pl.chunk_entries, pl.workgroups, pl.all_heads) == (2, 64, 8, 0)
+    # block-wise entries: 64 positions each, at most 512 rows = 8 entries a chunk
+    rc, pl = sfa_plan(sfa_args(split_hint=2, sparse_block_size=64))
+    assert rc == 0 and (pl.chunks, pl.chunk_entries) == (13, 8)
+
+
+def test_sfa_plan_validates_like_the_size_query():
+    assert sfa_plan(sfa_args(query=None))[0] == 161001
+    assert sfa_plan(sfa_args(head_dim=256))[0] == 161002
+    assert bd.lib().sfa_decode_mla_plan(ctypes.byref(sfa_args()), None) == 161001
+    assert ctypes.sizeof(bd.SfaMlaPlan) == 16
+
+
+def test_sfa_plan_needs_the_device_for_more_than_64_heads():
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present; this case needs a machine without one")
+    # the choice between 64-head and all-head workgroups reads the CU count
+    assert sfa_plan(sfa_args(split_hint=2, q_heads=128))[0] == 361001
+    assert sfa_plan(sfa_args(split_hint=0))[0] == 361001
 
 
 def test_sfa_workspace_counts_query_rows_and_block_wise_chunks():
