@@ -448,6 +448,16 @@ def graph_replay_us(fn, a, a_ref, ws_ptr, ws_len, calls: int = 50, replays: int 
     return round(us, 2)
 
 
+def sparse_kernel_name(dev, out, split: int) -> str:
+    """The gather kernel the sparse call launches (the planner's choice)."""
+    from decode_attention_kv_06_amd import binding, harness
+    pl = binding.sfa_decode_mla_plan(dev["q"], dev["q_rope"], dev["key"], dev["key_rope"], dev["value"],
+                                     dev["sparse_indices"], dev["block_table"], dev["actual_seq_lengths_kv"], out,
+                                     **harness.sfa_options(dev, split))
+    return "sfa_wide_kernel (sparse gather, every head in one workgroup)" if pl["all_heads"] \
+        else "sfa_kernel (sparse gather, 64 heads a workgroup)"
+
+
 def measure(gpu: Gpu, name: str, args, ceiling_gbs=None) -> tuple:
     """Run one workload through the protocol; returns (record, host inputs)."""
     import torch
@@ -501,7 +511,7 @@ def measure(gpu: Gpu, name: str, args, ceiling_gbs=None) -> tuple:
         "graph_replay_us_per_call": graph_us,
         "timed_calls": steps,
         "warmup_calls_run": r["warmup_calls"],
-        "roofline": {"bound": "hbm", "kernel": "sfa_kernel (sparse gather)" if sparse else "split_kernel (split-KV)",
+        "roofline": {"bound": "hbm", "kernel": sparse_kernel_name(dev, out, args.split) if sparse else "split_kernel (split-KV)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(name),
                      "kernel_us": r["kernel"]},
