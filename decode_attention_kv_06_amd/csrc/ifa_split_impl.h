@@ -271,8 +271,11 @@ void split_kernel(const SplitParams P) {
     // segment leaves one partial softmax state.  In row mode workgroup
     // blockIdx.x takes row blockIdx.x of the slice, its waves a quarter of the
     // window each.
+    // A row-mode wave knows its one segment from the workgroup id, so it
+    // skips the piece lookup and the segment decode (each a dependent read of
+    // the batch tables before the first query and K/V loads can issue).
     int64_t f0 = 0, f1 = 0;
-    piece_range(P, wave_id, lane, f0, f1);
+    if (I8 || !P.row_mode) piece_range(P, wave_id, lane, f0, f1);
     __shared__ float2 s_ml[kWavesPerBlock][G];   // row mode: each wave's (m, l) per head
     if constexpr (!I8) {
         if (P.row_mode) {
@@ -294,6 +297,16 @@ void split_kernel(const SplitParams P) {
             }
         }
     }
+    // Row mode: the wave's quarter of row blockIdx.x (no partial slot).
+    auto row_desc = [&]() -> SegDesc {
+        const int rpb = P.Nkv * P.n_hg;
+        const int row = blockIdx.x;
+        const int bl = row / rpb, rj = row - bl * rpb;
+        const int len = P.len[bl];
+        const int quarter = (len + kWavesPerBlock - 1) / kWavesPerBlock;
+        const int t0 = min(len, wave * quarter), t1 = min(len, (wave + 1) * quarter);
+        return SegDesc{bl, rj, P.lo[bl] + t0, t1 - t0, 0};
+    };
     // The segment that starts at position f: its batch is the number of
     // batches whose rows start at or before f.
     auto decode = [&](int64_t f) -> SegDesc {
@@ -357,7 +370,7 @@ void split_kernel(const SplitParams P) {
     for (int64_t f = f0; f < f1;) {
         const bool chained = kChain && pref;
         pref = false;
-        const SegDesc sg = chained ? nx : decode(f);
+        const SegDesc sg = chained ? nx : (!I8 && P.row_mode) ? row_desc() : decode(f);
         const int bl = sg.bl, rj = sg.rj, nseg = sg.nseg;   // row of the batch: j * n_hg + hg
         const int j = rj / P.n_hg, hg = rj - j * P.n_hg;
         const int lo = sg.lo;
