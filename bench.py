@@ -6,7 +6,8 @@ HBM and prints one JSON line.  The headline is the dense GQA decode (bf16,
 BSH, 64 batches, 32 query heads over 8 KV heads, head dim 128, lengths
 U[1024, 8192]); the same line carries a record for each other workload:
 the tiny fp16 decode, the paged decode with a mask, the int8-cache decode
-with left padding and the sparse MLA decode.
+with left padding, the sparse MLA decode, the dense decode with a
+positional bias and the sparse decode with two causal query rows a batch.
 
 Protocol, per workload:
   * inputs, output and workspace are allocated once, outside every timed region;
@@ -58,7 +59,8 @@ CEILING_BYTES = 1 << 30                  # read-probe buffer: about one dense de
 CPU_BASELINE_S = 10.0                    # seconds of oracle time per CPU-baseline leg
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.txt")
 HEADLINE = "dense_gqa_bf16_bsh"
-OTHERS = ["tiny_dense_f16", "paged_bf16_bs128", "int8_leftpad_f16", "sfa_mla_bf16"]
+OTHERS = ["tiny_dense_f16", "paged_bf16_bs128", "int8_leftpad_f16", "sfa_mla_bf16", "dense_pse_bf16_bsh",
+          "sfa_mtp_bf16"]
 
 
 def log(msg: str) -> None:
@@ -458,6 +460,15 @@ def sparse_kernel_name(dev, out, split: int) -> str:
         else "sfa_kernel (sparse gather, 64 heads a workgroup)"
 
 
+def ifa_kernel_name(s) -> str:
+    """The split kernel the dense / paged call launches: int8 caches with D = 128, head groups
+    of 8, dense and without mask or bias take the matrix-core int8 kernel."""
+    if s.kv_dtype == "i8" and s.D == 128 and s.N // s.nkv >= 8 and not s.paged and s.mask is None \
+            and not getattr(s, "pse", False):
+        return "split_kernel_i8m (split-KV, int8 products on the matrix cores)"
+    return "split_kernel (split-KV)"
+
+
 def measure(gpu: Gpu, name: str, args, ceiling_gbs=None) -> tuple:
     """Run one workload through the protocol; returns (record, host inputs)."""
     import torch
@@ -511,7 +522,7 @@ def measure(gpu: Gpu, name: str, args, ceiling_gbs=None) -> tuple:
         "graph_replay_us_per_call": graph_us,
         "timed_calls": steps,
         "warmup_calls_run": r["warmup_calls"],
-        "roofline": {"bound": "hbm", "kernel": sparse_kernel_name(dev, out, args.split) if sparse else "split_kernel (split-KV)",
+        "roofline": {"bound": "hbm", "kernel": sparse_kernel_name(dev, out, args.split) if sparse else ifa_kernel_name(spec),
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(name),
                      "kernel_us": r["kernel"]},
