@@ -121,7 +121,8 @@ int finish_plan(IfaPlan &p, int64_t split_tokens) {
         const int64_t tile = (int64_t)(p.G >= 8 ? 4 : 8) * (512 / p.Dc);   // positions per split-kernel tile
         int32_t max_len = 0;
         for (const Window &w : p.win) max_len = std::max(max_len, w.hi - w.lo);
-        p.row_mode = max_len <= kRowModeTiles * tile && (int64_t)p.B * rows_per_batch * kWavesPerBlock <= waves;
+        p.row_mode = max_len <= kRowModeTiles * tile && (int64_t)p.B * rows_per_batch * kWavesPerBlock <= waves &&
+                     (int64_t)p.B * rows_per_batch <= kRowTab;
     }
     if (p.row_mode) {
         SlicePlan sp;
@@ -460,6 +461,13 @@ int run(const IfaPlan &p, const Launch &L, void *ws, size_t ws_bytes, hipStream_
     sp.score_mul = (float)(L.scale * 1.4426950408889634);
     sp.out = L.out;
     sp.row_mode = p.row_mode ? 1 : 0;
+    const int64_t rows_pb = (int64_t)p.Nkv * p.n_hg;
+    if (p.row_mode) {
+        for (int64_t r = 0; r < (int64_t)p.B * rows_pb; r++) {
+            const Window &w = p.win[r / rows_pb];
+            sp.row_win[r] = ((int64_t)(w.hi - w.lo) << 32) | (uint32_t)w.lo;
+        }
+    }
     sp.Dr = p.D;
 
     CombineParams cp;

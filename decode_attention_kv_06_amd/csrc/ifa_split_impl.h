@@ -282,11 +282,11 @@ void split_kernel(const SplitParams P) {
             const int rpb = P.Nkv * P.n_hg;
             const int row = blockIdx.x;
             const int bl = row / rpb, rj = row - bl * rpb;
-            const int len = P.len[bl];
+            const int len = (int)(P.row_win[row] >> 32);
             const int quarter = (len + kWavesPerBlock - 1) / kWavesPerBlock;
-            const int64_t r0 = P.pre[bl] + (int64_t)rj * len;
-            f0 = r0 + min(len, wave * quarter);
-            f1 = r0 + min(len, (wave + 1) * quarter);
+            // only the quarter's length matters here: the segment itself comes from row_desc
+            f0 = min(len, wave * quarter);
+            f1 = min(len, (wave + 1) * quarter);
             if (len == 0) {     // an empty window: zero rows (the whole workgroup returns)
                 const int j = rj / P.n_hg, hg = rj - j * P.n_hg;
                 using T = std::conditional_t<KV == KV_BF16, __bf16, _Float16>;
@@ -302,10 +302,11 @@ void split_kernel(const SplitParams P) {
         const int rpb = P.Nkv * P.n_hg;
         const int row = blockIdx.x;
         const int bl = row / rpb, rj = row - bl * rpb;
-        const int len = P.len[bl];
+        const int64_t w = P.row_win[row];
+        const int len = (int)(w >> 32), lo = (int)(uint32_t)w;
         const int quarter = (len + kWavesPerBlock - 1) / kWavesPerBlock;
         const int t0 = min(len, wave * quarter), t1 = min(len, (wave + 1) * quarter);
-        return SegDesc{bl, rj, P.lo[bl] + t0, t1 - t0, 0};
+        return SegDesc{bl, rj, lo + t0, t1 - t0, 0};
     };
     // The segment that starts at position f: its batch is the number of
     // batches whose rows start at or before f.

@@ -9,6 +9,8 @@ namespace ifa {
 // Batches handled by one launch; the per-batch window table travels in the
 // kernel argument block, so it has a fixed capacity.
 constexpr int kSliceBatches = 128;
+// Rows of a row-mode call (listed in the kernel arguments, see SplitParams::row_win).
+constexpr int kRowTab = 512;
 constexpr int kWavesPerBlock = 4;
 
 enum KvKind { KV_F16 = 0, KV_BF16 = 1, KV_I8 = 2 };
@@ -67,6 +69,9 @@ struct SplitParams {
     float score_mul;        // scale * log2(e)
     int32_t nb;             // batches in this slice
     int32_t b0;             // first batch of the slice
+    int64_t row_win[kRowTab];         // row mode, row r (= workgroup r): (window length << 32) | window
+                                      // start; its address needs no other argument, so the kernel reads
+                                      // it in its first round of argument loads
     int64_t pre[kSliceBatches + 1];   // first flattened position of each batch's rows
     int32_t lo[kSliceBatches];        // window start of each batch
     int32_t len[kSliceBatches];       // window length of each batch

@@ -121,3 +121,17 @@ def test_longer_rows_and_int8_paths_keep_the_split():
     out, n = run_mode(inp)
     assert n > 0                               # the antiquant epilogue lives in the combine
     compare(inp, out)
+
+
+@pytest.mark.parametrize("B,row_mode", [(64, True), (65, False)])
+def test_row_table_limit(B, row_mode):
+    # 8 KV heads x one group of 8 heads: 8 rows a batch.  64 batches fill the
+    # 512-row window table of the kernel arguments exactly (one launch); 65
+    # batches are past it and take the split and the combine.
+    S = 4 * tile(128, 8)
+    spec = IfaSpec("row_table", 830 + B, "bf16", "bf16", B=B, N=64, Nkv=8, D=128, layout="BSH", S=S,
+                   len_range=(0, S))
+    inp = make_ifa(spec)
+    out, n = run_mode(inp)
+    assert (n == 0) == row_mode
+    compare(inp, out)
