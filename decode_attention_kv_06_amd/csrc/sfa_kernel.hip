@@ -652,16 +652,18 @@ __global__ __launch_bounds__(256, 1) void sfa_kernel(const SfaParams P) {
 // All heads of a query row in one workgroup.  The planner takes it when there
 // are more than 64 heads and the workgroups of 64 heads would not all fit on
 // the compute units at once (one workgroup per CU): it halves that grid, so
-// the call runs in one round instead of two.  Wave w
-// scores heads 32w .. 32w+31 (two groups of 16) and accumulates their P.V
-// over all 512 output columns.  So every gathered row is copied into LDS once
-// per chunk, each key operand read from LDS serves both head groups (half
-// the key reads of one wave per 16 heads), P stays in the wave's registers
-// (the score layout is the P.V operand layout), and each wave keeps its own
-// heads' softmax state: no exchange of P, rescale factors or flags between
-// waves.  The register file holds the query of 32 heads (144 registers) and
-// the accumulators of 32 heads x 512 columns (256).  The copy ring, the
-// pipeline and the chunk table are those of sfa_kernel.
+// the call runs in one round instead of two.
+//  * wave w scores heads 32w .. 32w+31 (two groups of 16) and accumulates
+//    their P.V over all 512 output columns;
+//  * so every gathered row is copied into LDS once per chunk, each key operand
+//    read from LDS serves both head groups, P stays in the wave's registers
+//    (the score layout is the P.V operand layout), and each wave keeps its own
+//    heads' softmax state: no P, rescale factors or flags cross waves;
+//  * the register file holds the query of 32 heads (144 registers) and the
+//    accumulators of 32 heads x 512 columns (256); that fits with the
+//    accumulators in VGPR-form MFMAs (this file's build flag) and the running
+//    max rescale kept out of the score step (see below);
+//  * the copy ring, the pipeline and the chunk table are those of sfa_kernel.
 template <bool BF>
 __global__ __launch_bounds__(256, 1) void sfa_wide_kernel(const SfaParams P) {
     using M = Mfma<BF>;
@@ -821,6 +823,7 @@ __global__ __launch_bounds__(256, 1) void sfa_wide_kernel(const SfaParams P) {
         for (int hg = 0; hg < 2; hg++) {
             if (!__builtin_amdgcn_readfirstlane((int)raised[hg])) continue;
             raised[hg] = false;
+            // accumulator rows are heads 4g + i: their factors sit in lanes 4g + i
             float ai[4];
 #pragma unroll
             for (int i = 0; i < 4; i++) ai[i] = __shfl(alpha_t[hg], 4 * g + i);
