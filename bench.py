@@ -33,7 +33,8 @@ Algorithmic bytes count what the method must move: the K/V rows of the
 attended window (for a mask, the rows some query head of the KV head
 attends), the mask bytes of the window, block-table entries used, antiquant
 parameters, the positional bias of the window, q and the output; for the
-sparse path the selected rows (512 + 64 + 512 elements), the indices, the
+sparse path the selected rows (512 + 64 + 512 elements; 512 + 64 when the
+value tensor is the key tensor), the indices, the
 block-table entries used, q, q_rope and the output.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME|all] [--flush write-read|write|read|none]
@@ -105,7 +106,7 @@ def algorithmic_bytes(inp) -> dict:
         rows = sfa_attended_rows(inp)
         eb = 2
         R = inp["q_rows"]
-        kv = rows * (s.D + s.DR + s.D) * eb
+        kv = rows * (s.D + s.DR + (0 if s.value_aliases_key else s.D)) * eb   # value rows that are key rows move once
         extra = R * inp["sparse_indices"].shape[-1] * 4 + s.B * 4 * (2 if s.layout_q == "TND" else 1)
         if s.layout_kv == "PA_BSND":
             extra += rows // s.sparse_block_size * 4       # one block-table entry per selected block

@@ -312,7 +312,7 @@ __device__ __forceinline__ void issue_value_half(const SfaParams &P, char *slot,
 // tile are still copied (the last valid row again, never read), so that count
 // is the same at every step.
 
-template <bool BF>
+template <bool BF, bool ALIAS>
 __global__ __launch_bounds__(256, 1) void sfa_kernel(const SfaParams P) {
     using M = Mfma<BF>;
     using vec8 = typename M::vec8;
@@ -544,53 +544,90 @@ __global__ __launch_bounds__(256, 1) void sfa_kernel(const SfaParams P) {
     auto end_half = [&]() { lds_wait(); };
 
     // ---------------------------------------------------- pipeline
-    // Half-tiles h = 0, 1, 2 are issued up front; step h waits for half h,
-    // synchronises the workgroup (every wave's copies of half h have landed,
-    // every wave is done with half h - 1, whose slot half h + 3 reuses, and P
-    // of the tile is visible), issues half h + 3 and computes half h.
-    // `rows_n` holds the rows of the next tile whose halves are still to be
-    // issued.
     // The compiler's own vector-memory loads (query, indices, block table) are
     // consumed by now; the copies below are the only ones in flight from here.
-    int rows_n = 0;
-    if (n_tiles > 0) {
-        rows_n = rows_of(0);
-        issue_k(s_slot0, rows_n);
-        issue_v(s_slot1, rows_n);
-        rows_n = rows_of(1);
-        issue_k(s_slot2, rows_n);
-    }
-    // two tiles (four half steps, one per slot) per iteration
-    for (int t = 0; t < n_tiles; t += 2) {
-        // h = 2t: scores of tile t (slot 0); issue V(t+1) into slot 3
-        wait_vmcnt<kKIns + kVIns>();
-        ring_barrier();
-        {
-            auto pre = [&]() { issue_v(s_slot3, rows_n); rows_n = rows_of(t + 2); };
-            if (qk_wave) qk(t, s_slot0, pre);
-            else pre();
+    if constexpr (ALIAS) {
+        // The value tensor is the key tensor: a tile's value rows are its key
+        // rows, already in the key slot, so a tile is one copy (key and rope)
+        // into slot t % 4, three tiles ahead.  Step t waits for tile t,
+        // synchronises (every wave's copies of tile t have landed and every
+        // wave is done with tile t - 1, whose slot tile t + 3 reuses), issues
+        // tile t + 3, scores tile t, synchronises again (P and the rescale
+        // factors are visible) and applies P.V from the same slot.
+        if (n_tiles > 0) {
+            issue_k(s_slot0, rows_of(0));
+            issue_k(s_slot1, rows_of(1));
+            issue_k(s_slot2, rows_of(2));
         }
-        end_half();
-        // h = 2t+1: P.V of tile t (slot 1); issue K(t+2) into slot 0
-        wait_vmcnt<kKIns + kVIns>();
-        ring_barrier();
-        pv(s_slot1, [&]() { issue_k(s_slot0, rows_n); });
-        end_half();
-        if (t + 1 >= n_tiles) break;
-        // h = 2t+2: scores of tile t+1 (slot 2); issue V(t+2) into slot 1
-        wait_vmcnt<kKIns + kVIns>();
-        ring_barrier();
-        {
-            auto pre = [&]() { issue_v(s_slot1, rows_n); rows_n = rows_of(t + 3); };
-            if (qk_wave) qk(t + 1, s_slot2, pre);
-            else pre();
+        auto step = [&](int t, char *cur, char *nxt) {
+            wait_vmcnt<2 * kKIns>();
+            ring_barrier();
+            {
+                auto pre = [&]() { issue_k(nxt, rows_of(t + 3)); };
+                if (qk_wave) qk(t, cur, pre);
+                else pre();
+            }
+            end_half();
+            ring_barrier();
+            pv(cur, [&]() {});
+            end_half();
+        };
+        for (int t = 0; t < n_tiles; t += 4) {
+            step(t, s_slot0, s_slot3);
+            if (t + 1 >= n_tiles) break;
+            step(t + 1, s_slot1, s_slot0);
+            if (t + 2 >= n_tiles) break;
+            step(t + 2, s_slot2, s_slot1);
+            if (t + 3 >= n_tiles) break;
+            step(t + 3, s_slot3, s_slot2);
         }
-        end_half();
-        // h = 2t+3: P.V of tile t+1 (slot 3); issue K(t+3) into slot 2
-        wait_vmcnt<kKIns + kVIns>();
-        ring_barrier();
-        pv(s_slot3, [&]() { issue_k(s_slot2, rows_n); });
-        end_half();
+    } else {
+        // Half-tiles h = 0, 1, 2 are issued up front; step h waits for half h,
+        // synchronises the workgroup (every wave's copies of half h have
+        // landed, every wave is done with half h - 1, whose slot half h + 3
+        // reuses, and P of the tile is visible), issues half h + 3 and
+        // computes half h.  `rows_n` holds the rows of the next tile whose
+        // halves are still to be issued.
+        int rows_n = 0;
+        if (n_tiles > 0) {
+            rows_n = rows_of(0);
+            issue_k(s_slot0, rows_n);
+            issue_v(s_slot1, rows_n);
+            rows_n = rows_of(1);
+            issue_k(s_slot2, rows_n);
+        }
+        // two tiles (four half steps, one per slot) per iteration
+        for (int t = 0; t < n_tiles; t += 2) {
+            // h = 2t: scores of tile t (slot 0); issue V(t+1) into slot 3
+            wait_vmcnt<kKIns + kVIns>();
+            ring_barrier();
+            {
+                auto pre = [&]() { issue_v(s_slot3, rows_n); rows_n = rows_of(t + 2); };
+                if (qk_wave) qk(t, s_slot0, pre);
+                else pre();
+            }
+            end_half();
+            // h = 2t+1: P.V of tile t (slot 1); issue K(t+2) into slot 0
+            wait_vmcnt<kKIns + kVIns>();
+            ring_barrier();
+            pv(s_slot1, [&]() { issue_k(s_slot0, rows_n); });
+            end_half();
+            if (t + 1 >= n_tiles) break;
+            // h = 2t+2: scores of tile t+1 (slot 2); issue V(t+2) into slot 1
+            wait_vmcnt<kKIns + kVIns>();
+            ring_barrier();
+            {
+                auto pre = [&]() { issue_v(s_slot1, rows_n); rows_n = rows_of(t + 3); };
+                if (qk_wave) qk(t + 1, s_slot2, pre);
+                else pre();
+            }
+            end_half();
+            // h = 2t+3: P.V of tile t+1 (slot 3); issue K(t+3) into slot 2
+            wait_vmcnt<kKIns + kVIns>();
+            ring_barrier();
+            pv(s_slot3, [&]() { issue_k(s_slot2, rows_n); });
+            end_half();
+        }
     }
 
     // the copies past the last tile land before the workgroup's LDS is released
@@ -664,7 +701,7 @@ __global__ __launch_bounds__(256, 1) void sfa_kernel(const SfaParams P) {
 //    accumulators in VGPR-form MFMAs (this file's build flag) and the running
 //    max rescale kept out of the score step (see below);
 //  * the copy ring, the pipeline and the chunk table are those of sfa_kernel.
-template <bool BF>
+template <bool BF, bool ALIAS>
 __global__ __launch_bounds__(256, 1) void sfa_wide_kernel(const SfaParams P) {
     using M = Mfma<BF>;
     using vec8 = typename M::vec8;
@@ -855,48 +892,79 @@ __global__ __launch_bounds__(256, 1) void sfa_wide_kernel(const SfaParams P) {
     auto end_half = [&]() { lds_wait(); };
 
     // ---------------------------------------------------- pipeline (as in sfa_kernel)
-    int rows_n = 0;
-    if (n_tiles > 0) {
-        rows_n = rows_of(0);
-        issue_k(s_slot0, rows_n);
-        issue_v(s_slot1, rows_n);
-        rows_n = rows_of(1);
-        issue_k(s_slot2, rows_n);
-    }
-    for (int t = 0; t < n_tiles; t += 2) {
-        wait_vmcnt<kKIns + kVIns>();
-        ring_barrier();
-        {
-            auto pre = [&]() { issue_v(s_slot3, rows_n); rows_n = rows_of(t + 2); };
-            if (act) qk(t, s_slot0, pre);
-            else pre();
+    if constexpr (ALIAS) {
+        // the value rows are the key rows: one copy per tile into slot t % 4,
+        // three tiles ahead; no P crosses waves, so one barrier a tile
+        if (n_tiles > 0) {
+            issue_k(s_slot0, rows_of(0));
+            issue_k(s_slot1, rows_of(1));
+            issue_k(s_slot2, rows_of(2));
         }
-        end_half();
-        wait_vmcnt<kKIns + kVIns>();
-        ring_barrier();
-        {
-            auto pre = [&]() { issue_k(s_slot0, rows_n); };
-            if (act) pv(s_slot1, pre);
-            else pre();
+        auto step = [&](int t, char *cur, char *nxt) {
+            wait_vmcnt<2 * kKIns>();
+            ring_barrier();
+            auto pre = [&]() { issue_k(nxt, rows_of(t + 3)); };
+            if (act) {
+                qk(t, cur, pre);
+                pv(cur, [&]() {});
+            } else {
+                pre();
+            }
+            end_half();
+        };
+        for (int t = 0; t < n_tiles; t += 4) {
+            step(t, s_slot0, s_slot3);
+            if (t + 1 >= n_tiles) break;
+            step(t + 1, s_slot1, s_slot0);
+            if (t + 2 >= n_tiles) break;
+            step(t + 2, s_slot2, s_slot1);
+            if (t + 3 >= n_tiles) break;
+            step(t + 3, s_slot3, s_slot2);
         }
-        end_half();
-        if (t + 1 >= n_tiles) break;
-        wait_vmcnt<kKIns + kVIns>();
-        ring_barrier();
-        {
-            auto pre = [&]() { issue_v(s_slot1, rows_n); rows_n = rows_of(t + 3); };
-            if (act) qk(t + 1, s_slot2, pre);
-            else pre();
+    } else {
+        int rows_n = 0;
+        if (n_tiles > 0) {
+            rows_n = rows_of(0);
+            issue_k(s_slot0, rows_n);
+            issue_v(s_slot1, rows_n);
+            rows_n = rows_of(1);
+            issue_k(s_slot2, rows_n);
         }
-        end_half();
-        wait_vmcnt<kKIns + kVIns>();
-        ring_barrier();
-        {
-            auto pre = [&]() { issue_k(s_slot2, rows_n); };
-            if (act) pv(s_slot3, pre);
-            else pre();
+        for (int t = 0; t < n_tiles; t += 2) {
+            wait_vmcnt<kKIns + kVIns>();
+            ring_barrier();
+            {
+                auto pre = [&]() { issue_v(s_slot3, rows_n); rows_n = rows_of(t + 2); };
+                if (act) qk(t, s_slot0, pre);
+                else pre();
+            }
+            end_half();
+            wait_vmcnt<kKIns + kVIns>();
+            ring_barrier();
+            {
+                auto pre = [&]() { issue_k(s_slot0, rows_n); };
+                if (act) pv(s_slot1, pre);
+                else pre();
+            }
+            end_half();
+            if (t + 1 >= n_tiles) break;
+            wait_vmcnt<kKIns + kVIns>();
+            ring_barrier();
+            {
+                auto pre = [&]() { issue_v(s_slot1, rows_n); rows_n = rows_of(t + 3); };
+                if (act) qk(t + 1, s_slot2, pre);
+                else pre();
+            }
+            end_half();
+            wait_vmcnt<kKIns + kVIns>();
+            ring_barrier();
+            {
+                auto pre = [&]() { issue_k(s_slot2, rows_n); };
+                if (act) pv(s_slot3, pre);
+                else pre();
+            }
+            end_half();
         }
-        end_half();
     }
     wait_vmcnt<0>();
 
@@ -1037,16 +1105,14 @@ hipError_t sfa_launch(const SfaParams &p, bool bf16, int grid, hipStream_t s, hi
                       hipEvent_t ev_end) {
     using namespace sfa_detail;
     if (ev_begin && hipEventRecord(ev_begin, s) != hipSuccess) return hipErrorUnknown;
-    if (p.wide) {
-        if (bf16)
-            hipLaunchKernelGGL(sfa_wide_kernel<true>, dim3(grid), dim3(256), 0, s, p);
-        else
-            hipLaunchKernelGGL(sfa_wide_kernel<false>, dim3(grid), dim3(256), 0, s, p);
-    } else if (bf16) {
-        hipLaunchKernelGGL(sfa_kernel<true>, dim3(grid), dim3(256), 0, s, p);
-    } else {
-        hipLaunchKernelGGL(sfa_kernel<false>, dim3(grid), dim3(256), 0, s, p);
-    }
+    // a value tensor that is the key tensor takes the pipelines that copy each
+    // row once
+    const bool alias = p.value == p.key;
+    auto kernel = p.wide ? (bf16 ? (alias ? sfa_wide_kernel<true, true> : sfa_wide_kernel<true, false>)
+                                 : (alias ? sfa_wide_kernel<false, true> : sfa_wide_kernel<false, false>))
+                         : (bf16 ? (alias ? sfa_kernel<true, true> : sfa_kernel<true, false>)
+                                 : (alias ? sfa_kernel<false, true> : sfa_kernel<false, false>));
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (ev_end && hipEventRecord(ev_end, s) != hipSuccess) return hipErrorUnknown;

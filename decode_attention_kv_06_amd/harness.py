@@ -12,10 +12,16 @@ from .workloads import IfaSpec, SfaSpec
 
 
 def to_device(inp: dict, device: str = "cuda") -> dict:
+    """Device copies of the host inputs.  A host tensor that appears under
+    several names (a value tensor that is the key tensor) gets one device copy,
+    so the call sees the same pointer for both."""
     out = {}
+    copies: dict = {}
     for key, val in inp.items():
         if isinstance(val, torch.Tensor):
-            out[key] = val.to(device)
+            if id(val) not in copies:
+                copies[id(val)] = val.to(device)
+            out[key] = copies[id(val)]
         elif isinstance(val, list) and val and isinstance(val[0], torch.Tensor):
             out[key] = [t.to(device) for t in val]
         else:

@@ -435,6 +435,8 @@ def workloads() -> dict:
         "sfa_mla_bf16": SfaSpec("sfa_mla_bf16", 5),
         # multi-token decode: C5's shapes with two query rows per batch under rightDownCausal
         "sfa_mtp_bf16": SfaSpec("sfa_mtp_bf16", 7, QS=2, sparse_mode=3),
+        # C5's shapes with the value tensor being the key tensor (the latent rows serve as both)
+        "sfa_mla_alias_bf16": SfaSpec("sfa_mla_alias_bf16", 8, value_aliases_key=True),
         # the dense GQA workload with a per-batch positional bias (pseShift) of N(0, 4)
         "dense_pse_bf16_bsh": IfaSpec("dense_pse_bf16_bsh", 6, "bf16", "bf16", B=64, N=32, Nkv=8, D=128,
                                       layout="BSH", S=8192, len_range=(1024, 8192), scale=s128, pse=True,

@@ -31,6 +31,17 @@ def test_full_size_workload_matches_oracle():
     compare(inp, out)
 
 
+def test_full_size_value_is_key_sampled_rows():
+    # the value tensor is the key tensor (one device buffer): the pipeline that
+    # copies each gathered row once
+    inp = make_sfa(workloads()["sfa_mla_alias_bf16"])
+    out, dev = run_gpu(inp)
+    assert dev["value"].data_ptr() == dev["key"].data_ptr()
+    n = inp["q_rows"] * inp["spec"].QN
+    rows = sorted(set([0, 1, n // 2, n - 1] + list(range(3, n, max(1, n // 131)))))
+    compare(inp, out, rows=rows)
+
+
 @pytest.mark.parametrize("QN", [1, 16, 20, 64, 100, 128])
 def test_head_counts(QN):
     inp = make_sfa(small(QN=QN, cfg_id=401))
