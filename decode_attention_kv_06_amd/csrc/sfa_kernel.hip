@@ -373,34 +373,10 @@ __global__ __launch_bounds__(256, 1) void sfa_kernel(const SfaParams P) {
     const int nv = compact_chunk(P, qr, sc, s_rows, s_cnt);
 
     // ---------------------------------------------------- gather copies
-    // Wave w copies tile rows 8w .. 8w+7: one 1 KiB instruction per key row and
-    // per value row (the row base is wave-uniform) and one instruction for the
-    // eight rope rows (lane l: row 8w + l/8, 16-byte chunk l%8).  `rows` holds,
-    // in lane l, the physical row of tile row 8w + l/8.
-    const char *keyb = reinterpret_cast<const char *>(P.key);
-    const char *ropeb = reinterpret_cast<const char *>(P.key_rope);
-    const char *valb = reinterpret_cast<const char *>(P.value);
     const int n_tiles = (nv + kT - 1) / kT;
-    const int n_half = 2 * n_tiles;
-    auto rows_of = [&](int tile) -> int {      // tiles past the last repeat its last row
-        return s_rows[min(tile * kT + 8 * wave + (lane >> 3), nv - 1)];
-    };
-    auto issue_k = [&](char *slot, int rows) {
-#pragma unroll
-        for (int j = 0; j < 8; j++) {
-            const int64_t row = __builtin_amdgcn_readlane(rows, 8 * j);
-            dma16(keyb + row * 1024 + lane * 16, slot + (8 * wave + j) * kRP);
-        }
-        const int r = 8 * wave + (lane >> 3);
-        dma16(ropeb + (int64_t)rows * 128 + 16 * ((lane & 7) ^ rope_swz(r)), slot + kRopeOff + wave * 1024);
-    };
-    auto issue_v = [&](char *slot, int rows) {
-#pragma unroll
-        for (int j = 0; j < 8; j++) {
-            const int64_t row = __builtin_amdgcn_readlane(rows, 8 * j);
-            dma16(valb + row * 1024 + lane * 16, slot + (8 * wave + j) * kRP);
-        }
-    };
+    auto rows_of = [&](int tile) { return tile_rows(s_rows, tile, nv, lane, wave); };
+    auto issue_k = [&](char *slot, int rows) { issue_key_half(P, slot, rows, lane, wave); };
+    auto issue_v = [&](char *slot, int rows) { issue_value_half(P, slot, rows, lane, wave); };
 
     // acc[hg][j]: heads 16 hg + 4g + i (i = 0..3) of the block, output column
     // 128 wave + 16 j + l16
