@@ -103,13 +103,16 @@ def algorithmic_bytes(inp) -> dict:
     from decode_attention_kv_06_amd.workloads import SfaSpec
     s = inp["spec"]
     if isinstance(s, SfaSpec):
-        rows = sfa_attended_rows(inp)
+        rows, blocks = sfa_attended(inp)
         eb = 2
         R = inp["q_rows"]
         kv = rows * (s.D + s.DR + (0 if s.value_aliases_key else s.D)) * eb   # value rows that are key rows move once
-        extra = R * inp["sparse_indices"].shape[-1] * 4 + s.B * 4 * (2 if s.layout_q == "TND" else 1)
+        extra = R * inp["sparse_indices"].shape[-1] * 4
+        for name in ("actual_seq_lengths_kv", "actual_seq_lengths_query"):   # device length arrays, when passed
+            if inp[name] is not None:
+                extra += inp[name].numel() * 4
         if s.layout_kv == "PA_BSND":
-            extra += rows // s.sparse_block_size * 4       # one block-table entry per selected block
+            extra += blocks * 4        # one block-table entry per selected block with an attended position
         qo = R * s.QN * (s.D + s.DR) * eb + R * s.QN * s.D * eb
         return {"total": kv + extra + qo, "kv": kv, "streamed": kv + extra + qo}
     B, N, nkv, D = s.B, s.N, s.nkv, s.D
@@ -153,9 +156,11 @@ def algorithmic_bytes(inp) -> dict:
     return {"total": kv + extra + qo, "kv": kv, "streamed": streamed + extra + qo}
 
 
-def sfa_attended_rows(inp) -> int:
-    """Cache rows the sparse call gathers: every selected position below its
-    query row's limit (the kv length, or the causal bound under mode 3)."""
+def sfa_attended(inp) -> tuple:
+    """(rows, blocks) of the sparse call: the cache rows it gathers (every
+    selected position below its query row's limit: the kv length, or the
+    causal bound under mode 3) and the selected blocks holding at least one
+    of them (each costs one block-table entry)."""
     import numpy as np
     s = inp["spec"]
     lkv, lq = inp["lkv_counts"], inp["lq_counts"]
@@ -168,12 +173,12 @@ def sfa_attended_rows(inp) -> int:
     sbs = s.sparse_block_size
     pos = idx[:, :, None] * sbs + np.arange(sbs)
     ok = (idx[:, :, None] >= 0) & (pos < limit[:, None, None])
-    return int(ok.sum())
+    return int(ok.sum()), int(ok.any(axis=2).sum())
 
 
 def sfa_flops(inp) -> int:
     s = inp["spec"]
-    return sfa_attended_rows(inp) * s.QN * 2 * (s.D + s.DR + s.D)
+    return sfa_attended(inp)[0] * s.QN * 2 * (s.D + s.DR + s.D)
 
 
 def describe_config(inp) -> dict:
