@@ -17,7 +17,7 @@ from gpu_util import compare, compare_int8, run_gpu, say
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 160
+N_CASES = 600
 
 
 def draw(i: int):

@@ -17,7 +17,7 @@ from test_sfa_breadth_gpu import run_lse
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 64
+N_CASES = 200
 
 
 def draw(i: int):

@@ -164,7 +164,7 @@ def test_planner_choice_on_the_benchmark_shapes():
     assert plan_of_shape(q_seq=2, sparse_mode=3, q_heads=64)[3] == 0
 
 
-N_RANDOM = 24
+N_RANDOM = 48
 
 
 def draw_all_heads(i: int):
