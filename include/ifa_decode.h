@@ -265,7 +265,9 @@ typedef struct ifa_paged_args {
  *   struct_size that stops before them allows the BSND query and the
  *   PA_BSND cache only.
  * split_hint: 0 lets the planner choose the number of index chunks per
- *   query row; a positive value forces it (testing and tuning).  The
+ *   query row (about one workgroup per compute unit, so a short call can get
+ *   well over 64 chunks); 1 to 64 forces it (testing and tuning), anything
+ *   else is IFA_ERR_PARAM_INVALID.  The
  *   planner reads the device's compute-unit count when split_hint is 0 or
  *   q_heads > 64 (IFA_ERR_RUNTIME without a device); sfa_decode_mla_plan
  *   reports what it chose.

@@ -161,3 +161,34 @@ def test_peaked_scores(layout_kv, split):
 def torch_isfinite(t):
     import torch
     return bool(torch.isfinite(t.float()).all())
+
+
+
+@pytest.mark.parametrize("layout_kv,sparse_size", [("TND", 3000), ("PA_BSND", 4096)])
+def test_more_than_64_chunks(layout_kv, sparse_size):
+    """One query row with a long index list: the planner cuts it into about
+    one chunk per compute unit (well past 64), where the merge reads the
+    chunks' (max, sum) pairs 64 at a time and requests the outputs of only
+    the first 8 up front; the trailing -1 entries leave the last chunks
+    empty (sum 0, weight 0).  The TND case checks softmax_max / softmax_sum
+    too."""
+    import numpy as np
+    import oracle
+    from decode_attention_kv_06_amd import binding, harness
+    inp = make_sfa(small(B=1, QN=16, lkv=[sparse_size + 500], sparse_size=sparse_size, tail_range=(0, 90),
+                         layout_kv=layout_kv, max_blocks=80, cfg_id=560 + sparse_size % 97))
+    dev = harness.to_device(inp)
+    pl = binding.sfa_decode_mla_plan(dev["q"], dev["q_rope"], dev["key"], dev["key_rope"], dev["value"],
+                                     dev["sparse_indices"], dev["block_table"], dev["actual_seq_lengths_kv"],
+                                     harness.alloc_out(dev), **harness.sfa_options(dev, 0))
+    assert pl["chunks"] > 64 and not pl["all_heads"], pl
+    if layout_kv == "PA_BSND":
+        out, _ = run_gpu(inp, split=0, dev=dev)
+        compare(inp, out)
+        return
+    out, mx, sm = run_lse(inp, 0)
+    compare(inp, out)
+    _, rmx, rsm = oracle.sfa(inp, lse=True)
+    rmx, rsm = rmx.reshape(-1), rsm.reshape(-1)
+    np.testing.assert_allclose(mx, rmx, rtol=0, atol=1e-3)
+    np.testing.assert_allclose(sm, rsm, rtol=2e-3, atol=0)
