@@ -69,15 +69,18 @@ def log(msg: str) -> None:
 
 
 def sources_sha() -> str:
-    """Hash of the library's kernel sources and build flags; counter-based
-    traffic figures are only reported for the sources they were taken on."""
+    """Hash of the library's sources (kernels, the public headers they
+    include) and build flags; counter-based traffic figures are only reported
+    for the sources they were taken on."""
     import hashlib
     pkg = os.path.join(ROOT, "decode_attention_kv_06_amd")
     h = hashlib.sha256()
-    files = sorted(os.path.join("csrc", f) for f in os.listdir(os.path.join(pkg, "csrc"))) + ["build.py"]
-    for rel in files:
-        h.update(rel.encode())
-        with open(os.path.join(pkg, rel), "rb") as f:
+    files = sorted(os.path.join(pkg, "csrc", f) for f in os.listdir(os.path.join(pkg, "csrc")))
+    files += sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include")))
+    files.append(os.path.join(pkg, "build.py"))
+    for path in files:
+        h.update(os.path.relpath(path, ROOT).encode())
+        with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
